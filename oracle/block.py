@@ -1,0 +1,145 @@
+"""The tiny YOCO block: self-decoder, one global KV projection, cross-decoder.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): float64 numpy, no code
+shared with the GPU path.
+
+What the method computes:
+* The L layers are split in half: a self-decoder below, a cross-decoder on
+  top ([P seg. 8]; [S §2]).
+* Self-decoder layer: efficient attention (here sliding-window) on the
+  normalised input plus a residual ([P seg. 12]; [S §3]).
+* At the halfway point the output is normalised once and projected by one
+  pair of matrices into the global keys and values ([P seg. 12]).
+* Cross-decoder layer: its own query projection, causal grouped-query
+  attention over that one shared pair, plus a residual ([P seg. 12]).
+* Early exit: prefill runs the self-decoder over the whole prompt, writes the
+  shared KV, skips the cross-decoder for the prompt tokens and sends only
+  the last position through it; the output is unchanged ([P seg. 14] and its
+  Figure 3; [S §2]; [A]).
+Readings taken: each attention keeps an output projection W_o; the SwiGLU
+feed-forward and the final norm are left out (position-wise, no sizes on the
+pages, and they cannot affect causality, sharing or early exit); the
+cross-decoder's residual stream continues from the self-decoder output, the
+same tensor the global K/V are projected from.
+
+Position-wise products are computed row by row with one routine (a
+matrix-vector product), so that a row's value is bitwise the same whether or
+not other rows are computed -- this is what makes the early-exit identity
+exact inside the oracle.
+"""
+
+from dataclasses import dataclass, field
+from typing import List
+
+import math
+
+import numpy as np
+
+from .attention import attend_row, cross_prefill_attention, swa_attention
+from .projection import global_kv_proj, rmsnorm_row
+
+__all__ = ["BlockParams", "linear_rows", "yoco_block", "yoco_block_early_exit"]
+
+
+@dataclass
+class BlockParams:
+    """Weights of the tiny block; every matrix is [out, in]."""
+    n_heads: int
+    n_kv_heads: int
+    head_dim: int
+    window: int
+    swa_wq: List[np.ndarray] = field(default_factory=list)   # [Hq*d, D]
+    swa_wk: List[np.ndarray] = field(default_factory=list)   # [Hkv*d, D]
+    swa_wv: List[np.ndarray] = field(default_factory=list)   # [Hkv*d, D]
+    swa_wo: List[np.ndarray] = field(default_factory=list)   # [D, Hq*d]
+    glob_wk: np.ndarray = None                               # [Hkv*d, D]
+    glob_wv: np.ndarray = None                               # [Hkv*d, D]
+    cross_wq: List[np.ndarray] = field(default_factory=list)  # [Hq*d, D]
+    cross_wo: List[np.ndarray] = field(default_factory=list)  # [D, Hq*d]
+    eps: float = 1e-6
+
+
+def linear_rows(x, w):
+    """y[..., :] = w @ x[..., :] computed one row at a time."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty((flat.shape[0], w.shape[0]))
+    for r in range(flat.shape[0]):
+        out[r] = w @ flat[r]
+    return out.reshape(x.shape[:-1] + (w.shape[0],))
+
+
+def _norm_rows(x, eps):
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty_like(flat)
+    for r in range(flat.shape[0]):
+        out[r] = rmsnorm_row(flat[r], None, eps)
+    return out.reshape(x.shape)
+
+
+def _heads(t, n_heads, head_dim):
+    """[B, N, H*d] -> [B, H, N, d]."""
+    B, N, _ = t.shape
+    return t.reshape(B, N, n_heads, head_dim).transpose(0, 2, 1, 3)
+
+
+def _merge(t):
+    """[B, H, N, d] -> [B, N, H*d]."""
+    B, H, N, d = t.shape
+    return t.transpose(0, 2, 1, 3).reshape(B, N, H * d)
+
+
+def _self_decoder_and_projection(x, p):
+    Hq, Hkv, d = p.n_heads, p.n_kv_heads, p.head_dim
+    x = np.array(x, dtype=np.float64)
+    for wq, wk, wv, wo in zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo):
+        n = _norm_rows(x, p.eps)
+        q = _heads(linear_rows(n, wq), Hq, d)
+        k = _heads(linear_rows(n, wk), Hkv, d)
+        v = _heads(linear_rows(n, wv), Hkv, d)
+        o, _ = swa_attention(q, k, v, p.window)
+        x = x + linear_rows(_merge(o), wo)
+    k_glob, v_glob = global_kv_proj(x, p.glob_wk, p.glob_wv, Hkv, d, eps=p.eps)
+    return x, k_glob, v_glob
+
+
+def yoco_block(x, p):
+    """Full forward: every position goes through the cross-decoder.
+
+    x [B, N, D].  Returns (x_out [B, N, D], (K, V) shared cache [B, Hkv, N, d]).
+    """
+    Hq, d = p.n_heads, p.head_dim
+    x, k_glob, v_glob = _self_decoder_and_projection(x, p)
+    for wq, wo in zip(p.cross_wq, p.cross_wo):
+        n = _norm_rows(x, p.eps)
+        q = _heads(linear_rows(n, wq), Hq, d)
+        # every cross layer reads the same k_glob / v_glob objects
+        o, _ = cross_prefill_attention(q, k_glob, v_glob)
+        x = x + linear_rows(_merge(o), wo)
+    return x, (k_glob, v_glob)
+
+
+def yoco_block_early_exit(x, p):
+    """Early-exit prefill: the cross-decoder runs for the last position only.
+
+    Returns (x_last [B, D], (K, V)).  Equal bitwise to yoco_block(x, p)[0][:, -1].
+    """
+    Hq, Hkv, d = p.n_heads, p.n_kv_heads, p.head_dim
+    x, k_glob, v_glob = _self_decoder_and_projection(x, p)
+    B, N, _ = x.shape
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    last = x[:, N - 1, :].copy()
+    for wq, wo in zip(p.cross_wq, p.cross_wo):
+        new = np.empty_like(last)
+        for b in range(B):
+            n = rmsnorm_row(last[b], None, p.eps)
+            q = (wq @ n).reshape(Hq, d)
+            o = np.empty((Hq, d))
+            for h in range(Hq):
+                o[h], _, _ = attend_row(q[h], k_glob[b, h // g, :N],
+                                        v_glob[b, h // g, :N], scale)
+            new[b] = last[b] + wo @ o.reshape(Hq * d)
+        last = new
+    return last, (k_glob, v_glob)
