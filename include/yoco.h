@@ -1,0 +1,188 @@
+/*
+ * yoco.h -- C ABI of libyoco.so, the MI355X (gfx950) hot path of YOCO
+ * ("You Only Cache Once") decoder-decoder attention.
+ *
+ * The method (pages cited by title and section/segment):
+ *   - paperlayer.ai summary of "You Only Cache Once: Decoder-Decoder
+ *     Architectures for Language Models" (arXiv 2405.05254v2), sections 1-3;
+ *   - podcast transcript "YOCO: caching once for decoder-decoder long-context
+ *     language models" (2026-09-25), segments 4, 8, 12, 14, 26.
+ * A self-decoder of sliding-window attention layers produces a hidden state;
+ * that state is normalised once and projected by one pair of matrices into a
+ * single global key/value cache; every cross-decoder layer has its own
+ * queries and attends causally, with grouped-query heads, to that one cache.
+ * Prefill may skip the cross-decoder for every prompt token but the last.
+ *
+ * Conventions shared by every call
+ *   Layouts     Q, O       [B, H, N, d]      d innermost, head-major
+ *               K, V       [B, Hkv, rows, d] head-major; for the global cache
+ *                          rows = n_cap (capacity), rows [0, n_kv) valid
+ *               X          [B, N, D]
+ *               W_K, W_V   [Hkv*d, D]        "out x in": K = norm(X) @ W_K^T
+ *               LSE        [B, H, N] float32, natural log of the softmax
+ *                          denominator, scale included
+ *   Heads       query head h reads KV head h / (Hq / Hkv) (contiguous groups)
+ *   dtypes      YOCO_F32 and YOCO_BF16 for activations, caches and outputs;
+ *               YOCO_FP8_E4M3 (OCP e4m3fn codes, uint8) only for a decode
+ *               cache.  All arithmetic accumulates in float32.
+ *   head_dim    d must be 64 or 128.
+ *   Pointers    device pointers (HIP), 16-byte aligned, owned by the caller.
+ *               Outputs must not overlap inputs.
+ *   Stream      `stream` is a hipStream_t passed as void* (NULL = the default
+ *               stream).  Every call is stream-ordered and asynchronous:
+ *               it enqueues kernels and returns; it never synchronises,
+ *               never allocates and keeps no mutable global state, so calls
+ *               on different streams may run concurrently.
+ *   Errors      argument errors are detected before any HIP call and leave
+ *               every output untouched; YOCO_ERR_HIP reports a failed launch
+ *               (hipGetLastError).  Faults inside a kernel surface
+ *               asynchronously at the caller's next synchronisation.
+ *               No C++ exception crosses this interface.
+ */
+#ifndef YOCO_H
+#define YOCO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  YOCO_OK = 0,
+  YOCO_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  YOCO_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent  */
+  YOCO_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination             */
+  YOCO_ERR_UNSUPPORTED = 4, /* valid but not implemented (head_dim, D alignment)  */
+  YOCO_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                   */
+  YOCO_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required         */
+  YOCO_ERR_HIP = 7          /* a HIP launch failed                                */
+} yoco_status;
+
+typedef enum { YOCO_F32 = 0, YOCO_BF16 = 1, YOCO_FP8_E4M3 = 2 } yoco_dtype;
+
+/*
+ * Global KV projection ("cache once").
+ * Source: podcast segment 12 (the self-decoder output is normalised once and
+ * projected by a single pair of matrices into the shared keys and values);
+ * paperlayer.ai summary section 2 (one global cache reused by every
+ * cross-decoder layer).  Normalisation read as RMSNorm:
+ *   n_t = x_t / sqrt(mean_j x_tj^2 + eps) * gamma,
+ *   K[b,h,pos0+t,c] = sum_j n_bt,j W_K[h*d+c, j]   (V likewise with W_V).
+ *   x       [B, N, D] act dtype
+ *   norm_w  [D] act dtype (gamma), or NULL for gamma = 1
+ *   w_k,w_v [Hkv*d, D] act dtype
+ *   k_out,v_out [B, Hkv, n_cap, d] act dtype; rows [pos0, pos0+N) written,
+ *           other rows untouched (so prompt chunks can be appended)
+ * Requires 1 <= N, 0 <= pos0, pos0 + N <= n_cap, D % 64 == 0, D <= 65536.
+ * Numerics: float32 accumulation; with gamma given and dtype bf16, x*gamma is
+ * rounded to bf16 before the product (the row scale is applied in float32).
+ */
+yoco_status yoco_global_kv_proj(const void* x, const void* norm_w,
+                                const void* w_k, const void* w_v,
+                                void* k_out, void* v_out,
+                                int B, int N, int D, int Hkv, int d,
+                                int n_cap, int pos0, float eps,
+                                yoco_dtype dtype, void* stream);
+
+/*
+ * Self-decoder sliding-window attention.
+ * Source: paperlayer.ai summary section 3, "Sliding-Window Attention" (each
+ * query restricted to a fixed window, constant-size cache); podcast
+ * segments 8 and 15.  Window read as W keys including the query itself:
+ *   O[b,h,t] = sum_{t-W < s <= t} softmax_s(scale * q_t . k_s) v_s.
+ *   q, o  [B, Hq, N, d];  k, v [B, Hkv, N, d];  lse [B, Hq, N] or NULL.
+ * window >= N is ordinary causal attention.  softmax_scale <= 0 selects
+ * 1/sqrt(d).
+ */
+yoco_status yoco_swa_attn(const void* q, const void* k, const void* v,
+                          void* o, float* lse,
+                          int B, int Hq, int Hkv, int N, int d, int window,
+                          float softmax_scale, yoco_dtype dtype, void* stream);
+
+/*
+ * Cross-decoder causal attention over the shared cache, many queries
+ * (full prefill of one cross-decoder layer, or a chunk of it).
+ * Source: podcast segment 12 (each cross layer has its own queries and
+ * attends causally to the one shared pair, grouped-query heads); paperlayer.ai
+ * summary sections 1-2 (causal masking; one cache reused across layers).
+ * Every cross layer passes the SAME k/v pointers: the call only reads them.
+ *   q, o  [B, Hq, Nq, d]: query i sits at absolute position q_offset + i and
+ *         sees cache rows 0 .. q_offset + i.
+ *   k, v  [B, Hkv, n_cap, d], rows [0, n_kv) valid.   lse [B, Hq, Nq] or NULL.
+ * Requires 0 <= q_offset, q_offset + Nq <= n_kv <= n_cap.
+ */
+yoco_status yoco_cross_attn_prefill(const void* q, const void* k, const void* v,
+                                    void* o, float* lse,
+                                    int B, int Hq, int Hkv, int Nq, int n_kv,
+                                    int n_cap, int q_offset, int d,
+                                    float softmax_scale, yoco_dtype dtype,
+                                    void* stream);
+
+/*
+ * Cross-decoder attention for one new token per sequence (decode step, and
+ * the last prompt position of an early-exit prefill).
+ * Source: podcast segment 4 and 26 (every decode step streams the whole
+ * cache, bandwidth bound), segment 14 and its Figure 3 (only the final prompt
+ * position goes through the cross-decoder; output unchanged).
+ * The cache already holds the current token: sequence b attends to rows
+ * 0 .. ctx_b - 1.  Split-K over the context with a combine pass.
+ *   q, o       [B, Hq, d] q_dtype (o in q_dtype)
+ *   k_cache, v_cache [B, Hkv, n_cap, d] kv_dtype
+ *   k_scale, v_scale [Hkv] float32, required iff kv_dtype == YOCO_FP8_E4M3:
+ *              a code c stands for scale[h] * decode_e4m3fn(c)
+ *   ctx_lens   [B] int32 on the device, or NULL: then every ctx_b = ctx.
+ *              When given, every ctx_lens[b] must lie in [1, ctx]
+ *              (checked by the kernel only by clamping: rows >= ctx are
+ *              never read).
+ *   ctx        1 <= ctx <= n_cap (context length, or its upper bound)
+ *   lse        [B, Hq] float32 or NULL
+ *   workspace  >= yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d)
+ *              bytes of device memory, 16-byte aligned; contents need not
+ *              be initialised; must not be shared by calls running
+ *              concurrently.
+ * Supported (q, kv) dtypes: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3).
+ */
+yoco_status yoco_cross_attn_decode(const void* q, const void* k_cache,
+                                   const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* ctx_lens,
+                                   int ctx, void* o, float* lse,
+                                   int B, int Hq, int Hkv, int n_cap, int d,
+                                   float softmax_scale, yoco_dtype q_dtype,
+                                   yoco_dtype kv_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Workspace of yoco_cross_attn_decode for these sizes (0 on invalid sizes). */
+size_t yoco_cross_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int ctx, int d);
+
+/*
+ * Quantise a K or V tensor to an 8-bit cache.
+ * Source: podcast segments 1 and 24 (8-bit KV cache as the deployed form);
+ * the format is fixed here: OCP e4m3fn, one float32 scale per KV head over
+ * all (b, n, d), s_h = amax_h / 448 (1 if the head is all zero),
+ * code = RNE-saturating e4m3fn(x / s_h) with x / s_h one IEEE float32
+ * division.
+ *   kv     [B, Hkv, n, d] in_dtype (F32 or BF16), finite values
+ *   codes  [B, Hkv, n, d] uint8 (written)
+ *   scale  [Hkv] float32 (written)
+ *   workspace >= yoco_kv_quantize_fp8_workspace_bytes(Hkv) bytes.
+ */
+yoco_status yoco_kv_quantize_fp8(const void* kv, yoco_dtype in_dtype, void* codes,
+                                 float* scale, int B, int Hkv, int n, int d,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+size_t yoco_kv_quantize_fp8_workspace_bytes(int Hkv);
+
+/* Static description of a status code (never NULL). */
+const char* yoco_status_string(yoco_status status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int yoco_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* YOCO_H */

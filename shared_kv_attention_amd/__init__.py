@@ -1,0 +1,207 @@
+"""Python binding of libyoco.so: the MI355X YOCO shared-KV attention hot path.
+
+Thin argument marshalling over the C ABI declared in include/yoco.h: every
+function takes torch tensors that already live on the GPU, checks dtypes and
+contiguity, and passes raw device pointers plus torch's current HIP stream to
+the library.  All computation happens in the library's HIP kernels; there is
+no fallback of any kind -- if libyoco.so is missing the first call raises.
+
+Entry points (same names as the C functions):
+    yoco_global_kv_proj        RMSNorm + one-time K/V projection into the cache
+    yoco_swa_attn              self-decoder sliding-window attention
+    yoco_cross_attn_prefill    causal cross-attention over the shared cache
+    yoco_cross_attn_decode     one-token split-K decode over the shared cache
+    yoco_kv_quantize_fp8       8-bit (e4m3fn) cache writer with per-head scales
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "YocoError",
+    "lib",
+    "library_path",
+    "yoco_global_kv_proj",
+    "yoco_swa_attn",
+    "yoco_cross_attn_prefill",
+    "yoco_cross_attn_decode",
+    "yoco_cross_attn_decode_workspace_bytes",
+    "yoco_kv_quantize_fp8",
+    "yoco_kv_quantize_fp8_workspace_bytes",
+    "yoco_status_string",
+    "yoco_version",
+    "F32",
+    "BF16",
+    "FP8_E4M3",
+]
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libyoco.so")
+_lib = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "yoco_global_kv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_swa_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_cross_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_cross_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
+                                    _vp, _sz, _vp]),
+    "yoco_cross_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "yoco_kv_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "yoco_kv_quantize_fp8_workspace_bytes": (_sz, [_i]),
+    "yoco_status_string": (ctypes.c_char_p, [_i]),
+    "yoco_version": (_i, []),
+}
+
+
+def lib():
+    """Load libyoco.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                f"{library_path} is missing: build it with `python -m shared_kv_attention_amd.build` "
+                "(there is no fallback path)")
+        handle = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class YocoError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({yoco_status_string(status)})")
+
+
+def yoco_status_string(status):
+    return lib().yoco_status_string(int(status)).decode()
+
+
+def yoco_version():
+    return lib().yoco_version()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.uint8:
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(status, fn):
+    if status != 0:
+        raise YocoError(status, fn)
+
+
+def yoco_global_kv_proj(x, w_k, w_v, k_out, v_out, pos0=0, norm_w=None, eps=1e-6, stream=None):
+    """K/V cache rows [pos0, pos0+N) = RMSNorm(x) @ W^T, split into KV heads.
+
+    x [B, N, D]; w_k, w_v [Hkv*d, D]; k_out, v_out [B, Hkv, n_cap, d]; same dtype.
+    """
+    B, N, D = x.shape
+    _, Hkv, n_cap, d = k_out.shape
+    st = lib().yoco_global_kv_proj(_ptr(x), _ptr(norm_w), _ptr(w_k), _ptr(w_v), _ptr(k_out), _ptr(v_out),
+                                   B, N, D, Hkv, d, n_cap, pos0, eps, _dtype_code(x), _stream(stream))
+    _check(st, "yoco_global_kv_proj")
+    return k_out, v_out
+
+
+def yoco_swa_attn(q, k, v, window, o=None, lse=None, softmax_scale=0.0, stream=None):
+    """Sliding-window attention; q [B, Hq, N, d], k/v [B, Hkv, N, d]. Returns o."""
+    torch = _torch()
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib().yoco_swa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, int(window),
+                             float(softmax_scale), _dtype_code(q), _stream(stream))
+    _check(st, "yoco_swa_attn")
+    return o
+
+
+def yoco_cross_attn_prefill(q, k, v, n_kv=None, q_offset=0, o=None, lse=None, softmax_scale=0.0, stream=None):
+    """Causal cross-attention; q [B, Hq, Nq, d] at positions q_offset.., cache k/v [B, Hkv, n_cap, d]."""
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    Hkv, n_cap = k.shape[1], k.shape[2]
+    if n_kv is None:
+        n_kv = n_cap
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib().yoco_cross_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, n_kv, n_cap,
+                                       q_offset, d, float(softmax_scale), _dtype_code(q), _stream(stream))
+    _check(st, "yoco_cross_attn_prefill")
+    return o
+
+
+def yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d):
+    return lib().yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d)
+
+
+def yoco_cross_attn_decode(q, k_cache, v_cache, ctx, ctx_lens=None, k_scale=None, v_scale=None, o=None, lse=None,
+                           workspace=None, softmax_scale=0.0, stream=None):
+    """One decode step; q [B, Hq, d], caches [B, Hkv, n_cap, d] (bf16/f32, or uint8 e4m3fn codes)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    Hkv, n_cap = k_cache.shape[1], k_cache.shape[2]
+    need = yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib().yoco_cross_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(ctx_lens), int(ctx), _ptr(o),
+        _ptr(lse), B, Hq, Hkv, n_cap, d, float(softmax_scale), _dtype_code(q), _dtype_code(k_cache),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "yoco_cross_attn_decode")
+    return o
+
+
+def yoco_kv_quantize_fp8_workspace_bytes(Hkv):
+    return lib().yoco_kv_quantize_fp8_workspace_bytes(Hkv)
+
+
+def yoco_kv_quantize_fp8(kv, codes=None, scale=None, workspace=None, stream=None):
+    """Quantise kv [B, Hkv, n, d] (f32/bf16) to e4m3fn codes + per-head float32 scales."""
+    torch = _torch()
+    B, Hkv, n, d = kv.shape
+    if codes is None:
+        codes = torch.empty(kv.shape, dtype=torch.uint8, device=kv.device)
+    if scale is None:
+        scale = torch.empty(Hkv, dtype=torch.float32, device=kv.device)
+    if workspace is None:
+        workspace = torch.empty(max(yoco_kv_quantize_fp8_workspace_bytes(Hkv), 16), dtype=torch.uint8,
+                                device=kv.device)
+    st = lib().yoco_kv_quantize_fp8(_ptr(kv), _dtype_code(kv), _ptr(codes), _ptr(scale), B, Hkv, n, d,
+                                    _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "yoco_kv_quantize_fp8")
+    return codes, scale

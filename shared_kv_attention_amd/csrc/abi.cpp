@@ -1,0 +1,194 @@
+// C ABI of libyoco: argument validation, workspace layout and dispatch to the
+// gfx950 kernels.  Validation runs before any HIP call, so every argument
+// error is reported synchronously and leaves the outputs untouched.
+// Check order for every call: null pointers, dtypes, sizes, unsupported
+// sizes, alignment, workspace.
+#include "../../include/yoco.h"
+
+#include <math.h>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;   // 0.1.0
+constexpr long long kIntMax = 2147483647LL;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool is_act(yoco_dtype t) { return t == YOCO_F32 || t == YOCO_BF16; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+size_t align16(size_t n) { return (n + 15) / 16 * 16; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / sqrtf((float)d); }
+
+yoco_status launched(hipError_t e) { return e == hipSuccess ? YOCO_OK : YOCO_ERR_HIP; }
+
+struct DecodeLayout {
+  int n_splits, chunk, n_hg;
+  size_t o_bytes, ml_bytes, total;
+};
+
+DecodeLayout decode_layout(int B, int Hq, int Hkv, int ctx, int d) {
+  DecodeLayout L{};
+  yoco::decode_plan(B, Hq, Hkv, ctx, &L.n_splits, &L.chunk, &L.n_hg);
+  const size_t rows = (size_t)B * Hq * L.n_splits;
+  L.o_bytes = align16(rows * d * sizeof(float));
+  L.ml_bytes = align16(rows * sizeof(float));
+  L.total = L.o_bytes + 2 * L.ml_bytes;
+  return L;
+}
+
+bool decode_sizes_ok(int B, int Hq, int Hkv, int ctx, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || ctx < 1 || Hq % Hkv != 0) return false;
+  if (!head_dim_ok(d)) return false;
+  if ((long long)B * Hq > 65535LL * 64 || (long long)B > 65535) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* yoco_status_string(yoco_status s) {
+  switch (s) {
+    case YOCO_OK: return "ok";
+    case YOCO_ERR_NULL: return "a required pointer is NULL";
+    case YOCO_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
+    case YOCO_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case YOCO_ERR_UNSUPPORTED: return "valid but unsupported size (head_dim must be 64 or 128; D a multiple of 64)";
+    case YOCO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case YOCO_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case YOCO_ERR_HIP: return "a HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int yoco_version(void) { return kVersion; }
+
+yoco_status yoco_global_kv_proj(const void* x, const void* norm_w, const void* w_k, const void* w_v,
+                                void* k_out, void* v_out, int B, int N, int D, int Hkv, int d,
+                                int n_cap, int pos0, float eps, yoco_dtype dtype, void* stream) {
+  if (!x || !w_k || !w_v || !k_out || !v_out) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (B < 1 || N < 1 || D < 1 || Hkv < 1 || n_cap < 1 || pos0 < 0 || (long long)pos0 + N > n_cap)
+    return YOCO_ERR_SHAPE;
+  if (!(eps >= 0.f) || isinf(eps)) return YOCO_ERR_SHAPE;
+  if ((long long)B * N > kIntMax || (long long)2 * Hkv * d > kIntMax || (long long)B * Hkv * n_cap > kIntMax)
+    return YOCO_ERR_SHAPE;
+  if (!head_dim_ok(d) || D % 64 != 0 || D > 65536) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
+      (norm_w && !aligned(norm_w, 16)))
+    return YOCO_ERR_ALIGN;
+  yoco::ProjArgs a{x, norm_w, w_k, w_v, k_out, v_out, B, N, D, Hkv, d, n_cap, pos0, eps};
+  return launched(yoco::launch_kv_proj(a, dtype == YOCO_BF16, as_stream(stream)));
+}
+
+static yoco_status attn_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                               int Hkv, int Nq, int n_kv, int kv_rows, int q_offset, int d, int window,
+                               bool swa, float softmax_scale, yoco_dtype dtype, void* stream) {
+  if (!q || !k || !v || !o) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || n_kv < 1 || Hq % Hkv != 0) return YOCO_ERR_SHAPE;
+  if (q_offset < 0 || (long long)q_offset + Nq > n_kv || n_kv > kv_rows) return YOCO_ERR_SHAPE;
+  if (swa && window < 1) return YOCO_ERR_SHAPE;
+  if (isnan(softmax_scale) || isinf(softmax_scale)) return YOCO_ERR_SHAPE;
+  const long long nqt = (Nq + 127) / 128;
+  if (nqt * B * Hq > kIntMax || (long long)kv_rows > kIntMax / 2) return YOCO_ERR_SHAPE;
+  if (!head_dim_ok(d)) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+    return YOCO_ERR_ALIGN;
+  const float scale = resolve_scale(softmax_scale, d);
+  yoco::AttnArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, n_kv, kv_rows, q_offset, swa ? window : 0,
+                   scale * 1.4426950408889634f};
+  return launched(yoco::launch_attn(a, dtype == YOCO_BF16, d, swa, as_stream(stream)));
+}
+
+yoco_status yoco_swa_attn(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                          int Hkv, int N, int d, int window, float softmax_scale, yoco_dtype dtype, void* stream) {
+  return attn_common(q, k, v, o, lse, B, Hq, Hkv, N, N, N, 0, d, window, true, softmax_scale, dtype, stream);
+}
+
+yoco_status yoco_cross_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                    int Hq, int Hkv, int Nq, int n_kv, int n_cap, int q_offset, int d,
+                                    float softmax_scale, yoco_dtype dtype, void* stream) {
+  return attn_common(q, k, v, o, lse, B, Hq, Hkv, Nq, n_kv, n_cap, q_offset, d, 0, false, softmax_scale, dtype,
+                     stream);
+}
+
+size_t yoco_cross_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int ctx, int d) {
+  if (!decode_sizes_ok(B, Hq, Hkv, ctx, d)) return 0;
+  return decode_layout(B, Hq, Hkv, ctx, d).total;
+}
+
+yoco_status yoco_cross_attn_decode(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                   const float* v_scale, const int32_t* ctx_lens, int ctx, void* o, float* lse,
+                                   int B, int Hq, int Hkv, int n_cap, int d, float softmax_scale,
+                                   yoco_dtype q_dtype, yoco_dtype kv_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const bool fp8 = kv_dtype == YOCO_FP8_E4M3;
+  if (!q || !k_cache || !v_cache || !o) return YOCO_ERR_NULL;
+  if (fp8 && (!k_scale || !v_scale)) return YOCO_ERR_NULL;
+  const bool combo_ok = (q_dtype == YOCO_F32 && kv_dtype == YOCO_F32) ||
+                        (q_dtype == YOCO_BF16 && kv_dtype == YOCO_BF16) ||
+                        (q_dtype == YOCO_BF16 && kv_dtype == YOCO_FP8_E4M3);
+  if (!combo_ok) return YOCO_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || n_cap < 1 || ctx < 1 || ctx > n_cap || Hq % Hkv != 0) return YOCO_ERR_SHAPE;
+  if (B > 65535 || (long long)B * Hkv * n_cap > kIntMax || (long long)Hkv * ((Hq / Hkv + 3) / 4) > 65535)
+    return YOCO_ERR_SHAPE;
+  if (isnan(softmax_scale) || isinf(softmax_scale)) return YOCO_ERR_SHAPE;
+  if (!head_dim_ok(d)) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)) || (ctx_lens && !aligned(ctx_lens, 4)) || (k_scale && !aligned(k_scale, 4)) ||
+      (v_scale && !aligned(v_scale, 4)))
+    return YOCO_ERR_ALIGN;
+  const DecodeLayout L = decode_layout(B, Hq, Hkv, ctx, d);
+  if (!workspace || workspace_bytes < L.total) return YOCO_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  yoco::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.ctx_lens = ctx_lens;
+  a.ctx = ctx;
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_m = reinterpret_cast<float*>(ws + L.o_bytes);
+  a.part_l = reinterpret_cast<float*>(ws + L.o_bytes + L.ml_bytes);
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_cap = n_cap;
+  a.n_splits = L.n_splits;
+  a.chunk = L.chunk;
+  a.n_hg = L.n_hg;
+  a.scale_log2 = resolve_scale(softmax_scale, d) * 1.4426950408889634f;
+  const int qk = q_dtype == YOCO_F32 ? 0 : 1;
+  const int kk = kv_dtype == YOCO_F32 ? 0 : (kv_dtype == YOCO_BF16 ? 1 : 2);
+  return launched(yoco::launch_decode(a, qk, kk, d, as_stream(stream)));
+}
+
+size_t yoco_kv_quantize_fp8_workspace_bytes(int Hkv) {
+  if (Hkv < 1) return 0;
+  return align16((size_t)Hkv * sizeof(uint32_t));
+}
+
+yoco_status yoco_kv_quantize_fp8(const void* kv, yoco_dtype in_dtype, void* codes, float* scale, int B, int Hkv,
+                                 int n, int d, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kv || !codes || !scale) return YOCO_ERR_NULL;
+  if (!is_act(in_dtype)) return YOCO_ERR_DTYPE;
+  if (B < 1 || Hkv < 1 || n < 1 || B > 65535 || Hkv > 65535) return YOCO_ERR_SHAPE;
+  if (!head_dim_ok(d)) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(kv, 16) || !aligned(codes, 16) || !aligned(scale, 4)) return YOCO_ERR_ALIGN;
+  if (!workspace || workspace_bytes < yoco_kv_quantize_fp8_workspace_bytes(Hkv)) return YOCO_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
+  yoco::QuantArgs a{kv, static_cast<uint8_t*>(codes), scale, static_cast<uint32_t*>(workspace), B, Hkv,
+                    (long long)n * d};
+  return launched(yoco::launch_quant_fp8(a, in_dtype == YOCO_BF16, as_stream(stream)));
+}
+
+}  // extern "C"

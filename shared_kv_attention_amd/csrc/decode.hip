@@ -1,0 +1,327 @@
+// Split-K decode attention over the shared global cache (one query token per
+// sequence), and the combine pass that merges the splits.
+//
+// What is computed (YOCO podcast transcript, segments 4, 14 and 26;
+// paperlayer.ai summary of "You Only Cache Once", section 2): for sequence b
+// and query head h, o = softmax(scale * q K^T) V over cache rows 0..ctx_b-1 of
+// KV head h / (Hq/Hkv).  Every cross-decoder layer streams the whole cache at
+// every step, so the kernel is bound by HBM bandwidth.
+//
+// Design (MI355X-first):
+//  * Grid (split, kv-head x head-group, batch); one wave per workgroup.  A
+//    workgroup reads its slice of K and V exactly once and serves all (up to
+//    4) query heads of its KV head.  Splits give thousands of workgroups even
+//    for one sequence, so all 256 CUs stream concurrently.
+//  * Keys are processed 16 at a time.  For q . k, lane l holds key l%16 and
+//    dims {32c + 8*(l/16) + j}: 16-byte row loads (8-byte for fp8 codes) in
+//    the natural operand layout of the 16x16x32 matrix core, so K needs no
+//    LDS staging.  The A operand is the query block replicated 4 times
+//    (row r -> head r%4), so every lane receives all 4 heads' scores of its
+//    own key.
+//  * For P V each lane owns D/64 output dims across all keys: one V row is
+//    read by one load instruction (fully contiguous), the probabilities of
+//    key j are taken from lane j as wave-uniform scalars (readlane), and the
+//    per-lane accumulator is only 4 heads x D/64 floats -- no cross-lane
+//    reduction of O is ever needed and occupancy stays high.
+//  * Online softmax in the exp2 domain; the running max per head is raised
+//    only when a block exceeds it by 2^8 (wave-uniform branch).
+//  * The next block's loads are issued before the current block is used.
+//  * fp8-e4m3 caches: codes are decoded in registers (exactly, to bf16 for
+//    the matrix core and to f32 for P V); the per-head scales factor out of
+//    both products: the K scale is folded into the softmax scale and the V
+//    scale multiplies the split's partial output once.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace yoco {
+
+template <typename KVT> struct KvTraits;
+template <> struct KvTraits<bf16> { static constexpr int bytes = 2; using mma_t = bf16; };
+template <> struct KvTraits<float> { static constexpr int bytes = 4; using mma_t = float; };
+template <> struct KvTraits<uint8_t> { static constexpr int bytes = 1; using mma_t = bf16; };
+
+// Raw per-lane storage for 8 consecutive elements of one K row.
+template <typename KVT> struct Raw8;
+template <> struct Raw8<bf16> { u32x4 w; };
+template <> struct Raw8<float> { u32x4 lo, hi; };
+template <> struct Raw8<uint8_t> { u32x2 w; };
+
+template <typename KVT>
+__device__ __forceinline__ Raw8<KVT> load_raw8(const KVT* p) {
+  Raw8<KVT> r;
+  if constexpr (sizeof(KVT) == 2) {
+    r.w = *reinterpret_cast<const u32x4*>(p);
+  } else if constexpr (sizeof(KVT) == 4) {
+    r.lo = *reinterpret_cast<const u32x4*>(p);
+    r.hi = *reinterpret_cast<const u32x4*>(p + 4);
+  } else {
+    r.w = *reinterpret_cast<const u32x2*>(p);
+  }
+  return r;
+}
+
+// Raw K elements -> matrix-core operand fragment.
+template <typename KVT>
+__device__ __forceinline__ typename Elem<typename KvTraits<KVT>::mma_t>::frag to_frag(const Raw8<KVT>& r) {
+  if constexpr (sizeof(KVT) == 2) {
+    return __builtin_bit_cast(bf16x8, r.w);
+  } else if constexpr (sizeof(KVT) == 4) {
+    f32x4 a = __builtin_bit_cast(f32x4, r.lo), b = __builtin_bit_cast(f32x4, r.hi);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    bf16x8 f;
+#pragma unroll
+    for (int wd = 0; wd < 2; ++wd) {
+      const f32x2 lo = fp8x2_to_f32(r.w[wd], false);
+      const f32x2 hi = fp8x2_to_f32(r.w[wd], true);
+      f[4 * wd + 0] = (bf16)lo[0];   // exact: every e4m3 value is a bf16 value
+      f[4 * wd + 1] = (bf16)lo[1];
+      f[4 * wd + 2] = (bf16)hi[0];
+      f[4 * wd + 3] = (bf16)hi[1];
+    }
+    return f;
+  }
+}
+
+// The V slice one lane owns in one key row: DPL = D/64 consecutive elements.
+template <typename KVT, int DPL> struct VSlice {
+  static constexpr int bytes = DPL * (int)sizeof(KVT);
+  using type = typename std::conditional<bytes == 1, uint8_t,
+               typename std::conditional<bytes == 2, uint16_t,
+               typename std::conditional<bytes == 4, uint32_t, u32x2>::type>::type>::type;
+};
+
+template <typename KVT, int DPL>
+__device__ __forceinline__ void vslice_to_f32(typename VSlice<KVT, DPL>::type w, float* out) {
+  if constexpr (sizeof(KVT) == 1) {
+    const f32x2 v = fp8x2_to_f32((uint32_t)w, false);
+    out[0] = v[0];
+    if constexpr (DPL == 2) out[1] = v[1];
+  } else if constexpr (sizeof(KVT) == 2) {
+    if constexpr (DPL == 1) {
+      out[0] = __uint_as_float((uint32_t)w << 16);
+    } else {
+      out[0] = __uint_as_float((uint32_t)w << 16);
+      out[1] = __uint_as_float((uint32_t)w & 0xFFFF0000u);
+    }
+  } else {
+    if constexpr (DPL == 1) {
+      out[0] = __uint_as_float((uint32_t)w);
+    } else {
+      out[0] = __uint_as_float(w[0]);
+      out[1] = __uint_as_float(w[1]);
+    }
+  }
+}
+
+template <typename QT>
+__device__ __forceinline__ typename Elem<QT>::frag load_q_frag(const QT* p) {
+  if constexpr (sizeof(QT) == 2) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  } else {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+}
+
+__device__ __forceinline__ int decode_ctx(const DecodeArgs& a, int b) {
+  if (a.ctx_lens == nullptr) return a.ctx;
+  return min(max((int)a.ctx_lens[b], 1), a.ctx);
+}
+
+template <typename QT, typename KVT, int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  using MT = typename KvTraits<KVT>::mma_t;
+  static_assert(sizeof(MT) == sizeof(QT), "query dtype must match the matrix-core dtype");
+  using frag = typename Elem<MT>::frag;
+  constexpr int NC = D / 32;     // 32-dim matrix-core steps of q . k
+  constexpr int DPL = D / 64;    // output dims owned by each lane in P V
+  using vword = typename VSlice<KVT, DPL>::type;
+
+  const int l = threadIdx.x, r16 = l & 15, G = l >> 4;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y / a.n_hg, hg = blockIdx.y % a.n_hg;
+  const int b = blockIdx.z;
+  const int grp = a.Hq / a.Hkv;
+  const int h0 = kvh * grp + 4 * hg;
+  const int nh = min(4, grp - 4 * hg);
+
+  const int ctx_b = decode_ctx(a, b);
+  const int key_begin = split * a.chunk;
+  if (key_begin >= ctx_b) return;
+  const int key_end = min(key_begin + a.chunk, ctx_b);
+
+  // Query operand: row r -> head (r & 3) of this group (zero beyond nh).
+  frag qa[NC];
+  {
+    const int hh = r16 & 3;
+    if (hh < nh) {
+      const QT* qrow = static_cast<const QT*>(a.q) + (size_t)(b * a.Hq + h0 + hh) * D;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qa[c] = load_q_frag<QT>(qrow + 32 * c + 8 * G);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qa[c] = frag{};
+    }
+  }
+  float sc = a.scale_log2;
+  if constexpr (sizeof(KVT) == 1) sc *= a.k_scale[kvh];
+
+  const size_t head_off = (size_t)(b * a.Hkv + kvh) * a.n_cap;
+  const KVT* kb = static_cast<const KVT*>(a.k) + head_off * D + 8 * G;          // K: MFMA operand layout
+  const KVT* vb = static_cast<const KVT*>(a.v) + head_off * D + DPL * l;        // V: lane-owned dims
+
+  float m_run[4], l_run[4];
+  float acc[4][DPL];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[i][e] = 0.f;
+  }
+
+  Raw8<KVT> kc[NC], kn[NC];
+  vword vc[16], vn[16];
+  auto load_block = [&](int key0, Raw8<KVT>* kr, vword* vr) {
+    const int kkey = min(key0 + r16, key_end - 1);   // never read rows >= ctx_b
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = load_raw8<KVT>(kb + (size_t)kkey * D + 32 * c);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int vkey = min(key0 + j, key_end - 1);
+      vr[j] = *reinterpret_cast<const vword*>(vb + (size_t)vkey * D);
+    }
+  };
+
+  load_block(key_begin, kc, vc);
+  for (int key0 = key_begin; key0 < key_end; key0 += 16) {
+    const bool has_next = key0 + 16 < key_end;
+    if (has_next) load_block(key0 + 16, kn, vn);
+
+    // scores: lane (G, r16) receives head i's score of key key0 + r16 in s[i]
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) s = mma16(qa[c], to_frag<KVT>(kc[c]), s);
+    const bool valid = key0 + r16 < key_end;
+    float x[4];
+    bool up = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = valid ? s[i] * sc : -INFINITY;
+      up |= x[i] > m_run[i] + 8.0f;
+    }
+    if (__any(up)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float m_new = fmaxf(m_run[i], row16_max(x[i]));
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+        l_run[i] *= alpha;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[i][e] *= alpha;
+        m_run[i] = m_new;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mref = (m_run[i] == -INFINITY) ? 0.f : m_run[i];
+      p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+      l_run[i] += p[i];
+    }
+    // P V: key j's probabilities are read from lane j as wave-uniform scalars
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float vf[DPL];
+      vslice_to_f32<KVT, DPL>(vc[j], vf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pjf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[i]), j));
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[i][e] = fmaf(pjf, vf[e], acc[i][e]);
+      }
+    }
+    if (has_next) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kc[c] = kn[c];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) vc[j] = vn[j];
+    }
+  }
+
+  // l: sum of the 16 key-lanes (the 4 rows hold identical copies)
+  float vscale = 1.f;
+  if constexpr (sizeof(KVT) == 1) vscale = a.v_scale[kvh];
+  const size_t S = gridDim.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lt = row16_sum(l_run[i]);
+    if (i < nh) {
+      const size_t row = (size_t)(b * a.Hq + h0 + i) * S + split;
+      float* dst = a.part_o + row * D + DPL * l;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) dst[e] = acc[i][e] * vscale;
+      if (l == 0) {
+        a.part_m[row] = m_run[i];
+        a.part_l[row] = lt;
+      }
+    }
+  }
+}
+
+// One workgroup per (query head, batch); thread = output dim.
+template <typename OT, int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+  const int S = a.n_splits;
+  const int ctx_b = decode_ctx(a, b);
+  const int ns = (ctx_b + a.chunk - 1) / a.chunk;
+  const size_t base = (size_t)(b * a.Hq + h) * S;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_m[base + s]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float wgt = __builtin_amdgcn_exp2f(a.part_m[base + s] - M);
+    L = fmaf(wgt, a.part_l[base + s], L);
+    acc = fmaf(wgt, a.part_o[(base + s) * D + dim], acc);
+  }
+  OT* o = static_cast<OT*>(a.o) + (size_t)(b * a.Hq + h) * D;
+  o[dim] = from_f32<OT>(acc / L);
+  if (a.lse != nullptr && dim == 0) a.lse[b * a.Hq + h] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+}
+
+template <typename QT, typename KVT, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.n_splits, a.Hkv * a.n_hg, a.B);
+  hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D>), grid, dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<QT, D>), dim3(a.Hq, a.B), dim3(D), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hipStream_t stream) {
+  // kinds: 0 = f32, 1 = bf16, 2 = fp8-e4m3 codes
+  if (q_kind == 0) return d == 128 ? launch_decode_t<float, float, 128>(a, stream) : launch_decode_t<float, float, 64>(a, stream);
+  if (kv_kind == 1) return d == 128 ? launch_decode_t<bf16, bf16, 128>(a, stream) : launch_decode_t<bf16, bf16, 64>(a, stream);
+  return d == 128 ? launch_decode_t<bf16, uint8_t, 128>(a, stream) : launch_decode_t<bf16, uint8_t, 64>(a, stream);
+}
+
+void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int* n_hg) {
+  const int grp = Hq / Hkv;
+  *n_hg = (grp + 3) / 4;
+  const long long units = (long long)B * Hkv * (*n_hg);
+  const long long target = 4096;                       // workgroups (one wave each)
+  long long s = (target + units - 1) / units;
+  const long long max_s = (ctx + 255) / 256;           // at least 256 keys per split
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  long long c = (ctx + s - 1) / s;
+  c = (c + 63) / 64 * 64;
+  *chunk = (int)c;
+  *n_splits = (int)((ctx + c - 1) / c);
+}
+
+}  // namespace yoco

@@ -1,0 +1,246 @@
+// Global KV projection: K, V = RMSNorm(X) W_K^T, RMSNorm(X) W_V^T, written
+// once into the head-major shared cache.
+//
+// What is computed (YOCO podcast transcript, segment 12: the self-decoder
+// output is normalised once and projected by a single pair of matrices into
+// the shared keys and values; paperlayer.ai summary of "You Only Cache Once",
+// section 2): for token t, n_t = x_t / sqrt(mean(x_t^2) + eps) * gamma and
+// K[b, h, pos0 + t, c] = n_t . W_K[h*d + c], V likewise.
+//
+// Design (MI355X-first):
+//  * One GEMM for both matrices: the output "features" are the 2*Hkv*d rows
+//    of [W_K; W_V]; the product is formed transposed, C^T = W X^T, on
+//    32x32x16 bf16 MFMA (32x32x2 f32 for float32), so each lane's results
+//    belong to one token and 4 consecutive channels of one head -- the
+//    epilogue scales by that token's RMS factor and stores 4 channels at a
+//    time straight into [B, Hkv, n_cap, d].
+//  * The normalisation is fused: the threads that stage X tiles into LDS
+//    accumulate the row sums of squares from the very values they move, so X
+//    is read once; the per-row factor is applied to the float32 accumulator.
+//    A norm gain gamma, when given, multiplies X during staging.
+//  * 128x128 output tile per 256-thread workgroup, 64-element k steps (32 for
+//    float32), LDS double buffering with XOR-swizzled 16-byte chunks.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace yoco {
+
+template <typename T>
+struct ProjCfg {
+  static constexpr int E = Elem<T>::bytes;
+  static constexpr int BM = 128;                 // features per tile
+  static constexpr int BN = 128;                 // tokens per tile
+  static constexpr int BKK = 128 / E;            // k elements per stage (128-byte rows)
+  static constexpr int CH = 8;                   // 16-byte chunks per tile row
+  static constexpr int PER_T = 128 * CH / 256;   // chunks per thread per operand (= 4)
+  static constexpr int NKS = BKK / 16;           // matrix-core k steps per stage
+  static constexpr int TILE_BYTES = 128 * 128;
+};
+
+__device__ __forceinline__ int swz8(int row) { return row & 7; }
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag lds_frag_row(const char* tile, int row, int kc, int g) {
+  const char* rowp = tile + row * 128;
+  const int sw = swz8(row);
+  typename Elem<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+    const int ch = 2 * kc + g;
+    f = *reinterpret_cast<const bf16x8*>(rowp + ((ch ^ sw) << 4));
+  } else {
+    const int ch = 4 * kc + 2 * g;
+    f32x4 a = *reinterpret_cast<const f32x4*>(rowp + ((ch ^ sw) << 4));
+    f32x4 b = *reinterpret_cast<const f32x4*>(rowp + (((ch + 1) ^ sw) << 4));
+    f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  return f;
+}
+
+// Square-sum of the elements in a raw 16-byte chunk.
+template <typename T>
+__device__ __forceinline__ float chunk_sumsq(u32x4 w) {
+  float s = 0.f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+      s = fmaf(lo, lo, s);
+      s = fmaf(hi, hi, s);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = __uint_as_float(w[i]);
+      s = fmaf(x, x, s);
+    }
+  }
+  return s;
+}
+
+// x * gamma, rounded back to T, for one 16-byte chunk.
+template <typename T>
+__device__ __forceinline__ u32x4 chunk_scale(u32x4 w, u32x4 gw) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(w[i] << 16) * __uint_as_float(gw[i] << 16);
+      const float hi = __uint_as_float(w[i] & 0xFFFF0000u) * __uint_as_float(gw[i] & 0xFFFF0000u);
+      bf16x2 p{(bf16)lo, (bf16)hi};
+      r[i] = __builtin_bit_cast(uint32_t, p);
+    }
+    return r;
+  } else {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(__uint_as_float(w[i]) * __uint_as_float(gw[i]));
+    return r;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
+  using C = ProjCfg<T>;
+  __shared__ __attribute__((aligned(16))) char smem[2][2][C::TILE_BYTES];   // [buf][W|X]
+  __shared__ float rs_lds[C::BN];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 5, r32 = l & 31;
+  const int wf = w >> 1, wt = w & 1;
+  const int HD = a.Hkv * a.d;
+  const int F = 2 * HD;
+  const int M = a.B * a.N;
+  const int t0 = blockIdx.x * C::BN;
+  const int f0 = blockIdx.y * C::BM;
+
+  // staging assignment: chunk id = tid + 256 r -> tile row id/8, chunk id%8
+  const int srow0 = tid >> 3, sch = tid & 7;
+  const char* wrow[C::PER_T];
+  const char* xrow[C::PER_T];
+#pragma unroll
+  for (int r = 0; r < C::PER_T; ++r) {
+    const int frow = f0 + srow0 + 32 * r;
+    const int trow = t0 + srow0 + 32 * r;
+    const void* wmat = frow < HD ? a.w_k : a.w_v;
+    const int fr = frow < HD ? frow : frow - HD;
+    wrow[r] = frow < F ? static_cast<const char*>(wmat) + (size_t)fr * a.D * C::E : nullptr;
+    xrow[r] = trow < M ? static_cast<const char*>(a.x) + (size_t)trow * a.D * C::E : nullptr;
+  }
+  float ss[C::PER_T];
+#pragma unroll
+  for (int r = 0; r < C::PER_T; ++r) ss[r] = 0.f;
+
+  u32x4 wr[C::PER_T], xr[C::PER_T];
+  auto load_stage = [&](int ks) {
+    const size_t koff = (size_t)ks * C::BKK * C::E + sch * 16;
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      wr[r] = wrow[r] ? *reinterpret_cast<const u32x4*>(wrow[r] + koff) : u32x4{0, 0, 0, 0};
+      xr[r] = xrow[r] ? *reinterpret_cast<const u32x4*>(xrow[r] + koff) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_stage = [&](int buf, int ks) {
+    u32x4 gw{0, 0, 0, 0};
+    if (a.norm_w != nullptr)
+      gw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.norm_w) + (size_t)ks * C::BKK * C::E + sch * 16);
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      const int row = srow0 + 32 * r;
+      ss[r] += chunk_sumsq<T>(xr[r]);
+      const u32x4 xv = a.norm_w != nullptr ? chunk_scale<T>(xr[r], gw) : xr[r];
+      *reinterpret_cast<u32x4*>(&smem[buf][0][row * 128 + ((sch ^ swz8(row)) << 4)]) = wr[r];
+      *reinterpret_cast<u32x4*>(&smem[buf][1][row * 128 + ((sch ^ swz8(row)) << 4)]) = xv;
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
+
+  const int nks = a.D / C::BKK;
+  load_stage(0);
+  store_stage(0, 0);
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
+    const bool has_next = ks + 1 < nks;
+    if (has_next) load_stage(ks + 1);
+    const char* wt_tile = smem[buf][0];
+    const char* xt_tile = smem[buf][1];
+#pragma unroll
+    for (int kc = 0; kc < C::NKS; ++kc) {
+      typename Elem<T>::frag af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = lds_frag_row<T>(wt_tile, wf * 64 + i * 32 + r32, kc, g);
+        bfr[i] = lds_frag_row<T>(xt_tile, wt * 64 + i * 32 + r32, kc, g);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma32(af[i], bfr[jj], acc[i][jj]);
+    }
+    if (has_next) store_stage(buf ^ 1, ks + 1);
+    __syncthreads();
+  }
+
+  // Row factors: the 8 threads of a staging row group hold partial sums.
+#pragma unroll
+  for (int r = 0; r < C::PER_T; ++r) {
+    float s = ss[r];
+    s += dpp_f32<kDppQuadSwap1>(s);
+    s += dpp_f32<kDppQuadSwap2>(s);
+    s += dpp_f32<kDppRowHalfMirror>(s);
+    if (sch == 0) rs_lds[srow0 + 32 * r] = 1.0f / sqrtf(s / (float)a.D + a.eps);
+  }
+  __syncthreads();
+
+  // Epilogue: acc[i][jj][e] = C^T[feature f0 + wf*64 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*64 + jj*32 + r32]
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int tl = wt * 64 + jj * 32 + r32;
+    const int tok = t0 + tl;
+    if (tok >= M) continue;
+    const float rs = rs_lds[tl];
+    const int bb = tok / a.N, n = tok % a.N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int f = f0 + wf * 64 + i * 32 + 8 * qd + 4 * g;
+        if (f >= F) continue;
+        const int which = f >= HD;
+        const int fr = which ? f - HD : f;
+        const int hh = fr / a.d, c = fr % a.d;
+        T* dst = static_cast<T*>(which ? a.v_out : a.k_out) +
+                 ((size_t)(bb * a.Hkv + hh) * a.n_cap + a.pos0 + n) * a.d + c;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[i][jj][4 * qd + e] * rs);
+          *reinterpret_cast<bf16x4*>(dst) = v4;
+        } else {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = acc[i][jj][4 * qd + e] * rs;
+          *reinterpret_cast<f32x4*>(dst) = v4;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream) {
+  const int F = 2 * a.Hkv * a.d;
+  const int M = a.B * a.N;
+  dim3 grid((M + 127) / 128, F / 128);
+  if (is_bf16)
+    hipLaunchKernelGGL((kv_proj_kernel<bf16>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((kv_proj_kernel<float>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

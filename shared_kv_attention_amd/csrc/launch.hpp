@@ -1,0 +1,72 @@
+// Internal interface between the C ABI (abi.cpp) and the HIP kernels.
+// Argument blocks are passed to kernels by value; every pointer is a device
+// pointer that abi.cpp has already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace yoco {
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // may be null
+  int B, Hq, Hkv, Nq;
+  int n_kv;            // valid key rows (keys >= n_kv are never read)
+  int kv_rows;         // rows per head in the k/v buffers
+  int q_offset;        // absolute position of query row 0
+  int window;          // sliding window (only read by the window variant)
+  float scale_log2;    // softmax scale * log2(e)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_scale;    // fp8 caches only
+  const float* v_scale;
+  const int32_t* ctx_lens; // may be null
+  int ctx;
+  float* part_o;           // [B, Hq, n_splits, d]
+  float* part_m;           // [B, Hq, n_splits]  (log2 domain)
+  float* part_l;           // [B, Hq, n_splits]
+  void* o;
+  float* lse;              // may be null
+  int B, Hq, Hkv, n_cap;
+  int n_splits, chunk, n_hg;
+  float scale_log2;
+};
+
+struct ProjArgs {
+  const void* x;
+  const void* norm_w;  // may be null
+  const void* w_k;
+  const void* w_v;
+  void* k_out;
+  void* v_out;
+  int B, N, D, Hkv, d, n_cap, pos0;
+  float eps;
+};
+
+struct QuantArgs {
+  const void* kv;
+  uint8_t* codes;
+  float* scale;
+  uint32_t* amax_bits;  // workspace [Hkv]
+  int B, Hkv;
+  long long slab;       // n * d elements per (batch, head)
+};
+
+hipError_t launch_attn(const AttnArgs& a, bool is_bf16, int d, bool swa, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hipStream_t stream);
+hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream);
+hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream);
+
+// Split plan of the decode kernel; the workspace size follows from it.
+void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int* n_hg);
+
+}  // namespace yoco

@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU.
+
+* libyoco.so loads and exports every function include/yoco.h declares;
+* every status code is reachable: argument validation runs before any HIP
+  call, so each single-fault call below returns its error without touching
+  a device (no compute is launched here);
+* workspace queries are consistent.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import shared_kv_attention_amd as yk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "yoco.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WS, HIP = range(8)
+P = 4096          # an aligned, never-dereferenced fake device address
+MIS = 4096 + 4    # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return yk.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(yoco_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert yk.yoco_version() == 100
+    seen = set()
+    for s in range(8):
+        msg = yk.yoco_status_string(s)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert yk.yoco_status_string(99) == "unknown status"
+
+
+def proj(L, **kw):
+    a = dict(x=P, g=None, wk=P, wv=P, ko=P, vo=P, B=1, N=8, D=128, Hkv=2, d=64, n_cap=16, pos0=0, eps=1e-6,
+             dt=yk.BF16)
+    a.update(kw)
+    return L.yoco_global_kv_proj(a["x"], a["g"], a["wk"], a["wv"], a["ko"], a["vo"], a["B"], a["N"], a["D"],
+                                 a["Hkv"], a["d"], a["n_cap"], a["pos0"], a["eps"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(wv=None), NULL), (dict(vo=None), NULL),
+    (dict(dt=yk.FP8_E4M3), DTYPE), (dict(dt=7), DTYPE),
+    (dict(N=0), SHAPE), (dict(pos0=-1), SHAPE), (dict(pos0=9), SHAPE), (dict(n_cap=7), SHAPE),
+    (dict(eps=float("nan")), SHAPE), (dict(eps=-1.0), SHAPE), (dict(Hkv=0), SHAPE),
+    (dict(d=96), UNSUP), (dict(D=100), UNSUP),
+    (dict(x=MIS), ALIGN), (dict(g=MIS), ALIGN), (dict(ko=MIS), ALIGN),
+])
+def test_global_kv_proj_errors(L, kw, code):
+    assert proj(L, **kw) == code
+
+
+def swa(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, N=64, d=128, W=16, scale=0.0, dt=yk.BF16)
+    a.update(kw)
+    return L.yoco_swa_attn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"],
+                           a["W"], a["scale"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(o=None), NULL),
+    (dict(dt=yk.FP8_E4M3), DTYPE),
+    (dict(Hq=6, Hkv=4), SHAPE), (dict(W=0), SHAPE), (dict(N=0), SHAPE), (dict(B=0), SHAPE),
+    (dict(scale=float("inf")), SHAPE),
+    (dict(d=32), UNSUP), (dict(d=256), UNSUP),
+    (dict(v=MIS), ALIGN), (dict(lse=4096 + 2), ALIGN),
+])
+def test_swa_errors(L, kw, code):
+    assert swa(L, **kw) == code
+
+
+def prefill(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Nq=8, n_kv=32, n_cap=40, off=24, d=64, scale=0.0,
+             dt=yk.F32)
+    a.update(kw)
+    return L.yoco_cross_attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                     a["Nq"], a["n_kv"], a["n_cap"], a["off"], a["d"], a["scale"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), NULL), (dict(dt=5), DTYPE),
+    (dict(off=25), SHAPE), (dict(off=-1), SHAPE), (dict(n_kv=41), SHAPE), (dict(n_cap=0), SHAPE),
+    (dict(Nq=0), SHAPE), (dict(d=100), UNSUP), (dict(q=MIS), ALIGN),
+])
+def test_cross_prefill_errors(L, kw, code):
+    assert prefill(L, **kw) == code
+
+
+def decode(L, **kw):
+    a = dict(q=P, k=P, v=P, ks=None, vs=None, cl=None, ctx=100, o=P, lse=None, B=2, Hq=8, Hkv=2, n_cap=128, d=128,
+             scale=0.0, qdt=yk.BF16, kvdt=yk.BF16, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.yoco_cross_attn_decode(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["cl"], a["ctx"], a["o"], a["lse"],
+                                    a["B"], a["Hq"], a["Hkv"], a["n_cap"], a["d"], a["scale"], a["qdt"], a["kvdt"],
+                                    a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(v=None), NULL), (dict(kvdt=yk.FP8_E4M3), NULL),
+    (dict(kvdt=yk.FP8_E4M3, ks=P), NULL),
+    (dict(qdt=yk.F32), DTYPE), (dict(qdt=yk.FP8_E4M3, kvdt=yk.FP8_E4M3, ks=P, vs=P), DTYPE),
+    (dict(qdt=yk.F32, kvdt=yk.FP8_E4M3, ks=P, vs=P), DTYPE),
+    (dict(ctx=0), SHAPE), (dict(ctx=129), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(B=0), SHAPE),
+    (dict(scale=float("nan")), SHAPE),
+    (dict(d=80), UNSUP),
+    (dict(o=MIS), ALIGN), (dict(cl=4096 + 2), ALIGN), (dict(ws=MIS), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=16), WS),
+])
+def test_decode_errors(L, kw, code):
+    assert decode(L, **kw) == code
+
+
+def test_decode_workspace_query():
+    need = yk.yoco_cross_attn_decode_workspace_bytes(2, 8, 2, 100, 128)
+    assert need > 0 and need % 16 == 0
+    big = yk.yoco_cross_attn_decode_workspace_bytes(16, 32, 8, 32768, 128)
+    assert big > need
+    # at least one partial (d + 2 floats) per (b, q-head)
+    assert big >= 16 * 32 * 130 * 4
+    for bad in [(0, 8, 2, 100, 128), (2, 6, 4, 100, 128), (2, 8, 2, 0, 128), (2, 8, 2, 100, 96)]:
+        assert yk.yoco_cross_attn_decode_workspace_bytes(*bad) == 0
+
+
+def test_decode_exact_workspace_boundary(L):
+    need = yk.yoco_cross_attn_decode_workspace_bytes(2, 8, 2, 100, 128)
+    assert decode(L, wsb=need - 1) == WS
+
+
+def quant(L, **kw):
+    a = dict(kv=P, dt=yk.F32, codes=P, scale=P, B=2, Hkv=4, n=10, d=64, ws=P, wsb=64)
+    a.update(kw)
+    return L.yoco_kv_quantize_fp8(a["kv"], a["dt"], a["codes"], a["scale"], a["B"], a["Hkv"], a["n"], a["d"],
+                                  a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=None), NULL), (dict(scale=None), NULL), (dict(dt=yk.FP8_E4M3), DTYPE),
+    (dict(n=0), SHAPE), (dict(Hkv=0), SHAPE), (dict(d=48), UNSUP), (dict(codes=MIS), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=15), WS),
+])
+def test_quantize_errors(L, kw, code):
+    assert quant(L, **kw) == code
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(yk, "library_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(yk, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        yk.lib()

@@ -1,0 +1,144 @@
+"""GPU parity of yoco_swa_attn and yoco_cross_attn_prefill against the oracle,
+and the method's invariants on the kernels (causality, window locality,
+sharing, constant values, determinism)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import shared_kv_attention_amd as yk
+from shared_kv_attention_amd.synth import randn
+from tests._tol import check, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(B, Hq, Hkv, Nq, Nk, d, dt, seed):
+    q = randn((B, Hq, Nq, d), seed, dtype=dt, device=DEV)
+    k = randn((B, Hkv, Nk, d), seed + 1, dtype=dt, device=DEV)
+    v = randn((B, Hkv, Nk, d), seed + 2, dtype=dt, device=DEV)
+    return q, k, v
+
+
+SWA_CASES = [
+    # B, Hq, Hkv, N, d, W, dtype
+    (1, 4, 1, 256, 64, 32, "f32"),       # tiny-block shapes
+    (2, 6, 2, 300, 128, 70, "bf16"),     # ragged tail, several tiles
+    (1, 8, 2, 200, 64, 1, "bf16"),       # window 1
+    (1, 3, 1, 130, 128, 1000, "bf16"),   # window >= N: causal
+    (2, 4, 4, 333, 128, 129, "f32"),
+    (1, 24, 8, 517, 128, 256, "bf16"),   # 3B head grouping
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,W,dt", SWA_CASES)
+def test_swa_parity(B, Hq, Hkv, N, d, W, dt):
+    print(f"swa parity B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} W={W} {dt}", flush=True)
+    q, k, v = _inputs(B, Hq, Hkv, N, N, d, dt, 100)
+    lse = torch.empty(B, Hq, N, dtype=torch.float32, device=DEV)
+    o = yk.yoco_swa_attn(q, k, v, W, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.swa_attention(to64(q), to64(k), to64(v), W)
+    check(to64(o), ro, dt, "swa O", rel_axes=(2, 3))
+    tol = 1e-5 if dt == "f32" else 1e-3
+    assert np.abs(to64(lse) - rl).max() <= tol
+
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, Nq, n_kv, n_cap, q_offset, d, dtype
+    (1, 4, 1, 256, 256, 256, 0, 64, "f32"),
+    (2, 6, 2, 190, 190, 256, 0, 128, "bf16"),
+    (1, 8, 2, 70, 300, 320, 230, 128, "bf16"),   # chunk of queries at an offset
+    (2, 4, 2, 1, 257, 300, 256, 64, "bf16"),     # a single (last) position
+    (1, 24, 8, 400, 400, 400, 0, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,n_kv,n_cap,off,d,dt", PREFILL_CASES)
+def test_cross_prefill_parity(B, Hq, Hkv, Nq, n_kv, n_cap, off, d, dt):
+    print(f"prefill parity B={B} Hq={Hq} Nq={Nq} n_kv={n_kv} n_cap={n_cap} off={off} d={d} {dt}", flush=True)
+    q, k, v = _inputs(B, Hq, Hkv, Nq, n_cap, d, dt, 200)
+    if n_cap > n_kv:   # rows past the valid ones hold garbage that must never be read
+        k[:, :, n_kv:] = float("nan")
+        v[:, :, n_kv:] = float("nan")
+    lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=DEV)
+    o = yk.yoco_cross_attn_prefill(q, k, v, n_kv=n_kv, q_offset=off, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.cross_prefill_attention(to64(q), to64(k)[:, :, :n_kv], to64(v)[:, :, :n_kv], n_kv=n_kv,
+                                            q_offset=off)
+    check(to64(o), ro, dt, "prefill O", rel_axes=(2, 3))
+    tol = 1e-5 if dt == "f32" else 1e-3
+    assert np.abs(to64(lse) - rl).max() <= tol
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_causality_bitwise_on_gpu(dt):
+    B, Hq, Hkv, N, d = 1, 4, 2, 300, 128
+    q, k, v = _inputs(B, Hq, Hkv, N, N, d, dt, 300)
+    t_star = 150
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    for t in (q2, k2, v2):
+        t[:, :, t_star + 1:] = 1e4 * torch.sign(randn(t[:, :, t_star + 1:].shape, 7, dtype=dt, device=DEV))
+    for fn in (lambda a, b_, c: yk.yoco_swa_attn(a, b_, c, 64),
+               lambda a, b_, c: yk.yoco_cross_attn_prefill(a, b_, c)):
+        o1, o2 = fn(q, k, v), fn(q2, k2, v2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[:, :, :t_star + 1], o2[:, :, :t_star + 1])
+
+
+def test_window_locality_bitwise_on_gpu():
+    B, Hq, Hkv, N, d, W = 1, 4, 1, 400, 128, 100
+    q, k, v = _inputs(B, Hq, Hkv, N, N, d, "bf16", 400)
+    t0 = 250
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, :t0 - W + 1] = 1e4
+    v2[:, :, :t0 - W + 1] = -1e4
+    o1 = yk.yoco_swa_attn(q, k, v, W)
+    o2 = yk.yoco_swa_attn(q, k2, v2, W)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, t0:], o2[:, :, t0:])
+
+
+def test_sharing_shared_cache_equals_copies_bitwise():
+    """Several cross layers reading one cache == each reading its own copy."""
+    B, Hq, Hkv, N, d = 1, 8, 2, 260, 128
+    _, k, v = _inputs(B, Hq, Hkv, N, N, d, "bf16", 500)
+    outs_shared, outs_copy = [], []
+    for layer in range(3):
+        q = randn((B, Hq, N, d), 510 + layer, device=DEV)
+        outs_shared.append(yk.yoco_cross_attn_prefill(q, k, v))
+        outs_copy.append(yk.yoco_cross_attn_prefill(q, k.clone(), v.clone()))
+    torch.cuda.synchronize()
+    for a, b in zip(outs_shared, outs_copy):
+        assert torch.equal(a, b)
+
+
+def test_constant_values_give_ones_and_rows_sum_to_one():
+    B, Hq, Hkv, N, d = 1, 4, 2, 200, 128
+    q, k, _ = _inputs(B, Hq, Hkv, N, N, d, "bf16", 600)
+    v = torch.ones(B, Hkv, N, d, dtype=torch.bfloat16, device=DEV)
+    for o in (yk.yoco_swa_attn(q * 4, k * 4, v, 37), yk.yoco_cross_attn_prefill(q * 4, k * 4, v)):
+        torch.cuda.synchronize()
+        assert (o.float() - 1).abs().max().item() <= 2e-2
+
+
+def test_deterministic_rerun():
+    q, k, v = _inputs(2, 6, 2, 300, 300, 128, "bf16", 700)
+    a = yk.yoco_swa_attn(q, k, v, 50)
+    b = yk.yoco_swa_attn(q, k, v, 50)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_planted_key_dominates_across_tiles():
+    B, Hq, Hkv, N, d = 1, 4, 1, 512, 128
+    q, k, v = _inputs(B, Hq, Hkv, N, N, d, "bf16", 800)
+    # key 40 aligned with every query: dominates rows >= 40 in causal attention
+    k[0, 0, 40] = (q[0, :, 300:].float().mean(dim=(0, 1)) * 40).to(torch.bfloat16)
+    o = yk.yoco_cross_attn_prefill(q, k, v)
+    torch.cuda.synchronize()
+    ro, _ = oracle.cross_prefill_attention(to64(q), to64(k), to64(v), rows=list(range(300, 512)))
+    check(to64(o)[:, :, 300:], ro[:, :, 300:], "bf16", "planted", rel_axes=(2, 3))

@@ -1,0 +1,114 @@
+"""GPU parity of yoco_cross_attn_decode (bf16, f32, fp8-e4m3 caches) and of the
+fp8 cache writer yoco_kv_quantize_fp8 against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import shared_kv_attention_amd as yk
+from shared_kv_attention_amd.synth import randn
+from tests._tol import check, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, n_cap, ctx, ctx_lens, d, dtype
+    (1, 4, 1, 256, 256, None, 64, "f32"),
+    (3, 8, 2, 1000, 1000, [1000, 1, 517], 128, "bf16"),
+    (2, 24, 8, 4096, 4096, None, 128, "bf16"),
+    (2, 6, 2, 700, 650, [650, 333], 64, "bf16"),
+    (2, 12, 2, 300, 300, None, 128, "bf16"),      # 6 query heads per KV head: two head groups
+    (1, 4, 4, 5000, 4999, None, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,n_cap,ctx,ctx_lens,d,dt", DECODE_CASES)
+def test_decode_parity(B, Hq, Hkv, n_cap, ctx, ctx_lens, d, dt):
+    print(f"decode parity B={B} Hq={Hq} Hkv={Hkv} n_cap={n_cap} ctx={ctx} lens={ctx_lens} d={d} {dt}", flush=True)
+    q = randn((B, Hq, d), 900, dtype=dt, device=DEV)
+    k = randn((B, Hkv, n_cap, d), 901, dtype=dt, device=DEV)
+    v = randn((B, Hkv, n_cap, d), 902, dtype=dt, device=DEV)
+    lens = [ctx] * B if ctx_lens is None else ctx_lens
+    for b in range(B):   # rows >= ctx_b must never be read
+        k[b, :, lens[b]:] = float("nan")
+        v[b, :, lens[b]:] = float("nan")
+    cl = None if ctx_lens is None else torch.tensor(ctx_lens, dtype=torch.int32, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+    o = yk.yoco_cross_attn_decode(q, k, v, ctx, ctx_lens=cl, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_attention(to64(q), to64(k), to64(v), lens)
+    check(to64(o), ro, dt, "decode O", rel_axes=(2,))
+    assert np.abs(to64(lse) - rl).max() <= (1e-5 if dt == "f32" else 1e-3)
+
+
+def test_decode_planted_key_at_split_boundaries():
+    B, Hq, Hkv, n, d = 1, 4, 1, 20000, 128
+    q = randn((B, Hq, d), 910, device=DEV)
+    k = randn((B, Hkv, n, d), 911, device=DEV)
+    v = randn((B, Hkv, n, d), 912, device=DEV)
+    for s in (0, 255, 256, 10000, n - 1):
+        k2 = k.clone()
+        k2[0, 0, s] = (q[0].float().mean(0) * 30).to(torch.bfloat16)
+        o = yk.yoco_cross_attn_decode(q, k2, v, n)
+        torch.cuda.synchronize()
+        ro, _ = oracle.decode_attention(to64(q), to64(k2), to64(v), [n])
+        check(to64(o), ro, "bf16", f"planted key at {s}", rel_axes=(2,))
+
+
+def test_decode_matches_prefill_last_row():
+    """Early exit: the last prompt position through decode == through prefill."""
+    B, Hq, Hkv, N, d = 2, 8, 2, 777, 128
+    q = randn((B, Hq, N, d), 920, device=DEV)
+    k = randn((B, Hkv, N, d), 921, device=DEV)
+    v = randn((B, Hkv, N, d), 922, device=DEV)
+    op = yk.yoco_cross_attn_prefill(q, k, v)
+    od = yk.yoco_cross_attn_decode(q[:, :, -1].contiguous(), k, v, N)
+    torch.cuda.synchronize()
+    ro, _ = oracle.decode_attention(to64(q)[:, :, -1], to64(k), to64(v), [N] * B)
+    check(to64(od), ro, "bf16", "decode last row", rel_axes=(2,))
+    check(to64(op)[:, :, -1], ro, "bf16", "prefill last row", rel_axes=(2,))
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_quantize_fp8_bit_exact(src):
+    B, Hkv, n, d = 2, 4, 333, 128
+    kv = randn((B, Hkv, n, d), 930, dtype=src, device=DEV)
+    kv[:, 1] *= 37.0
+    kv[:, 2] = 0
+    kv[:, 3] *= 1e-3
+    codes, scale = yk.yoco_kv_quantize_fp8(kv)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_kv_fp8(kv.float().cpu().numpy())
+    assert np.array_equal(scale.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_decode_fp8_parity():
+    B, Hq, Hkv, n, d = 2, 8, 2, 3000, 128
+    q = randn((B, Hq, d), 940, device=DEV)
+    kf = randn((B, Hkv, n, d), 941, dtype="f32", device=DEV)
+    vf = randn((B, Hkv, n, d), 942, dtype="f32", device=DEV)
+    kc, ks = yk.yoco_kv_quantize_fp8(kf)
+    vc, vs = yk.yoco_kv_quantize_fp8(vf)
+    cl = torch.tensor([3000, 1234], dtype=torch.int32, device=DEV)
+    o = yk.yoco_cross_attn_decode(q, kc, vc, n, ctx_lens=cl, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    kd = oracle.dequantize_kv_fp8(kc.cpu().numpy(), ks.cpu().numpy())
+    vd = oracle.dequantize_kv_fp8(vc.cpu().numpy(), vs.cpu().numpy())
+    ro, _ = oracle.decode_attention(to64(q), kd, vd, [3000, 1234])
+    check(to64(o), ro, "bf16", "fp8 decode", rel_axes=(2,))
+    # quantisation error against the unquantised cache is reported, not gated
+    ru, _ = oracle.decode_attention(to64(q), to64(kf), to64(vf), [3000, 1234])
+    print("fp8 cache: max |O - O_unquantised| =", np.abs(to64(o) - ru).max())
+
+
+def test_decode_constant_values():
+    B, Hq, Hkv, n, d = 2, 8, 2, 2000, 128
+    q = randn((B, Hq, d), 950, device=DEV) * 5
+    k = randn((B, Hkv, n, d), 951, device=DEV) * 5
+    v = torch.ones(B, Hkv, n, d, dtype=torch.bfloat16, device=DEV)
+    o = yk.yoco_cross_attn_decode(q, k, v, n)
+    torch.cuda.synchronize()
+    assert (o.float() - 1).abs().max().item() <= 2e-2
