@@ -1,0 +1,344 @@
+"""Benchmark of the YOCO shared-KV attention hot path on one MI355X.
+
+Default workload (the one the headline metric is quoted on): the 3B-shaped
+bf16 prefill -- batch 1, 4096 tokens, hidden 3072, 24 query / 8 KV heads,
+head_dim 128; 8 sliding-window layers (window 1024), one global KV
+projection, 8 causal cross-decoder layers over the one shared cache.
+One step = that whole pass over one batch; value = algorithmic TFLOP/s of
+the step (unmasked query-key pairs only, 2 flops per MAC, exp not counted).
+
+The same run also measures the cross-attention decode kernel at its own
+headline shape (batch 16, context 32768, 32/8 heads, 16 cross layers x 128
+steps) and reports its HBM GB/s, and times the float64 CPU oracle on a
+bounded sample of the prefill step ("cpu_baseline").
+
+Prints ONE JSON line.  Inputs are seeded synthetic tensors already resident
+in HBM when timing starts.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import shared_kv_attention_amd as yk  # noqa: E402
+from shared_kv_attention_amd.synth import WORKLOADS, randn, seed_for  # noqa: E402
+
+METRIC = "cross-attn decode KV GB/s (% HBM peak); prefill TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ---------------------------------------------------------------- counting
+def swa_pairs(n, w):
+    """Number of (query, key) pairs with t - W < s <= t."""
+    full = min(n, w)
+    return full * (full + 1) // 2 + (n - full) * w
+
+
+def causal_pairs(nq, q_offset=0):
+    """Pairs with s <= q_offset + i for query rows i = 0..nq-1."""
+    return nq * q_offset + nq * (nq + 1) // 2
+
+
+def attn_flops(pairs, heads, d, batch):
+    return 4.0 * d * heads * batch * pairs          # QK^T and PV, 2 flops per MAC
+
+
+def proj_flops(batch, n, hidden, kv_width):
+    return 2.0 * batch * n * hidden * 2 * kv_width
+
+
+def decode_bytes(batch, hkv, ctx, d, hq, kv_bytes, q_bytes):
+    return 2.0 * batch * hkv * ctx * d * kv_bytes + 2.0 * batch * hq * d * q_bytes
+
+
+# ---------------------------------------------------------------- helpers
+def events_ms(pairs):
+    return [s.elapsed_time(e) for s, e in pairs]
+
+
+def kernel_source_digest(name):
+    with open(os.path.join(ROOT, "shared_kv_attention_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(summary_name, kernel_file, per_launch_key):
+    """HBM bytes per launch from a committed counter summary, if the kernel is unchanged."""
+    path = os.path.join(PROFILES, summary_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source sha256/16:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_digest(kernel_file):
+        return None
+    m = re.search(per_launch_key + r":\s*([0-9.eE+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+# ---------------------------------------------------------------- prefill step
+class PrefillStep:
+    def __init__(self, wl, dev):
+        self.wl = wl
+        B, N, D, Hq, Hkv, d = wl.batch, wl.seq, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim
+        wid = wl.wid
+        self.x = randn((B, N, D), seed_for(wid, 0), device=dev)
+        self.wk = randn((Hkv * d, D), seed_for(wid, 1), std=wl.weight_std, device=dev)
+        self.wv = randn((Hkv * d, D), seed_for(wid, 2), std=wl.weight_std, device=dev)
+        self.swa = []
+        for layer in range(wl.n_self_layers):
+            s0 = seed_for(wid, 10 + 3 * layer)
+            self.swa.append((randn((B, Hq, N, d), s0, device=dev),
+                             randn((B, Hkv, N, d), s0 + 1, device=dev),
+                             randn((B, Hkv, N, d), s0 + 2, device=dev)))
+        self.cross_q = [randn((B, Hq, N, d), seed_for(wid, 200 + layer), device=dev)
+                        for layer in range(wl.n_cross_layers)]
+        self.kc = torch.empty(B, Hkv, N, d, dtype=torch.bfloat16, device=dev)
+        self.vc = torch.empty_like(self.kc)
+        self.o_swa = [torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=dev) for _ in self.swa]
+        self.o_cross = [torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=dev) for _ in self.cross_q]
+        self.flops_swa = attn_flops(swa_pairs(N, wl.window), Hq, d, B)
+        self.flops_cross = attn_flops(causal_pairs(N), Hq, d, B)
+        self.flops_proj = proj_flops(B, N, D, Hkv * d)
+        self.flops = (wl.n_self_layers * self.flops_swa + self.flops_proj
+                      + wl.n_cross_layers * self.flops_cross)
+
+    def run(self, ev=None):
+        wl = self.wl
+        for (q, k, v), o in zip(self.swa, self.o_swa):
+            yk.yoco_swa_attn(q, k, v, wl.window, o=o)
+        yk.yoco_global_kv_proj(self.x, self.wk, self.wv, self.kc, self.vc)
+        for q, o in zip(self.cross_q, self.o_cross):
+            if ev is not None:
+                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s.record()
+                yk.yoco_cross_attn_prefill(q, self.kc, self.vc, o=o)
+                e.record()
+                ev.append((s, e))
+            else:
+                yk.yoco_cross_attn_prefill(q, self.kc, self.vc, o=o)
+
+
+def cpu_baseline_prefill(step, budget_s):
+    """Time the float64 oracle on a sample of the prefill step's rows."""
+    import numpy as np
+
+    import oracle
+    wl = step.wl
+    N, Hq, d, W = wl.seq, wl.n_heads, wl.head_dim, wl.window
+    f = lambda t: t.double().cpu().numpy()  # noqa: E731
+    # sample: every `stride`-th query row of every head of one SWA layer and
+    # one cross layer, and every `stride`-th token of the projection
+    stride = 64
+    rows = list(range(stride // 2, N, stride))
+    q, k, v = (f(t) for t in step.swa[0])
+    kc, vc, qc = f(step.kc), f(step.vc), f(step.cross_q[0])
+    x, wk, wv = f(step.x), f(step.wk), f(step.wv)
+    flops = 0.0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.swa_attention(q, k, v, W, rows=rows)
+        flops += sum(4.0 * d * Hq * min(t + 1, W) for t in rows)
+        oracle.cross_prefill_attention(qc, kc, vc, rows=rows)
+        flops += sum(4.0 * d * Hq * (t + 1) for t in rows)
+        oracle.global_kv_proj(x, wk, wv, wl.n_kv_heads, d, rows=rows)
+        flops += proj_flops(1, len(rows), wl.hidden, wl.n_kv_heads * d)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        pass
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads or cores,
+        "host_cores": cores,
+        "kind": "oracle",
+        "sample": (f"{reps}x: {len(rows)} query rows (every {stride}th) x {Hq} heads of one SWA layer "
+                   f"and one cross layer, plus {len(rows)} projection tokens; float64 numpy, "
+                   f"{dt:.1f} s wall"),
+    }
+
+
+# ---------------------------------------------------------------- decode
+def run_decode(wl, dev, steps):
+    B, ctx, Hq, Hkv, d, L = wl.batch, wl.seq, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.n_cross_layers
+    wid = wl.wid
+    fp8 = wl.dtype == "fp8-kv"
+    if fp8:
+        kf = randn((B, Hkv, ctx, d), seed_for(wid, 0), dtype="f32", device=dev)
+        kc, ks = yk.yoco_kv_quantize_fp8(kf)
+        del kf
+        vf = randn((B, Hkv, ctx, d), seed_for(wid, 1), dtype="f32", device=dev)
+        vc, vs = yk.yoco_kv_quantize_fp8(vf)
+        del vf
+        kv_bytes = 1
+    else:
+        kc = randn((B, Hkv, ctx, d), seed_for(wid, 0), device=dev)
+        vc = randn((B, Hkv, ctx, d), seed_for(wid, 1), device=dev)
+        ks = vs = None
+        kv_bytes = 2
+    qs = randn((L, B, Hq, d), seed_for(wid, 2), device=dev)
+    o = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(yk.yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d), dtype=torch.uint8, device=dev)
+
+    def call(layer):
+        yk.yoco_cross_attn_decode(qs[layer], kc, vc, ctx, k_scale=ks, v_scale=vs, o=o, workspace=ws)
+
+    for layer in range(min(L, 4)):   # warm-up
+        call(layer)
+    torch.cuda.synchronize()
+    ev = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        for layer in range(L):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            call(layer)
+            e.record()
+            ev.append((s, e))
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per_call = sum(events_ms(ev)) / len(ev)
+    nbytes = decode_bytes(B, Hkv, ctx, d, Hq, kv_bytes, 2)
+    gbs = nbytes / (per_call * 1e-3) / 1e9
+    return {
+        "workload": wl.name,
+        "calls": len(ev),
+        "ms_per_call": per_call,
+        "total_ms": total_ms,
+        "bytes_per_call": nbytes,
+        "GB/s": gbs,
+        "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profile(f"decode_split_{wl.name}.txt", "decode.hip",
+                                                     "hbm bytes per launch")},
+        "timing": "HIP events around each call (split kernel + combine kernel)",
+    }
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128,
+                    help="decode steps (x16 cross layers) of the 32K-context decode measurement")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--fp8-decode", action="store_true",
+                    help="also measure the 512K fp8-cache decode (allocates ~40 GB)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    yk.lib()
+
+    wl = WORKLOADS["prefill_3b_bf16"]
+    step = PrefillStep(wl, dev)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    ev = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step.run(ev)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tflops = step.flops / (ms * 1e-3) / 1e12
+
+    attn_ms = sum(events_ms(ev)) / len(ev)
+    attn_tflops = step.flops_cross / (attn_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": "attn_fwd_kernel<bf16,128,causal> (yoco_cross_attn_prefill)",
+        "achieved": attn_tflops,
+        "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": attn_tflops / BF16_PEAK_TFLOPS,
+        "traffic": traffic_from_profile("attn_fwd_prefill_3b_bf16.txt", "attn_fwd.hip", "hbm bytes per launch"),
+        "flops_per_launch": step.flops_cross,
+        "ms_per_launch": attn_ms,
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations/queries/keys/values, N(0,0.02) weights)",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "seq_len": wl.seq, "hidden": wl.hidden,
+            "q_heads": wl.n_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+            "self_layers": wl.n_self_layers, "window": wl.window, "cross_layers": wl.n_cross_layers,
+            "step": "8x sliding-window attention + 1x global KV projection + 8x causal cross prefill",
+            "flops_per_step": step.flops,
+        },
+        "frac_mfma_peak": tflops / BF16_PEAK_TFLOPS,
+        "roofline": roofline,
+    }
+    del step
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        out["decode"] = run_decode(WORKLOADS["decode_32k_bf16"], dev, args.decode_steps)
+        torch.cuda.empty_cache()
+    if args.fp8_decode:
+        out["decode_fp8"] = run_decode(WORKLOADS["decode_512k_fp8"], dev, WORKLOADS["decode_512k_fp8"].decode_steps)
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        step = PrefillStep(wl, dev)
+        out["cpu_baseline"] = cpu_baseline_prefill(step, args.cpu_budget)
+        del step
+    else:
+        out["cpu_baseline"] = None
+
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
