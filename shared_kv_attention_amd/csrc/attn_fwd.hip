@@ -141,7 +141,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2][2][C::TILE_BYTES];  // [buf][K|V]
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, g = l >> 5, r32 = l & 31;
+  // wave index as a scalar: every wave-level decision below is a scalar branch
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, g = l >> 5, r32 = l & 31;
 
   // ---- workgroup -> (batch, head, query tile) ----
   const int BH = a.B * a.Hq;
@@ -161,6 +163,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int q_first = qt * C::BQ;
   const int qi = q_first + w * 32 + r32;
   const int pos = a.q_offset + qi;
+  const int lo_key = SWA ? max(0, pos - a.window + 1) : 0;   // allowed keys of this row
+  const int hi_key = min(pos, a.n_kv - 1);
   frag qf[C::NC];
   if (qi < a.Nq) {
     const T* qrow = qbase + (size_t)qi * D;
@@ -240,23 +244,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < C::NC; ++c) s[kb] = mma32(lds_frag_k<T, D>(ktile, krow, c, g), qf[c], s[kb]);
       }
-      // element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8*g + i%8
-      float mloc = -INFINITY;
+      // element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8*g + i%8.
+      // Masked scores become -inf (a select, never an additive mask).
+      float mraw = -INFINITY;
+      if (need_mask) {
+        // allowed keys of this lane's row: [lo_key, hi_key]; one unsigned range test per score
+        const unsigned span = (unsigned)(hi_key - lo_key);
+        const int base = k0 + 8 * g - lo_key;
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
+        for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[kb][i] * a.scale_log2;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-            const bool ok = key <= pos && key < a.n_kv && (!SWA || key > pos - a.window);
-            x = ok ? x : -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int off = kb * 32 + 16 * (i >> 3) + (i & 7);
+            const float x = ((unsigned)(base + off) <= span) ? s[kb][i] : -INFINITY;
+            s[kb][i] = x;
+            mraw = fmaxf(mraw, x);
           }
-          s[kb][i] = x;
-          mloc = fmaxf(mloc, x);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[kb][i]);
         }
       }
-      mloc = fmaxf(mloc, xor32(mloc));
+      mraw = fmaxf(mraw, xor32(mraw));
+      const float mloc = mraw * a.scale_log2;   // scale > 0: max commutes with it
       // Each row decides from its own scores only (rows of a wave never
       // influence each other, so results are bitwise causal).
       const bool up = mloc > m_run + 8.0f;
@@ -267,13 +280,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
         for (int db = 0; db < C::NDB; ++db) acc_o[db] *= alpha;
         m_run = up ? mloc : m_run;
       }
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[kb][i] - mref);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, neg_m));
           s[kb][i] = p;
           lsum += p;
         }

@@ -271,25 +271,63 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (query head, batch); thread = output dim.
+// Merge of the split partials: one 256-thread workgroup per (query head,
+// batch).  The maximum, the weights 2^(m_s - M) and the denominator are
+// reduced over splits in parallel; then 256/D thread groups sum strided
+// subsets of the splits' partial numerators (coalesced rows) and meet in LDS.
+constexpr int kMaxSplits = 4096;
+
+__device__ __forceinline__ float block256_reduce(float x, bool is_max, float* red4) {
+  x = is_max ? row16_max(x) : row16_sum(x);
+  const float y16 = __shfl_xor(x, 16);
+  x = is_max ? fmaxf(x, y16) : x + y16;
+  const float y32 = __shfl_xor(x, 32);
+  x = is_max ? fmaxf(x, y32) : x + y32;
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const float r = is_max ? fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]))
+                         : (red4[0] + red4[1]) + (red4[2] + red4[3]);
+  __syncthreads();
+  return r;
+}
+
 template <typename OT, int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, dim = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int NG = 256 / D;
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red4[4];
+  __shared__ float part[NG][D];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int S = a.n_splits;
   const int ctx_b = decode_ctx(a, b);
   const int ns = (ctx_b + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)(b * a.Hq + h) * S;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_m[base + s]);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wgt = __builtin_amdgcn_exp2f(a.part_m[base + s] - M);
-    L = fmaf(wgt, a.part_l[base + s], L);
-    acc = fmaf(wgt, a.part_o[(base + s) * D + dim], acc);
+
+  float m = -INFINITY;
+  for (int s = tid; s < ns; s += 256) m = fmaxf(m, a.part_m[base + s]);
+  const float M = block256_reduce(m, true, red4);
+  float lsum = 0.f;
+  for (int s = tid; s < ns; s += 256) {
+    const float w = __builtin_amdgcn_exp2f(a.part_m[base + s] - M);
+    wgt[s] = w;
+    lsum = fmaf(w, a.part_l[base + s], lsum);
   }
-  OT* o = static_cast<OT*>(a.o) + (size_t)(b * a.Hq + h) * D;
-  o[dim] = from_f32<OT>(acc / L);
-  if (a.lse != nullptr && dim == 0) a.lse[b * a.Hq + h] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+  const float L = block256_reduce(lsum, false, red4);   // its barriers also publish wgt[]
+
+  const int dim = tid % D, grp = tid / D;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int s = grp; s < ns; s += NG) acc = fmaf(wgt[s], a.part_o[(base + s) * D + dim], acc);
+  part[grp][dim] = acc;
+  __syncthreads();
+  if (grp == 0) {
+    float tot = part[0][dim];
+#pragma unroll
+    for (int g2 = 1; g2 < NG; ++g2) tot += part[g2][dim];
+    OT* o = static_cast<OT*>(a.o) + (size_t)(b * a.Hq + h) * D;
+    o[dim] = from_f32<OT>(tot / L);
+    if (a.lse != nullptr && dim == 0) a.lse[b * a.Hq + h] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+  }
 }
 
 template <typename QT, typename KVT, int D>
@@ -298,7 +336,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<QT, D>), dim3(a.Hq, a.B), dim3(D), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<QT, D>), dim3(a.Hq, a.B), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -320,6 +358,7 @@ void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int
   if (s < 1) s = 1;
   long long c = (ctx + s - 1) / s;
   c = (c + 63) / 64 * 64;
+  if ((ctx + c - 1) / c > kMaxSplits) c = ((ctx + kMaxSplits - 1) / kMaxSplits + 63) / 64 * 64;
   *chunk = (int)c;
   *n_splits = (int)((ctx + c - 1) / c);
 }
