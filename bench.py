@@ -249,6 +249,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="run one elementwise bf16 copy (x * 1) of this many MiB, read and written once, "
+                         "as the known-size reference for HBM byte counters")
     ap.add_argument("--fp8-decode", action="store_true",
                     help="also measure the 512K fp8-cache decode (allocates ~40 GB)")
     args = ap.parse_args()
@@ -264,6 +267,13 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     yk.lib()
+
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.mul(src, 1)
+        torch.cuda.synchronize()
+        del src, dst
 
     wl = WORKLOADS["prefill_3b_bf16"]
     step = PrefillStep(wl, dev)

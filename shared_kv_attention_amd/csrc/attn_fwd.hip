@@ -37,31 +37,45 @@ namespace yoco {
 template <typename T, int D>
 struct AttnCfg {
   static constexpr int E = Elem<T>::bytes;
-  static constexpr int BQ = 128;
+  // 4 waves x 32 query rows.  (Two 32-row blocks per wave halve the LDS
+  // traffic per MFMA but need one wave per SIMD; measured slower.)
+  static constexpr int RB = 1;                  // 32-row blocks per wave
+  static constexpr int NW = 4;                  // waves per workgroup
+  static constexpr int NT = NW * 64;            // threads per workgroup
+  static constexpr int BQ = NW * 32 * RB;       // query rows per workgroup (128)
   static constexpr int BK = (E == 2) ? 64 : 32;
   static constexpr int CH = D * E / 16;         // 16-byte chunks per K/V row
-  static constexpr int PER_T = BK * CH / 256;   // chunks per thread per tensor
+  static constexpr int PER_T = BK * CH / NT;    // chunks per thread per tensor
   static constexpr int NKB = BK / 32;           // 32-key score blocks per tile
   static constexpr int NC = D / 16;             // 16-deep k steps over d
   static constexpr int NDB = D / 32;            // 32-wide dim blocks of O
   static constexpr int NPC = BK / 16;           // 16-key steps of P V
   static constexpr int TILE_BYTES = BK * D * E;
-  static_assert(PER_T >= 1 && BK * CH % 256 == 0, "tile must split over 256 threads");
+  static_assert(PER_T >= 1 && BK * CH % NT == 0, "tile must split over the workgroup");
+  static constexpr int MIN_WAVES_PER_EU = (RB == 2) ? 1 : 2;
 };
-
-// Swizzle of the 16-byte chunk index within a row of the K tile: the 32 rows a
-// wave reads at once (bit-permuted order) land on distinct chunk columns.
-template <int CH>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (CH >= 16) return row & 15;
-  else return (row & 3) | ((row >> 1) & 4);
-}
-// V tile: the transpose loads read 4 consecutive rows x 32 bytes per 16 lanes.
-__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
 
 // Row index permutation: swap bits 2 and 3.
 __device__ __forceinline__ int sigma(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// XOR swizzles of the 16-byte chunk index within a tile row, chosen so that
+// the reads of one instruction spread over all banks whether the LDS serves
+// 8 or 16 lanes of 16-byte accesses per cycle.
+// K tile: a wave reads 32 rows at once in the permuted order sigma(r): rows
+// sigma(0..7) and sigma(0..15) map to distinct chunk columns.
+template <int CH>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (CH >= 16) return sigma(row) & 15;
+  else return (row & 3) | ((row >> 1) & 4);
+}
+// V tile: the transpose loads of 16 lanes read 4 consecutive rows x 32 bytes;
+// 32 lanes read the same 4 rows x 64 bytes.
+template <int CH>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (CH >= 16) return 4 * (row & 3) + 2 * ((row >> 1) & 1);
+  else return 2 * (row & 3);
 }
 
 template <typename T>
@@ -113,7 +127,7 @@ __device__ __forceinline__ typename Elem<T>::frag lds_frag_vt(const char* tile, 
       const int row = 16 * c + 8 * (G >> 1) + 4 * hh + (j16 >> 2);
       const int col = db * 32 + 16 * (G & 1) + 4 * (j16 & 3);
       const int ch = col >> 3;
-      const char* p = tile + row * C::CH * 16 + ((ch ^ swz_v(row)) << 4) + ((col & 7) << 1);
+      const char* p = tile + row * C::CH * 16 + ((ch ^ swz_v<C::CH>(row)) << 4) + ((col & 7) << 1);
       i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(p));
       bf16x4 rb = __builtin_bit_cast(bf16x4, r);
@@ -128,16 +142,17 @@ __device__ __forceinline__ typename Elem<T>::frag lds_frag_vt(const char* tile, 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 16 * c + 8 * g + j;
-      f[j] = *reinterpret_cast<const float*>(tile + row * C::CH * 16 + ((ch ^ swz_v(row)) << 4) + off);
+      f[j] = *reinterpret_cast<const float*>(tile + row * C::CH * 16 + ((ch ^ swz_v<C::CH>(row)) << 4) + off);
     }
   }
   return f;
 }
 
 template <typename T, int D, bool SWA>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_EU)) void attn_fwd_kernel(AttnArgs a) {
   using C = AttnCfg<T, D>;
   using frag = typename Elem<T>::frag;
+  constexpr int RB = C::RB;
   __shared__ __attribute__((aligned(16))) char smem[2][2][C::TILE_BYTES];  // [buf][K|V]
 
   const int tid = threadIdx.x;
@@ -159,20 +174,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const char* kbase = static_cast<const char*>(a.k) + ((size_t)(b * a.Hkv + kvh) * a.kv_rows) * D * C::E;
   const char* vbase = static_cast<const char*>(a.v) + ((size_t)(b * a.Hkv + kvh) * a.kv_rows) * D * C::E;
 
-  // ---- this lane's query row ----
+  // ---- this lane's query rows (one per 32-row block) ----
   const int q_first = qt * C::BQ;
-  const int qi = q_first + w * 32 + r32;
-  const int pos = a.q_offset + qi;
-  const int lo_key = SWA ? max(0, pos - a.window + 1) : 0;   // allowed keys of this row
-  const int hi_key = min(pos, a.n_kv - 1);
-  frag qf[C::NC];
-  if (qi < a.Nq) {
-    const T* qrow = qbase + (size_t)qi * D;
+  const int wq0 = q_first + w * 32 * RB;
+  int qi[RB], lo_key[RB], hi_key[RB];
+  frag qf[RB][C::NC];
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c) qf[c] = load_frag_global<T>(qrow + 16 * c + 8 * g);
-  } else {
+  for (int rb = 0; rb < RB; ++rb) {
+    qi[rb] = wq0 + rb * 32 + r32;
+    const int pos = a.q_offset + qi[rb];
+    lo_key[rb] = SWA ? max(0, pos - a.window + 1) : 0;   // allowed keys of this row
+    hi_key[rb] = min(pos, a.n_kv - 1);
+    if (qi[rb] < a.Nq) {
+      const T* qrow = qbase + (size_t)qi[rb] * D;
 #pragma unroll
-    for (int c = 0; c < C::NC; ++c) qf[c] = frag{};
+      for (int c = 0; c < C::NC; ++c) qf[rb][c] = load_frag_global<T>(qrow + 16 * c + 8 * g);
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) qf[rb][c] = frag{};
+    }
   }
 
   // ---- key-tile range of the workgroup and of this wave ----
@@ -180,53 +200,71 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const int P0 = a.q_offset + q_first, P1 = a.q_offset + q_last;
   const int t_lo = SWA ? max(0, P0 - a.window + 1) / C::BK : 0;
   const int t_hi = min(P1, a.n_kv - 1) / C::BK;
-  const int wq0 = q_first + w * 32;
   const bool wave_live = wq0 < a.Nq;
   const int pw0 = a.q_offset + wq0;
-  const int pw1 = a.q_offset + min(wq0 + 31, a.Nq - 1);
+  const int pw1 = a.q_offset + min(wq0 + 32 * RB - 1, a.Nq - 1);
 
-  // ---- cooperative tile staging ----
-  u32x4 kr[C::PER_T], vr[C::PER_T];
-  auto load_tile = [&](int t) {
+  // ---- cooperative tile staging: global -> LDS directly (no registers) ----
+  // Each wave instruction fills 64 consecutive 16-byte LDS slots (lane i ->
+  // slot base + i).  Slot P of a tile holds row P / CH at physical chunk
+  // P % CH, i.e. logical chunk (P % CH) ^ swizzle(row); so each lane fetches
+  // the global chunk that belongs in its slot.  Rows at or past n_kv are
+  // clamped to the last valid row (finite data, always masked out).
+  constexpr int ROWB = D * C::E;   // bytes per K/V row
+  unsigned koff[C::PER_T], voff[C::PER_T];   // loop-invariant byte offsets of this lane's slots
+  int srow[C::PER_T];
+#pragma unroll
+  for (int r = 0; r < C::PER_T; ++r) {
+    const int slot = C::NT * r + 64 * w + l;
+    const int row = slot / C::CH, pch = slot % C::CH;
+    srow[r] = row;
+    koff[r] = (unsigned)(row * ROWB + ((pch ^ swz_k<C::CH>(row)) << 4));
+    voff[r] = (unsigned)(row * ROWB + ((pch ^ swz_v<C::CH>(row)) << 4));
+  }
+  auto load_tile = [&](int t, int buf) {
+    const char* kt = kbase + (size_t)t * C::BK * ROWB;   // uniform tile base
+    const char* vt = vbase + (size_t)t * C::BK * ROWB;
+    const bool tail = (t + 1) * C::BK > a.n_kv;         // tile crosses the last valid row
 #pragma unroll
     for (int r = 0; r < C::PER_T; ++r) {
-      const int cid = tid + 256 * r;
-      const int row = cid / C::CH, ch = cid % C::CH;
-      const int key = t * C::BK + row;
-      if (key < a.n_kv) {
-        const size_t off = (size_t)key * (D * C::E) + ch * 16;
-        kr[r] = *reinterpret_cast<const u32x4*>(kbase + off);
-        vr[r] = *reinterpret_cast<const u32x4*>(vbase + off);
-      } else {
-        kr[r] = u32x4{0, 0, 0, 0};
-        vr[r] = u32x4{0, 0, 0, 0};
+      unsigned ko = koff[r], vo = voff[r];
+      if (tail) {
+        const int over = t * C::BK + srow[r] - (a.n_kv - 1);   // rows past n_kv-1 re-read row n_kv-1
+        if (over > 0) {
+          ko -= (unsigned)(over * ROWB);
+          vo -= (unsigned)(over * ROWB);
+        }
       }
+      char* kdst = &smem[buf][0][(C::NT * r + 64 * w) * 16];
+      char* vdst = &smem[buf][1][(C::NT * r + 64 * w) * 16];
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(kt + ko),
+                                       (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vt + vo),
+                                       (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < C::PER_T; ++r) {
-      const int cid = tid + 256 * r;
-      const int row = cid / C::CH, ch = cid % C::CH;
-      *reinterpret_cast<u32x4*>(&smem[buf][0][row * C::CH * 16 + ((ch ^ swz_k<C::CH>(row)) << 4)]) = kr[r];
-      *reinterpret_cast<u32x4*>(&smem[buf][1][row * C::CH * 16 + ((ch ^ swz_v(row)) << 4)]) = vr[r];
-    }
-  };
+  // the tile's LDS writes land asynchronously: wait for them before the
+  // barrier that hands the buffer to the other waves
+  auto tile_landed = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  f32x16 acc_o[C::NDB];
+  f32x16 acc_o[RB][C::NDB];
+  float m_run[RB], l_run[RB];   // running max (log2 domain) and this lane's partial denominator
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) acc_o[db] = f32x16{};
-  float m_run = -INFINITY;   // running max (log2 domain) of this lane's row
-  float l_run = 0.f;         // this lane's partial softmax denominator
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc_o[rb][db] = f32x16{};
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
 
-  load_tile(t_lo);
-  store_tile(0);
+  load_tile(t_lo, 0);
+  tile_landed();
   __syncthreads();
 
   for (int t = t_lo; t <= t_hi; ++t) {
     const int buf = (t - t_lo) & 1;
     const bool has_next = t < t_hi;
-    if (has_next) load_tile(t + 1);
+    if (has_next) load_tile(t + 1, buf ^ 1);   // buffer buf^1 was released by the last barrier
 
     const int k0 = t * C::BK, k1 = k0 + C::BK - 1;
     const bool skip = !wave_live || k0 > pw1 || (SWA && k1 <= pw0 - a.window);
@@ -235,109 +273,127 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       const char* ktile = smem[buf][0];
       const char* vtile = smem[buf][1];
 
-      // S^T = K Q^T for NKB blocks of 32 keys
-      f32x16 s[C::NKB];
+      // S^T = K Q^T: each K fragment serves every row block of the wave
+      f32x16 s[RB][C::NKB];
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) {
-        s[kb] = f32x16{};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = f32x16{};
         const int krow = kb * 32 + sigma(r32);
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) s[kb] = mma32(lds_frag_k<T, D>(ktile, krow, c, g), qf[c], s[kb]);
+        for (int c = 0; c < C::NC; ++c) {
+          const frag kf = lds_frag_k<T, D>(ktile, krow, c, g);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mma32(kf, qf[rb][c], s[rb][kb]);
+        }
       }
-      // element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8*g + i%8.
-      // Masked scores become -inf (a select, never an additive mask).
-      float mraw = -INFINITY;
-      if (need_mask) {
-        // allowed keys of this lane's row: [lo_key, hi_key]; one unsigned range test per score
-        const unsigned span = (unsigned)(hi_key - lo_key);
-        const int base = k0 + 8 * g - lo_key;
+
+      frag pf[RB][C::NPC];
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
+      for (int rb = 0; rb < RB; ++rb) {
+        // element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8*g + i%8.
+        // Masked scores become -inf (a select, never an additive mask).
+        float mraw = -INFINITY;
+        if (need_mask) {
+          // allowed keys of this lane's row: [lo_key, hi_key]; one unsigned range test per score
+          const unsigned span = (unsigned)(hi_key[rb] - lo_key[rb]);
+          const int base = k0 + 8 * g - lo_key[rb];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int off = kb * 32 + 16 * (i >> 3) + (i & 7);
-            const float x = ((unsigned)(base + off) <= span) ? s[kb][i] : -INFINITY;
-            s[kb][i] = x;
-            mraw = fmaxf(mraw, x);
+          for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int off = kb * 32 + 16 * (i >> 3) + (i & 7);
+              const float x = ((unsigned)(base + off) <= span) ? s[rb][kb][i] : -INFINITY;
+              s[rb][kb][i] = x;
+              mraw = fmaxf(mraw, x);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[rb][kb][i]);
           }
         }
-      } else {
+        mraw = fmaxf(mraw, xor32(mraw));
+        const float mloc = mraw * a.scale_log2;   // scale > 0: max commutes with it
+        // Each row decides from its own scores only (rows never influence
+        // each other, so results are bitwise causal).
+        const bool up = mloc > m_run[rb] + 8.0f;
+        if (__any(up)) {
+          const float alpha = !up ? 1.f : (m_run[rb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - mloc));
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) acc_o[rb][db] *= alpha;
+          m_run[rb] = up ? mloc : m_run[rb];
+        }
+        const float neg_m = (m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[kb][i]);
+          for (int i = 0; i < 16; ++i) s[rb][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[rb][kb][i], a.scale_log2, neg_m));
         }
-      }
-      mraw = fmaxf(mraw, xor32(mraw));
-      const float mloc = mraw * a.scale_log2;   // scale > 0: max commutes with it
-      // Each row decides from its own scores only (rows of a wave never
-      // influence each other, so results are bitwise causal).
-      const bool up = mloc > m_run + 8.0f;
-      if (__any(up)) {
-        const float alpha = !up ? 1.f : (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mloc));
-        l_run *= alpha;
+        // P^T fragments: step c covers keys 16c .. 16c+15 of the tile
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) acc_o[db] *= alpha;
-        m_run = up ? mloc : m_run;
-      }
-      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-      float lsum = 0.f;
+        for (int c = 0; c < C::NPC; ++c) {
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, neg_m));
-          s[kb][i] = p;
-          lsum += p;
+          for (int jj = 0; jj < 8; ++jj) pf[rb][c][jj] = from_f32<T>(s[rb][c >> 1][8 * (c & 1) + jj]);
         }
-      }
-      l_run += lsum;
-
-      // P^T fragments: step c covers keys 16c .. 16c+15 of the tile
-      frag pf[C::NPC];
+        // float32 row sum (4 independent partial sums for instruction-level parallelism)
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < C::NPC; ++c) {
+        for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) pf[c][jj] = from_f32<T>(s[c >> 1][8 * (c & 1) + jj]);
+          for (int i = 0; i < 16; ++i) ls[i & 3] += s[rb][kb][i];
+        }
+        const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        l_run[rb] += lsum;
       }
-      // O^T += V^T P^T
+      // O^T += V^T P^T: each V^T fragment serves every row block of the wave
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-        for (int c = 0; c < C::NPC; ++c) acc_o[db] = mma32(lds_frag_vt<T, D>(vtile, c, db, l), pf[c], acc_o[db]);
+        for (int c = 0; c < C::NPC; ++c) {
+          const frag vf = lds_frag_vt<T, D>(vtile, c, db, l);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = mma32(vf, pf[rb][c], acc_o[rb][db]);
+        }
       }
     }
 
-    if (has_next) store_tile(buf ^ 1);
+    if (has_next) tile_landed();
     __syncthreads();
   }
 
   // ---- normalise and write ----
-  if (qi < a.Nq) {
-    const float l_tot = l_run + xor32(l_run);
-    const float inv = 1.f / l_tot;
-    T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qi) * D;
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = l_run[rb] + xor32(l_run[rb]);
+    if (qi[rb] < a.Nq) {
+      const float inv = 1.f / l_tot;
+      T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qi[rb]) * D;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int dim = db * 32 + 8 * qd + 4 * g;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 v4;
+      for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc_o[db][4 * qd + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + dim) = v4;
-        } else {
-          f32x4 v4;
+        for (int qd = 0; qd < 4; ++qd) {
+          const int dim = db * 32 + 8 * qd + 4 * g;
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = acc_o[db][4 * qd + e] * inv;
-          *reinterpret_cast<f32x4*>(orow + dim) = v4;
+            for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc_o[rb][db][4 * qd + e] * inv);
+            *reinterpret_cast<bf16x4*>(orow + dim) = v4;
+          } else {
+            f32x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = acc_o[rb][db][4 * qd + e] * inv;
+            *reinterpret_cast<f32x4*>(orow + dim) = v4;
+          }
         }
       }
-    }
-    if (a.lse != nullptr && g == 0) {
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-      a.lse[(size_t)(b * a.Hq + h) * a.Nq + qi] = (mref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      if (a.lse != nullptr && g == 0) {
+        const float mref = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+        a.lse[(size_t)(b * a.Hq + h) * a.Nq + qi[rb]] = (mref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      }
     }
   }
 }
@@ -346,7 +402,7 @@ template <typename T, int D, bool SWA>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
   const int nqt = (a.Nq + AttnCfg<T, D>::BQ - 1) / AttnCfg<T, D>::BQ;
   const long long nblocks = (long long)nqt * a.B * a.Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, SWA>), dim3((unsigned)nblocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, SWA>), dim3((unsigned)nblocks), dim3(AttnCfg<T, D>::NT), 0, stream, a);
   return hipGetLastError();
 }
 

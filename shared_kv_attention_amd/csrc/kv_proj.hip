@@ -37,7 +37,10 @@ struct ProjCfg {
   static constexpr int TILE_BYTES = 128 * 128;
 };
 
-__device__ __forceinline__ int swz8(int row) { return row & 7; }
+// XOR swizzle of the 16-byte chunk index within a 128-byte tile row: the 32
+// rows a wave reads at once spread over all banks whether the LDS serves 8
+// or 16 lanes of 16-byte accesses per cycle.
+__device__ __forceinline__ int swz8(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag lds_frag_row(const char* tile, int row, int kc, int g) {
