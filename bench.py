@@ -238,6 +238,79 @@ def run_decode(wl, dev, steps):
     }
 
 
+# ---------------------------------------------------------------- early exit
+def run_early_exit(wl, dev, steps):
+    """1M-token early-exit prefill: L_s SWA layers over all tokens, the global
+    KV projection of all tokens, then the cross-decoder for the last position
+    only (one decode call per cross layer over the full cache)."""
+    B, N, D, Hq, Hkv, d, W = wl.batch, wl.seq, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    wid = wl.wid
+    layers = []
+    for layer in range(wl.n_self_layers):
+        s0 = seed_for(wid, 10 + 3 * layer)
+        layers.append((randn((B, Hq, N, d), s0, device=dev), randn((B, Hkv, N, d), s0 + 1, device=dev),
+                       randn((B, Hkv, N, d), s0 + 2, device=dev)))
+    o = torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=dev)
+    x = randn((B, N, D), seed_for(wid, 0), device=dev)
+    wk = randn((Hkv * d, D), seed_for(wid, 1), std=wl.weight_std, device=dev)
+    wv = randn((Hkv * d, D), seed_for(wid, 2), std=wl.weight_std, device=dev)
+    kc = torch.empty(B, Hkv, N, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    ql = randn((wl.n_cross_layers, B, Hq, d), seed_for(wid, 300), device=dev)
+    od = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(yk.yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8, device=dev)
+    ev = {"swa": [], "proj": [], "decode": []}
+
+    def timed(key, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        ev[key].append((s, e))
+
+    def step(record):
+        for q, k, v in layers:
+            f = lambda: yk.yoco_swa_attn(q, k, v, W, o=o)  # noqa: E731
+            timed("swa", f) if record else f()
+        f = lambda: yk.yoco_global_kv_proj(x, wk, wv, kc, vc)  # noqa: E731
+        timed("proj", f) if record else f()
+        for layer in range(wl.n_cross_layers):
+            f = lambda: yk.yoco_cross_attn_decode(ql[layer], kc, vc, N, o=od, workspace=ws)  # noqa: E731
+            timed("decode", f) if record else f()
+
+    step(False)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    swa_ms = sum(events_ms(ev["swa"])) / len(ev["swa"])
+    proj_ms = sum(events_ms(ev["proj"])) / len(ev["proj"])
+    dec_ms = sum(events_ms(ev["decode"])) / len(ev["decode"])
+    f_swa = attn_flops(swa_pairs(N, W), Hq, d, B)
+    f_proj = proj_flops(B, N, D, Hkv * d)
+    dbytes = decode_bytes(B, Hkv, N, d, Hq, 2, 2)
+    flops = wl.n_self_layers * f_swa + f_proj + wl.n_cross_layers * attn_flops(N, Hq, d, B)
+    full_cross = wl.n_cross_layers * attn_flops(causal_pairs(N), Hq, d, B)
+    return {
+        "workload": wl.name,
+        "ms_per_step": ms,
+        "steps": steps,
+        "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+        "swa": {"ms": swa_ms, "TFLOP/s": f_swa / (swa_ms * 1e-3) / 1e12,
+                "frac_mfma_peak": f_swa / (swa_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "kv_proj": {"ms": proj_ms, "TFLOP/s": f_proj / (proj_ms * 1e-3) / 1e12,
+                    "frac_mfma_peak": f_proj / (proj_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "last_token_decode": {"ms": dec_ms, "GB/s": dbytes / (dec_ms * 1e-3) / 1e9,
+                              "frac_hbm_peak": dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "cross_decoder_flops_skipped_by_early_exit": full_cross,
+        "timing": "HIP events around every call of each step",
+    }
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -252,8 +325,11 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="run one elementwise bf16 copy (x * 1) of this many MiB, read and written once, "
                          "as the known-size reference for HBM byte counters")
-    ap.add_argument("--fp8-decode", action="store_true",
-                    help="also measure the 512K fp8-cache decode (allocates ~40 GB)")
+    ap.add_argument("--no-fp8-decode", action="store_true",
+                    help="skip the 512K fp8-cache decode measurement (allocates ~26 GB)")
+    ap.add_argument("--no-early-exit", action="store_true",
+                    help="skip the 1M-token early-exit flow measurement (allocates ~110 GB)")
+    ap.add_argument("--extra-steps", type=int, default=3, help="steps of the 1M early-exit flow")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -336,8 +412,11 @@ def main():
     if not args.no_decode:
         out["decode"] = run_decode(WORKLOADS["decode_32k_bf16"], dev, args.decode_steps)
         torch.cuda.empty_cache()
-    if args.fp8_decode:
+    if not args.no_fp8_decode:
         out["decode_fp8"] = run_decode(WORKLOADS["decode_512k_fp8"], dev, WORKLOADS["decode_512k_fp8"].decode_steps)
+        torch.cuda.empty_cache()
+    if not args.no_early_exit:
+        out["early_exit_1m"] = run_early_exit(WORKLOADS["early_exit_1m_bf16"], dev, args.extra_steps)
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
