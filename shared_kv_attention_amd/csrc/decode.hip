@@ -19,10 +19,13 @@
 //    (row r -> head r%4), so every lane receives all 4 heads' scores of its
 //    own key.
 //  * For P V each lane owns D/64 output dims across all keys: one V row is
-//    read by one load instruction (fully contiguous), the probabilities of
-//    key j are taken from lane j as wave-uniform scalars (readlane), and the
-//    per-lane accumulator is only 4 heads x D/64 floats -- no cross-lane
-//    reduction of O is ever needed and occupancy stays high.
+//    read by one load instruction (fully contiguous), and the per-lane
+//    accumulator is only 4 heads x D/64 floats -- no cross-lane reduction of
+//    O is ever needed and occupancy stays high.  Probabilities reach the
+//    lanes as wave-uniform scalars (readlane); for bf16 / fp8 caches two keys
+//    are handled per v_dot2_f32_bf16 (probabilities rounded to bf16, as in
+//    any bf16 attention; float32 accumulation), for float32 caches by exact
+//    float32 FMAs.
 //  * Online softmax in the exp2 domain; the running max per head is raised
 //    only when a block exceeds it by 2^8 (wave-uniform branch).
 //  * The next block's loads are issued before the current block is used.
@@ -231,16 +234,63 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
       l_run[i] += p[i];
     }
-    // P V: key j's probabilities are read from lane j as wave-uniform scalars
+    if constexpr (sizeof(KVT) == 4) {
+      // float32 cache: exact float32 products; key j's probabilities are
+      // read from lane j as wave-uniform scalars
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float vf[DPL];
-      vslice_to_f32<KVT, DPL>(vc[j], vf);
+      for (int j = 0; j < 16; ++j) {
+        float vf[DPL];
+        vslice_to_f32<KVT, DPL>(vc[j], vf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pjf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[i]), j));
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[i][e] = fmaf(pjf, vf[e], acc[i][e]);
+        }
+      }
+    } else {
+      // bf16 / fp8 cache: two keys per instruction with v_dot2_f32_bf16.
+      // Lane 2m packs (p_2m, p_2m+1) as bf16x2 (neighbour via DPP); the pair
+      // is read as a wave-uniform scalar.  The V values of keys 2m, 2m+1 at
+      // the same dim are paired with a byte permute (fp8 codes are decoded
+      // exactly to bf16 first).  Accumulation stays float32.
+      uint32_t pp[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pjf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p[i]), j));
+        const float nb = dpp_f32<kDppQuadSwap1>(p[i]);
+        pp[i] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)p[i], (bf16)nb});
+      }
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[i][e] = fmaf(pjf, vf[e], acc[i][e]);
+      for (int m = 0; m < 8; ++m) {
+        bf16x2 ps[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps[i] = __builtin_bit_cast(bf16x2, (uint32_t)__builtin_amdgcn_readlane((int)pp[i], 2 * m));
+        bf16x2 vp[DPL];
+        if constexpr (sizeof(KVT) == 2) {
+          if constexpr (DPL == 2) {
+            vp[0] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm((uint32_t)vc[2 * m + 1], (uint32_t)vc[2 * m], 0x05040100u));
+            vp[1] = __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm((uint32_t)vc[2 * m + 1], (uint32_t)vc[2 * m], 0x07060302u));
+          } else {
+            vp[0] = __builtin_bit_cast(bf16x2, (uint32_t)vc[2 * m] | ((uint32_t)vc[2 * m + 1] << 16));
+          }
+        } else {
+          if constexpr (DPL == 2) {
+            const uint32_t w = (uint32_t)vc[2 * m] | ((uint32_t)vc[2 * m + 1] << 16);   // a0 a1 b0 b1
+            const uint32_t x = __builtin_amdgcn_perm(w, w, 0x03010200u);                  // a0 b0 a1 b1
+            const f32x2 lo = fp8x2_to_f32(x, false), hi = fp8x2_to_f32(x, true);
+            vp[0] = bf16x2{(bf16)lo[0], (bf16)lo[1]};   // exact conversions
+            vp[1] = bf16x2{(bf16)hi[0], (bf16)hi[1]};
+          } else {
+            const uint32_t w = (uint32_t)vc[2 * m] | ((uint32_t)vc[2 * m + 1] << 8);
+            const f32x2 lo = fp8x2_to_f32(w, false);
+            vp[0] = bf16x2{(bf16)lo[0], (bf16)lo[1]};
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[i][e] = __builtin_amdgcn_fdot2_f32_bf16(ps[i], vp[e], acc[i][e], false);
+        }
       }
     }
     if (has_next) {
