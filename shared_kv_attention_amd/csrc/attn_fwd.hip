@@ -26,7 +26,8 @@
 //  * Masking is a select to -inf on tiles that straddle a boundary; tiles
 //    entirely outside a wave's rows are skipped.  Keys past the valid rows
 //    are never loaded (zero-filled), so stale cache memory cannot leak in.
-//  * Grid order: heaviest query tiles first (causal), and within each round
+//  * Grid order: heaviest query tiles first (causal; natural order for the
+//    sliding window, whose tiles all cost the same), and within each round
 //    the heads of one KV head are placed on one XCD (workgroups go to the 8
 //    XCDs round-robin), so each XCD's L2 holds one KV head's K/V.
 #include "common.hpp"
@@ -164,7 +165,9 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
   const int BH = a.B * a.Hq;
   const int nqt = (a.Nq + C::BQ - 1) / C::BQ;
   const int id = blockIdx.x;
-  const int qt = nqt - 1 - id / BH;          // heaviest (latest) tiles first
+  // causal: heaviest (latest) query tiles first; sliding window: all tiles
+  // cost the same, and the natural order lets neighbouring windows share L2
+  const int qt = SWA ? id / BH : nqt - 1 - id / BH;
   int j = id % BH;
   if ((BH & 7) == 0) j = (j & 7) * (BH >> 3) + (j >> 3);   // same KV head -> same XCD
   const int b = j / a.Hq, h = j % a.Hq;
