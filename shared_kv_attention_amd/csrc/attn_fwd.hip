@@ -154,7 +154,12 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
   using C = AttnCfg<T, D>;
   using frag = typename Elem<T>::frag;
   constexpr int RB = C::RB;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][C::TILE_BYTES];  // [buf][K|V]
+  // Two buffer sets as distinct LDS objects, used in a statically alternating
+  // order (the tile loop is unrolled by two): the compiler can then see that
+  // the asynchronous loads into one set never alias reads of the other, and
+  // does not wait for them before the current tile's LDS reads.
+  __shared__ __attribute__((aligned(16))) char kbuf0[C::TILE_BYTES], vbuf0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char kbuf1[C::TILE_BYTES], vbuf1[C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   // wave index as a scalar: every wave-level decision below is a scalar branch
@@ -224,7 +229,7 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
     koff[r] = (unsigned)(row * ROWB + ((pch ^ swz_k<C::CH>(row)) << 4));
     voff[r] = (unsigned)(row * ROWB + ((pch ^ swz_v<C::CH>(row)) << 4));
   }
-  auto load_tile = [&](int t, int buf) {
+  auto load_tile = [&](int t, char* kdst_tile, char* vdst_tile) {
     const char* kt = kbase + (size_t)t * C::BK * ROWB;   // uniform tile base
     const char* vt = vbase + (size_t)t * C::BK * ROWB;
     const bool tail = (t + 1) * C::BK > a.n_kv;         // tile crosses the last valid row
@@ -238,8 +243,8 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
           vo -= (unsigned)(over * ROWB);
         }
       }
-      char* kdst = &smem[buf][0][(C::NT * r + 64 * w) * 16];
-      char* vdst = &smem[buf][1][(C::NT * r + 64 * w) * 16];
+      char* kdst = kdst_tile + (C::NT * r + 64 * w) * 16;
+      char* vdst = vdst_tile + (C::NT * r + 64 * w) * 16;
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(kt + ko),
                                        (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vt + vo),
@@ -260,21 +265,15 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
     l_run[rb] = 0.f;
   }
 
-  load_tile(t_lo, 0);
-  tile_landed();
-  __syncthreads();
-
-  for (int t = t_lo; t <= t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
+  // one tile: compute from (ktile, vtile) while tile t+1 streams into (knext, vnext)
+  auto tile_step = [&](int t, const char* ktile, const char* vtile, char* knext, char* vnext)
+      __attribute__((always_inline)) {
     const bool has_next = t < t_hi;
-    if (has_next) load_tile(t + 1, buf ^ 1);   // buffer buf^1 was released by the last barrier
-
+    if (has_next) load_tile(t + 1, knext, vnext);   // this set was released by the last barrier
     const int k0 = t * C::BK, k1 = k0 + C::BK - 1;
     const bool skip = !wave_live || k0 > pw1 || (SWA && k1 <= pw0 - a.window);
     if (!skip) {
       const bool need_mask = k1 > pw0 || k1 >= a.n_kv || (SWA && k0 <= pw1 - a.window);
-      const char* ktile = smem[buf][0];
-      const char* vtile = smem[buf][1];
 
       // S^T = K Q^T: each K fragment serves every row block of the wave
       f32x16 s[RB][C::NKB];
@@ -366,6 +365,14 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
 
     if (has_next) tile_landed();
     __syncthreads();
+  };
+
+  load_tile(t_lo, kbuf0, vbuf0);
+  tile_landed();
+  __syncthreads();
+  for (int t = t_lo; t <= t_hi; t += 2) {
+    tile_step(t, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (t + 1 <= t_hi) tile_step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
 
   // ---- normalise and write ----

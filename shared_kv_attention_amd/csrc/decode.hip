@@ -321,10 +321,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the split partials: one 256-thread workgroup per (query head,
-// batch).  The maximum, the weights 2^(m_s - M) and the denominator are
-// reduced over splits in parallel; then 256/D thread groups sum strided
-// subsets of the splits' partial numerators (coalesced rows) and meet in LDS.
+// Merge of the split partials.  The maximum, the weights 2^(m_s - M) and the
+// denominator are reduced over splits in parallel; then 8 thread groups sum
+// strided subsets of the splits' partial numerators (coalesced 128-byte rows,
+// four independent chains each) and meet in LDS.
 constexpr int kMaxSplits = 4096;
 
 __device__ __forceinline__ float block256_reduce(float x, bool is_max, float* red4) {
@@ -343,10 +343,12 @@ __device__ __forceinline__ float block256_reduce(float x, bool is_max, float* re
 
 template <typename OT, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int NG = 256 / D;
+  // grid (query head, batch, D / 32): each workgroup owns 32 output dims;
+  // its 256 threads are 8 split groups x 32 dims.
+  constexpr int NG = 8;
   __shared__ float wgt[kMaxSplits];
   __shared__ float red4[4];
-  __shared__ float part[NG][D];
+  __shared__ float part[NG][32];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int S = a.n_splits;
   const int ctx_b = decode_ctx(a, b);
@@ -364,16 +366,21 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
   const float L = block256_reduce(lsum, false, red4);   // its barriers also publish wgt[]
 
-  const int dim = tid % D, grp = tid / D;
-  float acc = 0.f;
-#pragma unroll 4
-  for (int s = grp; s < ns; s += NG) acc = fmaf(wgt[s], a.part_o[(base + s) * D + dim], acc);
-  part[grp][dim] = acc;
+  const int dl = tid & 31, grp = tid >> 5;
+  const int dim = blockIdx.z * 32 + dl;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};   // independent chains for memory-level parallelism
+  int s = grp;
+  for (; s + 3 * NG < ns; s += 4 * NG) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = fmaf(wgt[s + u * NG], a.part_o[(base + s + u * NG) * D + dim], acc[u]);
+  }
+  for (; s < ns; s += NG) acc[0] = fmaf(wgt[s], a.part_o[(base + s) * D + dim], acc[0]);
+  part[grp][dl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (grp == 0) {
-    float tot = part[0][dim];
+    float tot = part[0][dl];
 #pragma unroll
-    for (int g2 = 1; g2 < NG; ++g2) tot += part[g2][dim];
+    for (int g2 = 1; g2 < NG; ++g2) tot += part[g2][dl];
     OT* o = static_cast<OT*>(a.o) + (size_t)(b * a.Hq + h) * D;
     o[dim] = from_f32<OT>(tot / L);
     if (a.lse != nullptr && dim == 0) a.lse[b * a.Hq + h] = (M + __builtin_amdgcn_logf(L)) * kLn2;
@@ -386,7 +393,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<QT, D>), dim3(a.Hq, a.B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<QT, D>), dim3(a.Hq, a.B, D / 32), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -64,11 +64,12 @@ template <typename T>
 __device__ __forceinline__ float chunk_sumsq(u32x4 w) {
   float s = 0.f;
   if constexpr (sizeof(T) == 2) {
+    // products of bf16 values are exact in float32: x0^2 + x1^2 per instruction
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
-      s = fmaf(lo, lo, s);
-      s = fmaf(hi, hi, s);
+      const uint32_t wi = w[i];   // element to a scalar first (bit_cast of a vector element mis-compiles)
+      const bf16x2 x = __builtin_bit_cast(bf16x2, wi);
+      s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
     }
   } else {
 #pragma unroll
@@ -104,7 +105,11 @@ __device__ __forceinline__ u32x4 chunk_scale(u32x4 w, u32x4 gw) {
 template <typename T>
 __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
   using C = ProjCfg<T>;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][C::TILE_BYTES];   // [buf][W|X]
+  // two buffer sets as distinct LDS objects, alternated statically (the k
+  // loop is unrolled by two) so that the asynchronous W loads into one set are
+  // never mistaken for writes to the set being read
+  __shared__ __attribute__((aligned(16))) char wbuf0[C::TILE_BYTES], xbuf0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char wbuf1[C::TILE_BYTES], xbuf1[C::TILE_BYTES];
   __shared__ float rs_lds[C::BN];
 
   const int tid = threadIdx.x;
@@ -113,36 +118,62 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
   const int HD = a.Hkv * a.d;
   const int F = 2 * HD;
   const int M = a.B * a.N;
-  const int t0 = blockIdx.x * C::BN;
-  const int f0 = blockIdx.y * C::BM;
+  // Workgroup -> (token tile, feature tile).  With the feature tiles split
+  // evenly over the 8 XCDs (workgroups are dealt to XCDs round-robin), each
+  // XCD keeps its slice of W in its own L2 while all XCDs stream the same
+  // token tiles of X at the same time (X is read from HBM about once).
+  const int nft = F / C::BM;
+  const int ntt = (M + C::BN - 1) / C::BN;
+  const int id = blockIdx.x;
+  int tt, ft;
+  if (nft % 8 == 0) {
+    const int per = nft / 8, xcd = id & 7, sl = id >> 3;
+    ft = xcd * per + sl % per;
+    tt = sl / per;
+  } else {
+    ft = id % nft;
+    tt = id / nft;
+  }
+  const int t0 = tt * C::BN;
+  const int f0 = ft * C::BM;
+  (void)ntt;
 
-  // staging assignment: chunk id = tid + 256 r -> tile row id/8, chunk id%8
+  // staging: chunk slot P = 256 r + tid of a tile holds row P / 8 at physical
+  // chunk P % 8 (logical chunk (P % 8) ^ swizzle(row)).  W goes global -> LDS
+  // directly (each wave instruction fills 64 consecutive slots); X passes
+  // through registers because the row sums of squares (and the optional gain)
+  // are taken on the way.  Rows past the end are clamped to the last row
+  // (finite data; such tokens are never written).
   const int srow0 = tid >> 3, sch = tid & 7;
-  const char* wrow[C::PER_T];
+  const char* wsrc[C::PER_T];
   const char* xrow[C::PER_T];
 #pragma unroll
   for (int r = 0; r < C::PER_T; ++r) {
-    const int frow = f0 + srow0 + 32 * r;
-    const int trow = t0 + srow0 + 32 * r;
+    const int slot = 256 * r + 64 * w + l;          // == 256 r + tid
+    const int row = slot >> 3, pch = slot & 7;
+    const int frow = f0 + row;                        // F is a multiple of 128: always valid
     const void* wmat = frow < HD ? a.w_k : a.w_v;
     const int fr = frow < HD ? frow : frow - HD;
-    wrow[r] = frow < F ? static_cast<const char*>(wmat) + (size_t)fr * a.D * C::E : nullptr;
-    xrow[r] = trow < M ? static_cast<const char*>(a.x) + (size_t)trow * a.D * C::E : nullptr;
+    wsrc[r] = static_cast<const char*>(wmat) + (size_t)fr * a.D * C::E + ((pch ^ swz8(row)) << 4);
+    const int trow = min(t0 + srow0 + 32 * r, M - 1);
+    xrow[r] = static_cast<const char*>(a.x) + (size_t)trow * a.D * C::E + sch * 16;
   }
   float ss[C::PER_T];
 #pragma unroll
   for (int r = 0; r < C::PER_T; ++r) ss[r] = 0.f;
 
-  u32x4 wr[C::PER_T], xr[C::PER_T];
-  auto load_stage = [&](int ks) {
-    const size_t koff = (size_t)ks * C::BKK * C::E + sch * 16;
+  u32x4 xr[C::PER_T];
+  auto load_stage = [&](int ks, char* wdst) {
+    const size_t koff = (size_t)ks * C::BKK * C::E;
 #pragma unroll
     for (int r = 0; r < C::PER_T; ++r) {
-      wr[r] = wrow[r] ? *reinterpret_cast<const u32x4*>(wrow[r] + koff) : u32x4{0, 0, 0, 0};
-      xr[r] = xrow[r] ? *reinterpret_cast<const u32x4*>(xrow[r] + koff) : u32x4{0, 0, 0, 0};
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(wsrc[r] + koff),
+                                       (__attribute__((address_space(3))) void*)(wdst + (256 * r + 64 * w) * 16),
+                                       16, 0, 0);
+      xr[r] = *reinterpret_cast<const u32x4*>(xrow[r] + koff);
     }
   };
-  auto store_stage = [&](int buf, int ks) {
+  auto store_stage = [&](char* xdst, int ks) {
     u32x4 gw{0, 0, 0, 0};
     if (a.norm_w != nullptr)
       gw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.norm_w) + (size_t)ks * C::BKK * C::E + sch * 16);
@@ -151,10 +182,11 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
       const int row = srow0 + 32 * r;
       ss[r] += chunk_sumsq<T>(xr[r]);
       const u32x4 xv = a.norm_w != nullptr ? chunk_scale<T>(xr[r], gw) : xr[r];
-      *reinterpret_cast<u32x4*>(&smem[buf][0][row * 128 + ((sch ^ swz8(row)) << 4)]) = wr[r];
-      *reinterpret_cast<u32x4*>(&smem[buf][1][row * 128 + ((sch ^ swz8(row)) << 4)]) = xv;
+      *reinterpret_cast<u32x4*>(xdst + row * 128 + ((sch ^ swz8(row)) << 4)) = xv;
     }
   };
+  // W's LDS writes land asynchronously: wait for them before the barrier
+  auto landed = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -163,15 +195,10 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
 
   const int nks = a.D / C::BKK;
-  load_stage(0);
-  store_stage(0, 0);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
+  // one k stage: multiply from (wt_tile, xt_tile) while stage ks+1 is staged into (wn, xn)
+  auto kstep = [&](int ks, const char* wt_tile, const char* xt_tile, char* wn, char* xn) __attribute__((always_inline)) {
     const bool has_next = ks + 1 < nks;
-    if (has_next) load_stage(ks + 1);
-    const char* wt_tile = smem[buf][0];
-    const char* xt_tile = smem[buf][1];
+    if (has_next) load_stage(ks + 1, wn);
 #pragma unroll
     for (int kc = 0; kc < C::NKS; ++kc) {
       typename Elem<T>::frag af[2], bfr[2];
@@ -185,8 +212,19 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma32(af[i], bfr[jj], acc[i][jj]);
     }
-    if (has_next) store_stage(buf ^ 1, ks + 1);
+    if (has_next) {
+      store_stage(xn, ks + 1);
+      landed();
+    }
     __syncthreads();
+  };
+  load_stage(0, wbuf0);
+  store_stage(xbuf0, 0);
+  landed();
+  __syncthreads();
+  for (int ks = 0; ks < nks; ks += 2) {
+    kstep(ks, wbuf0, xbuf0, wbuf1, xbuf1);
+    if (ks + 1 < nks) kstep(ks + 1, wbuf1, xbuf1, wbuf0, xbuf0);
   }
 
   // Row factors: the 8 threads of a staging row group hold partial sums.
@@ -238,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream) {
   const int F = 2 * a.Hkv * a.d;
   const int M = a.B * a.N;
-  dim3 grid((M + 127) / 128, F / 128);
+  dim3 grid((unsigned)(((long long)(M + 127) / 128) * (F / 128)));
   if (is_bf16)
     hipLaunchKernelGGL((kv_proj_kernel<bf16>), grid, dim3(256), 0, stream, a);
   else
