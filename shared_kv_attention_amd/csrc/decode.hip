@@ -325,7 +325,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 // denominator are reduced over splits in parallel; then 8 thread groups sum
 // strided subsets of the splits' partial numerators (coalesced 128-byte rows,
 // four independent chains each) and meet in LDS.
-constexpr int kMaxSplits = 4096;
+constexpr int kMaxSplits = kDecodeMaxSplits;
 
 __device__ __forceinline__ float block256_reduce(float x, bool is_max, float* red4) {
   x = is_max ? row16_max(x) : row16_sum(x);
@@ -402,22 +402,6 @@ hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hi
   if (q_kind == 0) return d == 128 ? launch_decode_t<float, float, 128>(a, stream) : launch_decode_t<float, float, 64>(a, stream);
   if (kv_kind == 1) return d == 128 ? launch_decode_t<bf16, bf16, 128>(a, stream) : launch_decode_t<bf16, bf16, 64>(a, stream);
   return d == 128 ? launch_decode_t<bf16, uint8_t, 128>(a, stream) : launch_decode_t<bf16, uint8_t, 64>(a, stream);
-}
-
-void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int* n_hg) {
-  const int grp = Hq / Hkv;
-  *n_hg = (grp + 3) / 4;
-  const long long units = (long long)B * Hkv * (*n_hg);
-  const long long target = 4096;                       // workgroups (one wave each)
-  long long s = (target + units - 1) / units;
-  const long long max_s = (ctx + 255) / 256;           // at least 256 keys per split
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  long long c = (ctx + s - 1) / s;
-  c = (c + 63) / 64 * 64;
-  if ((ctx + c - 1) / c > kMaxSplits) c = ((ctx + kMaxSplits - 1) / kMaxSplits + 63) / 64 * 64;
-  *chunk = (int)c;
-  *n_splits = (int)((ctx + c - 1) / c);
 }
 
 }  // namespace yoco

@@ -66,7 +66,10 @@ hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hi
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream);
 
-// Split plan of the decode kernel; the workspace size follows from it.
+// Split plan of the decode kernel (host code, plan.cpp); the workspace size
+// follows from it.  At most kDecodeMaxSplits splits (the combine pass keeps one
+// weight per split in LDS).
+constexpr int kDecodeMaxSplits = 4096;
 void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int* n_hg);
 
 }  // namespace yoco

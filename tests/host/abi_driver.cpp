@@ -1,0 +1,118 @@
+// Drives every entry point of the C ABI on the host with stub launchers:
+// valid argument sets must reach the launcher with the expected argument
+// block, invalid ones must return their status without launching, and the
+// decode workspace layout must fit in exactly the bytes the query returns.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/yoco.h"
+#include "../../shared_kv_attention_amd/csrc/launch.hpp"
+
+namespace yoco {
+extern int g_launches;
+extern AttnArgs g_attn;
+extern DecodeArgs g_decode;
+extern ProjArgs g_proj;
+extern QuantArgs g_quant;
+extern int g_decode_kinds[3];
+}  // namespace yoco
+
+static int failures = 0;
+#define CHECK(cond)                                                   \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      std::fprintf(stderr, "FAIL line %d: %s\n", __LINE__, #cond);    \
+      ++failures;                                                     \
+    }                                                                 \
+  } while (0)
+
+alignas(256) static unsigned char arena[1 << 16];
+
+int main() {
+  void* P = arena;
+  void* M = arena + 4;   // misaligned
+  int n;
+
+  // ---- global KV projection
+  n = yoco::g_launches;
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_launches == n + 1);
+  CHECK(yoco::g_proj.B == 2 && yoco::g_proj.N == 10 && yoco::g_proj.pos0 == 3 && yoco::g_proj.n_cap == 32);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 12, 3, 1e-6f, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_global_kv_proj(P, M, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, 1e-6f, YOCO_F32, nullptr) == YOCO_ERR_ALIGN);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 100, 2, 64, 32, 3, 1e-6f, YOCO_F32, nullptr) == YOCO_ERR_UNSUPPORTED);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, NAN, YOCO_F32, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco::g_launches == n + 1);
+
+  // ---- sliding window and cross prefill
+  n = yoco::g_launches;
+  CHECK(yoco_swa_attn(P, P, P, P, nullptr, 1, 8, 2, 300, 128, 64, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(std::fabs(yoco::g_attn.scale_log2 - 1.4426950408889634f / std::sqrt(128.f)) < 1e-6f);
+  CHECK(yoco::g_attn.window == 64 && yoco::g_attn.n_kv == 300 && yoco::g_attn.kv_rows == 300);
+  CHECK(yoco_cross_attn_prefill(P, P, P, P, (float*)P, 2, 6, 3, 17, 40, 64, 23, 64, 0.5f, YOCO_F32, nullptr) == YOCO_OK);
+  CHECK(yoco::g_attn.window == 0 && yoco::g_attn.q_offset == 23 && yoco::g_attn.kv_rows == 64);
+  CHECK(std::fabs(yoco::g_attn.scale_log2 - 0.5f * 1.4426950408889634f) < 1e-6f);
+  CHECK(yoco_cross_attn_prefill(P, P, P, P, nullptr, 2, 6, 3, 18, 40, 64, 23, 64, 0.f, YOCO_F32, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_swa_attn(P, P, P, P, (float*)(arena + 2), 1, 8, 2, 300, 128, 64, 0.f, YOCO_BF16, nullptr) == YOCO_ERR_ALIGN);
+  CHECK(yoco::g_launches == n + 2);
+
+  // ---- decode: the workspace layout fits in exactly the queried size
+  const int shapes[][5] = {{16, 32, 8, 32768, 128}, {1, 32, 8, 1 << 20, 128}, {3, 8, 2, 1000, 64}, {2, 12, 2, 300, 128},
+                           {1, 4, 4, 1, 64}, {8, 32, 8, 1 << 19, 128}, {1, 1, 1, 2000000000, 64}};
+  for (const auto& s : shapes) {
+    const int B = s[0], Hq = s[1], Hkv = s[2], ctx = s[3], d = s[4];
+    const size_t need = yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d);
+    CHECK(need > 0 && need % 16 == 0);
+    unsigned char* ws = (unsigned char*)std::malloc(need);
+    n = yoco::g_launches;
+    const yoco_status st = yoco_cross_attn_decode(P, P, P, nullptr, nullptr, nullptr, ctx, P, nullptr, B, Hq, Hkv, ctx, d,
+                                                  0.f, YOCO_BF16, YOCO_BF16, ws, need, nullptr);
+    if ((long long)B * Hkv * ctx > 2147483647LL) {
+      CHECK(st == YOCO_ERR_SHAPE);
+    } else {
+      CHECK(st == YOCO_OK && yoco::g_launches == n + 1);
+      const yoco::DecodeArgs& a = yoco::g_decode;
+      CHECK(a.n_splits >= 1 && a.n_splits <= yoco::kDecodeMaxSplits);
+      CHECK((long long)a.n_splits * a.chunk >= ctx && (long long)(a.n_splits - 1) * a.chunk < ctx);
+      CHECK(a.chunk % 64 == 0);
+      const size_t rows = (size_t)B * Hq * a.n_splits;
+      CHECK((unsigned char*)a.part_o == ws);
+      CHECK((unsigned char*)(a.part_o + rows * d) <= (unsigned char*)a.part_m);
+      CHECK((unsigned char*)(a.part_m + rows) <= (unsigned char*)a.part_l);
+      CHECK((unsigned char*)(a.part_l + rows) <= ws + need);
+      CHECK(yoco_cross_attn_decode(P, P, P, nullptr, nullptr, nullptr, ctx, P, nullptr, B, Hq, Hkv, ctx, d, 0.f, YOCO_BF16,
+                                   YOCO_BF16, ws, need - 1, nullptr) == YOCO_ERR_WORKSPACE);
+    }
+    std::free(ws);
+  }
+  {
+    const size_t need = yoco_cross_attn_decode_workspace_bytes(2, 8, 2, 100, 128);
+    n = yoco::g_launches;
+    CHECK(yoco_cross_attn_decode(P, P, P, (float*)P, (float*)P, (const int32_t*)P, 100, P, nullptr, 2, 8, 2, 128, 128, 0.f,
+                                 YOCO_BF16, YOCO_FP8_E4M3, arena, need, nullptr) == YOCO_OK);
+    CHECK(yoco::g_decode_kinds[0] == 1 && yoco::g_decode_kinds[1] == 2 && yoco::g_decode_kinds[2] == 128);
+    CHECK(yoco_cross_attn_decode(P, P, P, nullptr, (float*)P, nullptr, 100, P, nullptr, 2, 8, 2, 128, 128, 0.f, YOCO_BF16,
+                                 YOCO_FP8_E4M3, arena, need, nullptr) == YOCO_ERR_NULL);
+    CHECK(yoco_cross_attn_decode(P, P, P, nullptr, nullptr, nullptr, 129, P, nullptr, 2, 8, 2, 128, 128, 0.f, YOCO_BF16,
+                                 YOCO_BF16, arena, need, nullptr) == YOCO_ERR_SHAPE);
+    CHECK(yoco::g_launches == n + 1);
+  }
+
+  // ---- fp8 quantiser
+  n = yoco::g_launches;
+  CHECK(yoco_kv_quantize_fp8(P, YOCO_F32, P, (float*)P, 2, 3, 17, 64, arena, yoco_kv_quantize_fp8_workspace_bytes(3), nullptr) ==
+        YOCO_OK);
+  CHECK(yoco::g_quant.slab == 17LL * 64 && yoco::g_quant.Hkv == 3);
+  CHECK(yoco_kv_quantize_fp8(P, YOCO_F32, P, (float*)P, 2, 3, 17, 64, arena, 8, nullptr) == YOCO_ERR_WORKSPACE);
+  CHECK(yoco::g_launches == n + 1);
+
+  // ---- strings
+  for (int s = -1; s < 10; ++s) CHECK(yoco_status_string((yoco_status)s) != nullptr);
+  CHECK(yoco_version() == 100);
+
+  if (failures) return 1;
+  std::printf("abi host driver: all checks passed\n");
+  return 0;
+}

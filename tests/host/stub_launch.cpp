@@ -1,0 +1,21 @@
+// Host-only stand-ins for the kernel launchers of libyoco, so that the C ABI
+// (argument validation, workspace layout, dispatch) can be built with the
+// host compiler under AddressSanitizer / UndefinedBehaviorSanitizer.  Each
+// stub records the argument block it received and reports success.
+#include "../../shared_kv_attention_amd/csrc/launch.hpp"
+
+namespace yoco {
+int g_launches = 0;
+AttnArgs g_attn;
+DecodeArgs g_decode;
+ProjArgs g_proj;
+QuantArgs g_quant;
+int g_decode_kinds[3];
+
+hipError_t launch_attn(const AttnArgs& a, bool, int, bool, hipStream_t) { ++g_launches; g_attn = a; return hipSuccess; }
+hipError_t launch_decode(const DecodeArgs& a, int qk, int kk, int d, hipStream_t) {
+  ++g_launches; g_decode = a; g_decode_kinds[0] = qk; g_decode_kinds[1] = kk; g_decode_kinds[2] = d; return hipSuccess;
+}
+hipError_t launch_kv_proj(const ProjArgs& a, bool, hipStream_t) { ++g_launches; g_proj = a; return hipSuccess; }
+hipError_t launch_quant_fp8(const QuantArgs& a, bool, hipStream_t) { ++g_launches; g_quant = a; return hipSuccess; }
+}  // namespace yoco
