@@ -52,6 +52,8 @@ struct AttnCfg {
   static constexpr int NDB = D / 32;            // 32-wide dim blocks of O
   static constexpr int NPC = BK / 16;           // 16-key steps of P V
   static constexpr int TILE_BYTES = BK * D * E;
+  // bf16 matrix steps read their LDS fragments this many MFMA slots ahead
+  static constexpr int FRAG_AHEAD = 3;
   static_assert(PER_T >= 1 && BK * CH % NT == 0, "tile must split over the workgroup");
   static constexpr int MIN_WAVES_PER_EU = (RB == 2) ? 1 : 2;
 };
@@ -147,6 +149,27 @@ __device__ __forceinline__ typename Elem<T>::frag lds_frag_vt(const char* tile, 
     }
   }
   return f;
+}
+
+// Scheduler hints for a run of NS matrix-core slots whose LDS operand (R
+// reads each) is fetched PD slots ahead: the reads of the first PD slots,
+// then per slot one MFMA followed by the reads of slot n + PD.  Without them
+// the compiler reads one or two fragments ahead and every step waits for
+// the LDS round trip.
+template <int R, int PD, int n>
+__device__ __forceinline__ void pipe_sched_prologue() {
+  if constexpr (n < PD) {
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);   // DS reads
+    pipe_sched_prologue<R, PD, n + 1>();
+  }
+}
+template <int R, int NS, int PD, int n>
+__device__ __forceinline__ void pipe_sched_steps() {
+  if constexpr (n < NS) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    if constexpr (n + PD < NS) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    pipe_sched_steps<R, NS, PD, n + 1>();
+  }
 }
 
 template <typename T, int D, bool SWA>
@@ -277,16 +300,39 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
 
       // S^T = K Q^T: each K fragment serves every row block of the wave
       f32x16 s[RB][C::NKB];
+      if constexpr (sizeof(T) == 2 && RB == 1) {
+        // slot n = (k step c = n / NKB, key block kb = n % NKB): the two key
+        // blocks alternate, so consecutive MFMAs are independent; fragments
+        // are read FRAG_AHEAD slots ahead through a small ring
+        constexpr int NS = C::NC * C::NKB, PD = C::FRAG_AHEAD;
+        const int krow = sigma(r32);
+        frag ring[PD + 1];
 #pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) {
+        for (int kb = 0; kb < C::NKB; ++kb) s[0][kb] = f32x16{};
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = f32x16{};
-        const int krow = kb * 32 + sigma(r32);
+        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_k<T, D>(ktile, (n % C::NKB) * 32 + krow, n / C::NKB, g);
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) {
-          const frag kf = lds_frag_k<T, D>(ktile, krow, c, g);
+        for (int n = 0; n < NS; ++n) {
+          if (n + PD < NS) {
+            const int m = n + PD;
+            ring[m % (PD + 1)] = lds_frag_k<T, D>(ktile, (m % C::NKB) * 32 + krow, m / C::NKB, g);
+          }
+          s[0][n % C::NKB] = mma32(ring[n % (PD + 1)], qf[0][n / C::NKB], s[0][n % C::NKB]);
+        }
+        pipe_sched_prologue<1, PD, 0>();
+        pipe_sched_steps<1, NS, PD, 0>();
+      } else {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mma32(kf, qf[rb][c], s[rb][kb]);
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s[rb][kb] = f32x16{};
+          const int krow = kb * 32 + sigma(r32);
+#pragma unroll
+          for (int c = 0; c < C::NC; ++c) {
+            const frag kf = lds_frag_k<T, D>(ktile, krow, c, g);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mma32(kf, qf[rb][c], s[rb][kb]);
+          }
         }
       }
 
@@ -352,13 +398,33 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
         l_run[rb] += lsum;
       }
       // O^T += V^T P^T: each V^T fragment serves every row block of the wave
+      if constexpr (sizeof(T) == 2 && RB == 1) {
+        // slot n = (key step c = n / NDB, dim block db = n % NDB): the dim
+        // blocks alternate; each fragment is two transposed reads, issued
+        // FRAG_AHEAD slots ahead
+        constexpr int NS = C::NPC * C::NDB, PD = C::FRAG_AHEAD;
+        frag ring[PD + 1];
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
+        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_vt<T, D>(vtile, n / C::NDB, n % C::NDB, l);
 #pragma unroll
-        for (int c = 0; c < C::NPC; ++c) {
-          const frag vf = lds_frag_vt<T, D>(vtile, c, db, l);
+        for (int n = 0; n < NS; ++n) {
+          if (n + PD < NS) {
+            const int m = n + PD;
+            ring[m % (PD + 1)] = lds_frag_vt<T, D>(vtile, m / C::NDB, m % C::NDB, l);
+          }
+          acc_o[0][n % C::NDB] = mma32(ring[n % (PD + 1)], pf[0][n / C::NDB], acc_o[0][n % C::NDB]);
+        }
+        pipe_sched_prologue<2, PD, 0>();
+        pipe_sched_steps<2, NS, PD, 0>();
+      } else {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = mma32(vf, pf[rb][c], acc_o[rb][db]);
+        for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+          for (int c = 0; c < C::NPC; ++c) {
+            const frag vf = lds_frag_vt<T, D>(vtile, c, db, l);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = mma32(vf, pf[rb][c], acc_o[rb][db]);
+          }
         }
       }
     }

@@ -28,7 +28,9 @@
 //    float32 FMAs.
 //  * Online softmax in the exp2 domain; the running max per head is raised
 //    only when a block exceeds it by 2^8 (wave-uniform branch).
-//  * The next block's loads are issued before the current block is used.
+//  * The next block's loads are issued before the current block is used; the
+//    K loads that first touch each 128-byte line go two blocks ahead, so the
+//    other loads of that line hit in L2 instead of fetching it again.
 //  * fp8-e4m3 caches: codes are decoded in registers (exactly, to bf16 for
 //    the matrix core and to f32 for P V); the per-head scales factor out of
 //    both products: the K scale is folded into the softmax scale and the V
@@ -186,12 +188,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     for (int e = 0; e < DPL; ++e) acc[i][e] = 0.f;
   }
 
-  Raw8<KVT> kc[NC], kn[NC];
+  // One K load instruction covers 16 rows x 32 dims, i.e. part of a 128-byte
+  // line of each row.  Two instructions that share lines and are issued back
+  // to back both miss in L2 and each fetch the line from memory, so the
+  // instruction that touches a line first ("lead") is issued two blocks
+  // ahead and the others one block ahead, when the line is already in L2.
+  auto is_lead = [](int c) { return (32 * c * (int)sizeof(KVT)) % 128 == 0; };
+  Raw8<KVT> kc[NC], kn[NC], k2[NC];
   vword vc[16], vn[16];
-  auto load_block = [&](int key0, Raw8<KVT>* kr, vword* vr) {
+  auto load_k = [&](int key0, Raw8<KVT>* kr, bool lead) {
     const int kkey = min(key0 + r16, key_end - 1);   // never read rows >= ctx_b
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = load_raw8<KVT>(kb + (size_t)kkey * D + 32 * c);
+    for (int c = 0; c < NC; ++c)
+      if (is_lead(c) == lead) kr[c] = load_raw8<KVT>(kb + (size_t)kkey * D + 32 * c);
+  };
+  auto load_v = [&](int key0, vword* vr) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int vkey = min(key0 + j, key_end - 1);
@@ -199,10 +210,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  load_block(key_begin, kc, vc);
+  load_k(key_begin, kc, true);
+  load_k(key_begin, kc, false);
+  load_v(key_begin, vc);
+  if (key_begin + 16 < key_end) load_k(key_begin + 16, kn, true);
   for (int key0 = key_begin; key0 < key_end; key0 += 16) {
     const bool has_next = key0 + 16 < key_end;
-    if (has_next) load_block(key0 + 16, kn, vn);
+    if (has_next) {
+      load_k(key0 + 16, kn, false);
+      load_v(key0 + 16, vn);
+    }
+    if (key0 + 32 < key_end) load_k(key0 + 32, k2, true);
 
     // scores: lane (G, r16) receives head i's score of key key0 + r16 in s[i]
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -295,7 +313,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
     if (has_next) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kc[c] = kn[c];
+      for (int c = 0; c < NC; ++c) {
+        kc[c] = kn[c];
+        if (is_lead(c)) kn[c] = k2[c];
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) vc[j] = vn[j];
     }
