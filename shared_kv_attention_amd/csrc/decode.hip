@@ -28,9 +28,9 @@
 //    float32 FMAs.
 //  * Online softmax in the exp2 domain; the running max per head is raised
 //    only when a block exceeds it by 2^8 (wave-uniform branch).
-//  * The next block's loads are issued before the current block is used; the
-//    K loads that first touch each 128-byte line go two blocks ahead, so the
-//    other loads of that line hit in L2 instead of fetching it again.
+//  * The next block's loads are issued before the current block is used; for
+//    bf16 caches the K loads that first touch each 128-byte line go two
+//    blocks ahead.
 //  * fp8-e4m3 caches: codes are decoded in registers (exactly, to bf16 for
 //    the matrix core and to f32 for P V); the per-head scales factor out of
 //    both products: the K scale is folded into the softmax scale and the V
@@ -188,12 +188,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     for (int e = 0; e < DPL; ++e) acc[i][e] = 0.f;
   }
 
-  // One K load instruction covers 16 rows x 32 dims, i.e. part of a 128-byte
-  // line of each row.  Two instructions that share lines and are issued back
-  // to back both miss in L2 and each fetch the line from memory, so the
-  // instruction that touches a line first ("lead") is issued two blocks
-  // ahead and the others one block ahead, when the line is already in L2.
-  auto is_lead = [](int c) { return (32 * c * (int)sizeof(KVT)) % 128 == 0; };
+  // One K load instruction covers 16 rows x 32 dims, i.e. half of a 128-byte
+  // line of each bf16 row.  For bf16 caches the instruction that touches a
+  // line first ("lead") is issued two blocks ahead and the other one block
+  // ahead, so the line's fill is already under way when it arrives (+3% on
+  // the 32K decode; K and V are still read once).  fp8 and f32 caches issue
+  // all K loads one block ahead (the staggering measured slower for fp8).
+  auto is_lead = [](int c) { return sizeof(KVT) == 2 && (c & 1) == 0; };
   Raw8<KVT> kc[NC], kn[NC], k2[NC];
   vword vc[16], vn[16];
   auto load_k = [&](int key0, Raw8<KVT>* kr, bool lead) {
