@@ -38,6 +38,8 @@ from .attention import (  # noqa: F401
     decode_attention,
     swa_allowed,
     causal_allowed,
+    ring_window,
+    swa_ring_decode_attention,
 )
 from .projection import rmsnorm_row, rmsnorm, global_kv_proj  # noqa: F401
 from .fp8 import (  # noqa: F401
@@ -47,5 +49,5 @@ from .fp8 import (  # noqa: F401
     quantize_kv_fp8,
     dequantize_kv_fp8,
 )
-from .block import BlockParams, yoco_block, yoco_block_early_exit  # noqa: F401
+from .block import BlockParams, yoco_block, yoco_block_early_exit, yoco_block_generate  # noqa: F401
 from .memory import yoco_kv_cache_bytes, transformer_kv_cache_bytes  # noqa: F401

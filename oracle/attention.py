@@ -16,7 +16,12 @@ What the method computes (pages cited as in the package docstring):
   one shared key/value pair produced by the global projection, with
   grouped-query heads ([P seg. 12]; [S §2]).
 * Decoding produces one token per step and reads the entire cache each step
-  ([P seg. 4], [P seg. 26]).  Reading taken: the cache already holds the
+  ([P seg. 4], [P seg. 26]).
+* During generation the self-decoder keeps only a window-sized cache: its
+  memory is constant in the sequence length ([S §3 Sliding-Window
+  Attention]; [S §2]).  Reading taken for its layout: a ring of W slots per
+  layer and KV head, position t stored in slot t mod W, so that the slots
+  always hold the last W positions.  Reading taken: the cache already holds the
   current token, so a decode query at step ctx-1 attends to keys 0..ctx-1.
 * Grouped-query attention: several query heads share one KV head
   ([P seg. 4]; [S App. C]).  Reading taken: contiguous groups, query head h
@@ -45,6 +50,8 @@ __all__ = [
     "swa_attention",
     "cross_prefill_attention",
     "decode_attention",
+    "ring_window",
+    "swa_ring_decode_attention",
 ]
 
 
@@ -169,4 +176,44 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, bh=None):
         kvh = h // g
         o[b, h], lse[b, h], _ = attend_row(
             q[b, h], k_cache[b, kvh, :c], v_cache[b, kvh, :c], scale)
+    return o, lse
+
+
+def ring_window(pos, window):
+    """(position, slot) pairs a decode query at position pos reads from a ring
+    of W slots, in position order: positions max(0, pos-W+1) .. pos, position
+    t in slot t mod W."""
+    if pos < 0 or window < 1:
+        raise ValueError("pos must be >= 0 and window >= 1")
+    return [(t, t % window) for t in range(max(0, pos - window + 1), pos + 1)]
+
+
+def swa_ring_decode_attention(q, k_ring, v_ring, pos, scale=None, bh=None):
+    """One decode step of a self-decoder sliding-window layer over its ring
+    cache ([S §3 Sliding-Window Attention]).
+
+    q [B, Hq, d] is the query of the token at position pos (the same for the
+    whole batch); k_ring/v_ring [B, Hkv, W, d] hold position t in slot t mod W
+    for the last W positions, the current one included.  The keys are
+    gathered in position order, so the result equals row pos of
+    swa_attention over the full sequence.
+    Returns (o [B, Hq, d], lse [B, Hq]).
+    """
+    q, k_ring, v_ring = _as64(q), _as64(k_ring), _as64(v_ring)
+    B, Hq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    slots = [s for _, s in ring_window(pos, W)]
+    if bh is None:
+        bh = [(b, h) for b in range(B) for h in range(Hq)]
+    o = np.full(q.shape, np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for b, h in bh:
+        kvh = h // g
+        o[b, h], lse[b, h], _ = attend_row(
+            q[b, h], k_ring[b, kvh, slots], v_ring[b, kvh, slots], scale)
     return o, lse

@@ -16,6 +16,11 @@ What the method computes:
   shared KV, skips the cross-decoder for the prompt tokens and sends only
   the last position through it; the output is unchanged ([P seg. 14] and its
   Figure 3; [S §2]; [A]).
+* Generation: one token per step; each self-decoder layer keeps a constant
+  window-sized cache, the global cache grows by one row per token, and every
+  cross-decoder layer reads the whole global cache ([P seg. 4], [P seg. 26];
+  [S §2], [S §3]).  Causality makes token-by-token generation reproduce the
+  rows of a full forward over the same sequence.
 Readings taken: each attention keeps an output projection W_o; the SwiGLU
 feed-forward and the final norm are left out (position-wise, no sizes on the
 pages, and they cannot affect causality, sharing or early exit); the
@@ -35,10 +40,10 @@ import math
 
 import numpy as np
 
-from .attention import attend_row, cross_prefill_attention, swa_attention
+from .attention import attend_row, cross_prefill_attention, ring_window, swa_attention
 from .projection import global_kv_proj, rmsnorm_row
 
-__all__ = ["BlockParams", "linear_rows", "yoco_block", "yoco_block_early_exit"]
+__all__ = ["BlockParams", "linear_rows", "yoco_block", "yoco_block_early_exit", "yoco_block_generate"]
 
 
 @dataclass
@@ -143,3 +148,57 @@ def yoco_block_early_exit(x, p):
             new[b] = last[b] + wo @ o.reshape(Hq * d)
         last = new
     return last, (k_glob, v_glob)
+
+
+def yoco_block_generate(x, p):
+    """Token-by-token forward with generation-time caches.
+
+    Position t is processed after positions 0..t-1 only.  Each self-decoder
+    layer appends the token's K/V to its ring of W slots (slot t mod W) and
+    attends over the window read back in position order; the hidden state
+    after the self-decoder is normalised and projected into row t of the
+    global cache; each cross-decoder layer attends over global rows 0..t.
+    Returns (x_out [B, N, D], (K, V) [B, Hkv, N, d], rings) where rings[l] =
+    (K ring, V ring) [B, Hkv, W, d] of self-decoder layer l after the last
+    token.  Equal bitwise to yoco_block(x, p) (the same per-row arithmetic).
+    """
+    Hq, Hkv, d, W = p.n_heads, p.n_kv_heads, p.head_dim, p.window
+    x = np.array(x, dtype=np.float64)
+    B, N, D = x.shape
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    rings = [(np.zeros((B, Hkv, W, d)), np.zeros((B, Hkv, W, d))) for _ in p.swa_wq]
+    k_glob = np.zeros((B, Hkv, N, d))
+    v_glob = np.zeros((B, Hkv, N, d))
+    out = np.empty_like(x)
+    for t in range(N):
+        slots = [s for _, s in ring_window(t, W)]
+        h_t = x[:, t, :].copy()
+        for (wq, wk, wv, wo), (kr, vr) in zip(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo), rings):
+            new = np.empty_like(h_t)
+            for b in range(B):
+                n = rmsnorm_row(h_t[b], None, p.eps)
+                q = (wq @ n).reshape(Hq, d)
+                kr[b, :, t % W] = (wk @ n).reshape(Hkv, d)
+                vr[b, :, t % W] = (wv @ n).reshape(Hkv, d)
+                o = np.empty((Hq, d))
+                for h in range(Hq):
+                    o[h], _, _ = attend_row(q[h], kr[b, h // g, slots], vr[b, h // g, slots], scale)
+                new[b] = h_t[b] + wo @ o.reshape(Hq * d)
+            h_t = new
+        for b in range(B):
+            k_row, v_row = global_kv_proj(h_t[b][None, None, :], p.glob_wk, p.glob_wv, Hkv, d, eps=p.eps)
+            k_glob[b, :, t] = k_row[0, :, 0]
+            v_glob[b, :, t] = v_row[0, :, 0]
+        for wq, wo in zip(p.cross_wq, p.cross_wo):
+            new = np.empty_like(h_t)
+            for b in range(B):
+                n = rmsnorm_row(h_t[b], None, p.eps)
+                q = (wq @ n).reshape(Hq, d)
+                o = np.empty((Hq, d))
+                for h in range(Hq):
+                    o[h], _, _ = attend_row(q[h], k_glob[b, h // g, :t + 1], v_glob[b, h // g, :t + 1], scale)
+                new[b] = h_t[b] + wo @ o.reshape(Hq * d)
+            h_t = new
+        out[:, t, :] = h_t
+    return out, (k_glob, v_glob), rings
