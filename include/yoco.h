@@ -157,6 +157,33 @@ yoco_status yoco_cross_attn_decode(const void* q, const void* k_cache,
 size_t yoco_cross_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int ctx, int d);
 
 /*
+ * Self-decoder sliding-window attention for one new token per sequence (a
+ * generation step), over the layer's ring cache of W slots.
+ * Source: paperlayer.ai summary section 3 (each query sees a fixed window of
+ * recent positions, so the self-decoder's cache stays window-sized however
+ * long the sequence) and section 2; podcast segment 4 (one token per decoding
+ * step).
+ * Ring layout: k_ring, v_ring [B, Hkv, W, d]; position t lives in slot t mod W.
+ * If k_new and v_new ([B, Hkv, d]) are given, they are first written to slot
+ * pos mod W (the current token's K/V; both or neither may be NULL).  The query
+ * at position pos then attends to positions max(0, pos - W + 1) .. pos, i.e.
+ * ring slots 0 .. min(pos + 1, W) - 1; the caller must have written every
+ * earlier position of that window.  All sequences are at the same pos.
+ *   q, o  [B, Hq, d]      lse [B, Hq] float32 or NULL      pos >= 0, W >= 1
+ *   workspace >= yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d) bytes of
+ *   device memory, 16-byte aligned, not shared by concurrent calls.
+ * Supported dtypes: F32, BF16 (q, rings, new K/V and o in that dtype).
+ */
+yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new,
+                            void* k_ring, void* v_ring, int pos, void* o, float* lse,
+                            int B, int Hq, int Hkv, int W, int d, float softmax_scale,
+                            yoco_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace of yoco_swa_decode for any pos with this window (0 on invalid sizes). */
+size_t yoco_swa_decode_workspace_bytes(int B, int Hq, int Hkv, int W, int d);
+
+/*
  * Quantise a K or V tensor to an 8-bit cache.
  * Source: podcast segments 1 and 24 (8-bit KV cache as the deployed form);
  * the format is fixed here: OCP e4m3fn, one float32 scale per KV head over

@@ -26,6 +26,8 @@ __all__ = [
     "yoco_cross_attn_prefill",
     "yoco_cross_attn_decode",
     "yoco_cross_attn_decode_workspace_bytes",
+    "yoco_swa_decode",
+    "yoco_swa_decode_workspace_bytes",
     "yoco_kv_quantize_fp8",
     "yoco_kv_quantize_fp8_workspace_bytes",
     "yoco_status_string",
@@ -49,6 +51,8 @@ _SIGS = {
     "yoco_cross_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
                                     _vp, _sz, _vp]),
     "yoco_cross_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "yoco_swa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
+    "yoco_swa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "yoco_kv_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "yoco_kv_quantize_fp8_workspace_bytes": (_sz, [_i]),
     "yoco_status_string": (ctypes.c_char_p, [_i]),
@@ -183,6 +187,30 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, ctx, ctx_lens=None, k_scale=None
         _ptr(lse), B, Hq, Hkv, n_cap, d, float(softmax_scale), _dtype_code(q), _dtype_code(k_cache),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "yoco_cross_attn_decode")
+    return o
+
+
+def yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d):
+    return lib().yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d)
+
+
+def yoco_swa_decode(q, k_ring, v_ring, pos, k_new=None, v_new=None, o=None, lse=None, workspace=None,
+                    softmax_scale=0.0, stream=None):
+    """Self-decoder window decode of the token at position pos; q [B, Hq, d], rings [B, Hkv, W, d]
+    (position t in slot t mod W).  k_new/v_new [B, Hkv, d], if given, are written to slot pos mod W first."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    need = yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib().yoco_swa_decode(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_ring), _ptr(v_ring), int(pos), _ptr(o), _ptr(lse),
+        B, Hq, Hkv, W, d, float(softmax_scale), _dtype_code(q), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "yoco_swa_decode")
     return o
 
 

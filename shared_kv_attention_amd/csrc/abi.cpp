@@ -172,6 +172,63 @@ yoco_status yoco_cross_attn_decode(const void* q, const void* k_cache, const voi
   return launched(yoco::launch_decode(a, qk, kk, d, as_stream(stream)));
 }
 
+size_t yoco_swa_decode_workspace_bytes(int B, int Hq, int Hkv, int W, int d) {
+  if (!decode_sizes_ok(B, Hq, Hkv, W, d)) return 0;
+  // a call at position pos plans ctx = min(pos + 1, W) <= W, whose split count
+  // is at most decode_split_bound(.., W)
+  const size_t rows = (size_t)B * Hq * yoco::decode_split_bound(B, Hq, Hkv, W);
+  return align16(rows * d * sizeof(float)) + 2 * align16(rows * sizeof(float));
+}
+
+yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new, void* k_ring, void* v_ring,
+                            int pos, void* o, float* lse, int B, int Hq, int Hkv, int W, int d,
+                            float softmax_scale, yoco_dtype dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!q || !k_ring || !v_ring || !o) return YOCO_ERR_NULL;
+  if ((k_new == nullptr) != (v_new == nullptr)) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || W < 1 || pos < 0 || Hq % Hkv != 0) return YOCO_ERR_SHAPE;
+  if (B > 65535 || (long long)B * Hkv * W > kIntMax || (long long)Hkv * ((Hq / Hkv + 3) / 4) > 65535)
+    return YOCO_ERR_SHAPE;
+  if (isnan(softmax_scale) || isinf(softmax_scale)) return YOCO_ERR_SHAPE;
+  if (!head_dim_ok(d)) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_ring, 16) || !aligned(v_ring, 16) || !aligned(o, 16) ||
+      (k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)) || (lse && !aligned(lse, 4)))
+    return YOCO_ERR_ALIGN;
+  const int ctx = pos + 1 < W ? pos + 1 : W;   // slots 0 .. ctx-1 hold the window
+  const DecodeLayout L = decode_layout(B, Hq, Hkv, ctx, d);
+  if (!workspace || workspace_bytes < L.total) return YOCO_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
+  const int esz = dtype == YOCO_F32 ? 4 : 2;
+  if (k_new) {
+    yoco::RingAppendArgs r{k_new, v_new, k_ring, v_ring, B, Hkv, W, pos % W, d * esz};
+    const yoco_status st = launched(yoco::launch_ring_append(r, as_stream(stream)));
+    if (st != YOCO_OK) return st;
+  }
+  char* ws = static_cast<char*>(workspace);
+  yoco::DecodeArgs a{};
+  a.q = q;
+  a.k = k_ring;
+  a.v = v_ring;
+  a.ctx_lens = nullptr;
+  a.ctx = ctx;
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_m = reinterpret_cast<float*>(ws + L.o_bytes);
+  a.part_l = reinterpret_cast<float*>(ws + L.o_bytes + L.ml_bytes);
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_cap = W;
+  a.n_splits = L.n_splits;
+  a.chunk = L.chunk;
+  a.n_hg = L.n_hg;
+  a.scale_log2 = resolve_scale(softmax_scale, d) * 1.4426950408889634f;
+  const int kind = dtype == YOCO_F32 ? 0 : 1;
+  return launched(yoco::launch_decode(a, kind, kind, d, as_stream(stream)));
+}
+
 size_t yoco_kv_quantize_fp8_workspace_bytes(int Hkv) {
   if (Hkv < 1) return 0;
   return align16((size_t)Hkv * sizeof(uint32_t));

@@ -419,6 +419,26 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Writes the current token's K and V rows into ring slot `slot` of every
+// (sequence, KV head): one workgroup per (sequence, KV head), 4-byte words.
+__global__ __launch_bounds__(64) void ring_append_kernel(RingAppendArgs a) {
+  const int bh = blockIdx.x;
+  const int words = a.row_bytes / 4;
+  const uint32_t* ks = static_cast<const uint32_t*>(a.k_new) + (size_t)bh * words;
+  const uint32_t* vs = static_cast<const uint32_t*>(a.v_new) + (size_t)bh * words;
+  uint32_t* kd = static_cast<uint32_t*>(a.k_ring) + ((size_t)bh * a.W + a.slot) * words;
+  uint32_t* vd = static_cast<uint32_t*>(a.v_ring) + ((size_t)bh * a.W + a.slot) * words;
+  for (int i = threadIdx.x; i < words; i += 64) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hipStream_t stream) {
   // kinds: 0 = f32, 1 = bf16, 2 = fp8-e4m3 codes
   if (q_kind == 0) return d == 128 ? launch_decode_t<float, float, 128>(a, stream) : launch_decode_t<float, float, 64>(a, stream);

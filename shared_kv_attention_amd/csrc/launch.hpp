@@ -52,6 +52,15 @@ struct ProjArgs {
   float eps;
 };
 
+struct RingAppendArgs {
+  const void* k_new;   // [B, Hkv, d]
+  const void* v_new;
+  void* k_ring;        // [B, Hkv, W, d]
+  void* v_ring;
+  int B, Hkv, W, slot;
+  int row_bytes;       // d * element size (a multiple of 4)
+};
+
 struct QuantArgs {
   const void* kv;
   uint8_t* codes;
@@ -65,11 +74,14 @@ hipError_t launch_attn(const AttnArgs& a, bool is_bf16, int d, bool swa, hipStre
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hipStream_t stream);
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream);
+hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
 
 // Split plan of the decode kernel (host code, plan.cpp); the workspace size
 // follows from it.  At most kDecodeMaxSplits splits (the combine pass keeps one
 // weight per split in LDS).
 constexpr int kDecodeMaxSplits = 4096;
 void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int* n_hg);
+// An upper bound on decode_plan's n_splits for every context length <= ctx.
+int decode_split_bound(int B, int Hq, int Hkv, int ctx);
 
 }  // namespace yoco

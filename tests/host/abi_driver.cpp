@@ -16,6 +16,7 @@ extern AttnArgs g_attn;
 extern DecodeArgs g_decode;
 extern ProjArgs g_proj;
 extern QuantArgs g_quant;
+extern RingAppendArgs g_ring;
 extern int g_decode_kinds[3];
 }  // namespace yoco
 
@@ -98,6 +99,35 @@ int main() {
     CHECK(yoco_cross_attn_decode(P, P, P, nullptr, nullptr, nullptr, 129, P, nullptr, 2, 8, 2, 128, 128, 0.f, YOCO_BF16,
                                  YOCO_BF16, arena, need, nullptr) == YOCO_ERR_SHAPE);
     CHECK(yoco::g_launches == n + 1);
+  }
+
+  // ---- self-decoder ring decode: append + decode, workspace bound over all positions
+  {
+    const int B = 3, Hq = 8, Hkv = 2, W = 1024, d = 128;
+    const size_t need = yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d);
+    CHECK(need > 0 && need % 16 == 0);
+    unsigned char* ws = (unsigned char*)std::malloc(need);
+    for (int pos : {0, 1, 255, 256, 1022, 1023, 1024, 5000, 1 << 20}) {
+      n = yoco::g_launches;
+      CHECK(yoco_swa_decode(P, P, P, P, P, pos, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_BF16, ws, need, nullptr) == YOCO_OK);
+      CHECK(yoco::g_launches == n + 2);
+      CHECK(yoco::g_ring.slot == pos % W && yoco::g_ring.row_bytes == d * 2 && yoco::g_ring.W == W);
+      const yoco::DecodeArgs& a = yoco::g_decode;
+      CHECK(a.ctx == (pos + 1 < W ? pos + 1 : W) && a.n_cap == W && a.ctx_lens == nullptr);
+      const size_t rows = (size_t)B * Hq * a.n_splits;
+      CHECK((unsigned char*)(a.part_l + rows) <= ws + need);
+      CHECK((long long)a.n_splits * a.chunk >= a.ctx);
+    }
+    n = yoco::g_launches;
+    CHECK(yoco_swa_decode(P, nullptr, nullptr, P, P, 7, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_OK);
+    CHECK(yoco::g_launches == n + 1);   // no append without new K/V
+    CHECK(yoco_swa_decode(P, P, nullptr, P, P, 7, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_ERR_NULL);
+    CHECK(yoco_swa_decode(P, P, P, P, P, -1, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_ERR_SHAPE);
+    CHECK(yoco_swa_decode(P, P, P, P, P, 7, P, nullptr, B, Hq, Hkv, 0, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_ERR_SHAPE);
+    CHECK(yoco_swa_decode(P, P, P, P, P, 7, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_FP8_E4M3, ws, need, nullptr) == YOCO_ERR_DTYPE);
+    CHECK(yoco_swa_decode(P, P, P, P, P, 7000, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_F32, ws, 16, nullptr) == YOCO_ERR_WORKSPACE);
+    CHECK(yoco::g_launches == n + 1);
+    std::free(ws);
   }
 
   // ---- fp8 quantiser

@@ -145,6 +145,37 @@ def test_decode_exact_workspace_boundary(L):
     assert decode(L, wsb=need - 1) == WS
 
 
+def swa_dec(L, **kw):
+    a = dict(q=P, kn=P, vn=P, kr=P, vr=P, pos=300, o=P, lse=None, B=2, Hq=8, Hkv=2, W=256, d=128,
+             scale=0.0, dt=yk.BF16, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.yoco_swa_decode(a["q"], a["kn"], a["vn"], a["kr"], a["vr"], a["pos"], a["o"], a["lse"], a["B"],
+                             a["Hq"], a["Hkv"], a["W"], a["d"], a["scale"], a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(kr=None), NULL), (dict(o=None), NULL), (dict(kn=None), NULL), (dict(vn=None), NULL),
+    (dict(dt=yk.FP8_E4M3), DTYPE), (dict(dt=7), DTYPE),
+    (dict(pos=-1), SHAPE), (dict(W=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(B=0), SHAPE),
+    (dict(scale=float("inf")), SHAPE),
+    (dict(d=32), UNSUP),
+    (dict(kn=MIS), ALIGN), (dict(vr=MIS), ALIGN), (dict(lse=4096 + 2), ALIGN), (dict(ws=MIS), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=16), WS),
+])
+def test_swa_decode_errors(L, kw, code):
+    assert swa_dec(L, **kw) == code
+
+
+def test_swa_decode_workspace_covers_every_position(L):
+    need = yk.yoco_swa_decode_workspace_bytes(2, 8, 2, 256, 128)
+    assert need > 0 and need % 16 == 0
+    # positions before the ring fills plan on fewer keys: never more than the bound
+    for pos in range(0, 600, 7):
+        assert yk.yoco_cross_attn_decode_workspace_bytes(2, 8, 2, min(pos + 1, 256), 128) <= need
+    for bad in [(0, 8, 2, 256, 128), (2, 8, 2, 0, 128), (2, 8, 2, 256, 100)]:
+        assert yk.yoco_swa_decode_workspace_bytes(*bad) == 0
+
+
 def quant(L, **kw):
     a = dict(kv=P, dt=yk.F32, codes=P, scale=P, B=2, Hkv=4, n=10, d=64, ws=P, wsb=64)
     a.update(kw)
