@@ -9,8 +9,11 @@ the step (unmasked query-key pairs only, 2 flops per MAC, exp not counted).
 
 The same run also measures the cross-attention decode kernel at its own
 headline shape (batch 16, context 32768, 32/8 heads, 16 cross layers x 128
-steps) and reports its HBM GB/s, and times the float64 CPU oracle on a
-bounded sample of the prefill step ("cpu_baseline").
+steps) and reports its HBM GB/s, the 512K fp8-cache decode, the one-token
+generation step at the decode shape (16 self-decoder ring layers, the
+one-row KV projection, 16 cross layers), the 1M-token early-exit prefill,
+and times the float64 CPU oracle on a bounded sample of the prefill step
+("cpu_baseline").
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors already resident
 in HBM when timing starts.
@@ -238,6 +241,85 @@ def run_decode(wl, dev, steps):
     }
 
 
+# ---------------------------------------------------------------- generation
+def run_generation(wl, dev, steps):
+    """One generated token per sequence: every self-decoder layer appends the
+    token's K/V to its W-slot ring and attends over the window; the hidden
+    state is projected into row ctx-1 of the global cache; every cross layer
+    attends over rows 0..ctx-1.  Synthetic queries, new K/V and hidden state
+    per layer; full rings."""
+    B, ctx, Hq, Hkv, d, W, D = wl.batch, wl.seq, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.window, wl.hidden
+    Ls, Lc, wid = wl.n_self_layers, wl.n_cross_layers, wl.wid
+    rings = [(randn((B, Hkv, W, d), seed_for(wid, 10 + 2 * i), device=dev),
+              randn((B, Hkv, W, d), seed_for(wid, 11 + 2 * i), device=dev)) for i in range(Ls)]
+    kc = randn((B, Hkv, ctx, d), seed_for(wid, 0), device=dev)
+    vc = randn((B, Hkv, ctx, d), seed_for(wid, 1), device=dev)
+    wk = randn((Hkv * d, D), seed_for(wid, 3), std=wl.weight_std, device=dev)
+    wv = randn((Hkv * d, D), seed_for(wid, 4), std=wl.weight_std, device=dev)
+    qs_self = randn((Ls, B, Hq, d), seed_for(wid, 5), device=dev)
+    kn = randn((Ls, B, Hkv, d), seed_for(wid, 6), device=dev)
+    vn = randn((Ls, B, Hkv, d), seed_for(wid, 7), device=dev)
+    hid = randn((B, 1, D), seed_for(wid, 8), device=dev)
+    qs_cross = randn((Lc, B, Hq, d), seed_for(wid, 2), device=dev)
+    o = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws_self = torch.empty(yk.yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d), dtype=torch.uint8, device=dev)
+    ws_cross = torch.empty(yk.yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d), dtype=torch.uint8,
+                           device=dev)
+    pos = ctx - 1    # the token being generated sits at the last cached position
+
+    parts = {"self_decoder": [], "kv_append": [], "cross_decoder": []}
+
+    def ev_call(key, fn, record):
+        if record:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            parts[key].append((s, e))
+        else:
+            fn()
+
+    def step(record):
+        for i in range(Ls):
+            ev_call("self_decoder", lambda: yk.yoco_swa_decode(qs_self[i], rings[i][0], rings[i][1], pos,
+                                                               k_new=kn[i], v_new=vn[i], o=o, workspace=ws_self),
+                    record)
+        ev_call("kv_append", lambda: yk.yoco_global_kv_proj(hid, wk, wv, kc, vc, pos0=pos), record)
+        for i in range(Lc):
+            ev_call("cross_decoder", lambda: yk.yoco_cross_attn_decode(qs_cross[i], kc, vc, ctx, o=o,
+                                                                       workspace=ws_cross), record)
+
+    step(False)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    part_ms = {k: sum(events_ms(v)) / steps for k, v in parts.items()}
+    self_bytes = Ls * (B * Hkv * W * d * 2 * 2 + B * Hq * d * 2 * 2 + B * Hkv * d * 2 * 2)
+    proj_bytes = 2 * Hkv * d * D * 2 + B * D * 2 + 2 * B * Hkv * d * 2
+    cross_bytes = Lc * decode_bytes(B, Hkv, ctx, d, Hq, 2, 2)
+    nbytes = self_bytes + proj_bytes + cross_bytes
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    return {
+        "workload": wl.name,
+        "steps": steps,
+        "ms_per_step": ms_step,
+        "tokens_per_s": B / (ms_step * 1e-3),
+        "bytes_per_step": nbytes,
+        "GB/s": gbs,
+        "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+        "parts_ms_per_step": part_ms,
+        "parts_GB/s": {"self_decoder": self_bytes / (part_ms["self_decoder"] * 1e-3) / 1e9,
+                       "kv_append": proj_bytes / (part_ms["kv_append"] * 1e-3) / 1e9,
+                       "cross_decoder": cross_bytes / (part_ms["cross_decoder"] * 1e-3) / 1e9},
+        "timing": "HIP events around the whole step and around every call",
+    }
+
+
 # ---------------------------------------------------------------- early exit
 def run_early_exit(wl, dev, steps):
     """1M-token early-exit prefill: L_s SWA layers over all tokens, the global
@@ -330,6 +412,7 @@ def main():
     ap.add_argument("--no-early-exit", action="store_true",
                     help="skip the 1M-token early-exit flow measurement (allocates ~110 GB)")
     ap.add_argument("--extra-steps", type=int, default=3, help="steps of the 1M early-exit flow")
+    ap.add_argument("--no-generation", action="store_true", help="skip the one-token generation step measurement")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -414,6 +497,10 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_fp8_decode:
         out["decode_fp8"] = run_decode(WORKLOADS["decode_512k_fp8"], dev, WORKLOADS["decode_512k_fp8"].decode_steps)
+        torch.cuda.empty_cache()
+    if not args.no_generation:
+        wg = WORKLOADS["generation_32k_bf16"]
+        out["generation"] = run_generation(wg, dev, wg.decode_steps)
         torch.cuda.empty_cache()
     if not args.no_early_exit:
         out["early_exit_1m"] = run_early_exit(WORKLOADS["early_exit_1m_bf16"], dev, args.extra_steps)

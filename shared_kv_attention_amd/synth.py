@@ -52,6 +52,11 @@ WORKLOADS = {
                                    128, 4, 8, 1024, 0.02),
     "decode_512k_fp8": Workload(5, "decode_512k_fp8", "fp8-kv", 8, 1 << 19, 0, 32, 8, 128,
                                 0, 16, 0, 0.0, decode_steps=8),
+    # one generated token per sequence at the decode shape: 16 self-decoder
+    # layers (window 1024, ring caches), the one-row global KV projection
+    # (hidden = 32 heads x 128), 16 cross-decoder layers over 32768 rows
+    "generation_32k_bf16": Workload(6, "generation_32k_bf16", "bf16", 16, 32768, 4096, 32, 8, 128,
+                                    16, 16, 1024, 0.02, decode_steps=16),
 }
 
 
