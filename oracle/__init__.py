@@ -27,6 +27,8 @@ Modules:
   fp8         OCP fp8-e4m3fn codec and per-head KV quantisation.
   block       the tiny YOCO block (self-decoder, projection, cross-decoder)
               and its early-exit variant.
+  retention   gated retention (recurrent, parallel, chunkwise) and its
+              per-head GroupNorm with swish gate.
   memory      closed-form KV-cache sizes the pages reason with.
 """
 
@@ -51,3 +53,10 @@ from .fp8 import (  # noqa: F401
 )
 from .block import BlockParams, yoco_block, yoco_block_early_exit, yoco_block_generate  # noqa: F401
 from .memory import yoco_kv_cache_bytes, transformer_kv_cache_bytes  # noqa: F401
+from .retention import (  # noqa: F401
+    gret_log_decay,
+    gret_recurrent,
+    gret_parallel,
+    gret_chunkwise,
+    gret_group_norm_swish,
+)
