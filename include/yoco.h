@@ -184,6 +184,57 @@ yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new,
 size_t yoco_swa_decode_workspace_bytes(int B, int Hq, int Hkv, int W, int d);
 
 /*
+ * Gated retention, the self-decoder's other choice (prefill, chunkwise form).
+ * Source: paperlayer.ai summary section 3 Gated Retention and appendix B;
+ * podcast segment 16 (retention with a data-dependent, head-wise scalar
+ * decay gate sigmoid(z)^(1/tau); recurrent, parallel and chunkwise forms give
+ * equal results; chunk size 256).  Per head (state S is d x d, [dk][dv]):
+ *     S_n = gamma_n S_{n-1} + k_n^T v_n,   o_n = q_n S_n,
+ *     gamma_n = sigmoid(gate_logit_n)^(1/tau)
+ * computed chunkwise over chunks of `chunk` positions.  No scale on q . k
+ * and no rotation (the per-head GroupNorm that follows cancels a scale).
+ *   q, k, v, o   [B, H, N, d] BF16          gate_logit [B, H, N] float32
+ *   state_in     [B, H, d, d] float32, or NULL for a zero state
+ *   state_out    [B, H, d, d] float32, or NULL: the state after position N-1
+ *                (feed it to yoco_gret_decode to continue)
+ *   tau > 0; d in {64, 128}; chunk in {128, 256}
+ *   workspace >= yoco_gret_prefill_workspace_bytes(B, H, N, d, chunk) bytes,
+ *   16-byte aligned, not shared by concurrent calls.
+ */
+yoco_status yoco_gret_prefill(const void* q, const void* k, const void* v, const float* gate_logit,
+                              float tau, const float* state_in, void* o, float* state_out,
+                              int B, int H, int N, int d, int chunk, yoco_dtype dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of yoco_gret_prefill for these sizes (0 on invalid sizes). */
+size_t yoco_gret_prefill_workspace_bytes(int B, int H, int N, int d, int chunk);
+
+/*
+ * Gated retention, one decode step (recurrent form): for every (b, h),
+ *     S <- gamma S + k^T v,  o = q S,  gamma = sigmoid(gate_logit)^(1/tau).
+ * Source: podcast segment 16 (recurrent form for decoding, one d x d state
+ * per head, constant memory); paperlayer.ai summary section 3.
+ *   q, k, v, o [B, H, d] (F32 or BF16)   gate_logit [B, H] float32
+ *   state      [B, H, d, d] float32, read and updated in place
+ *   tau > 0; d in {64, 128}
+ */
+yoco_status yoco_gret_decode(const void* q, const void* k, const void* v, const float* gate_logit,
+                             float tau, float* state, void* o, int B, int H, int d,
+                             yoco_dtype dtype, void* stream);
+
+/*
+ * Multi-head gated retention's output combination: each head's output is
+ * normalised over its d channels (GroupNorm with one group per head, unit
+ * gain, zero bias) and multiplied by a swish gate.
+ * Source: paperlayer.ai summary section 3 Gated Retention (heads combined
+ * with GroupNorm, plus a swish gate).
+ *   out[b, n, h*d + j] = swish(g[b, n, h*d + j]) * (y[b,h,n,j] - mean) / sqrt(var + eps)
+ *   y [B, H, N, d]; g, out [B, N, H*d]; F32 or BF16; d in {64, 128}; eps >= 0
+ */
+yoco_status yoco_gret_group_norm_swish(const void* y, const void* g, void* out, int B, int H, int N,
+                                       int d, float eps, yoco_dtype dtype, void* stream);
+
+/*
  * Quantise a K or V tensor to an 8-bit cache.
  * Source: podcast segments 1 and 24 (8-bit KV cache as the deployed form);
  * the format is fixed here: OCP e4m3fn, one float32 scale per KV head over

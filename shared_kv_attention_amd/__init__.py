@@ -28,6 +28,10 @@ __all__ = [
     "yoco_cross_attn_decode_workspace_bytes",
     "yoco_swa_decode",
     "yoco_swa_decode_workspace_bytes",
+    "yoco_gret_prefill",
+    "yoco_gret_prefill_workspace_bytes",
+    "yoco_gret_decode",
+    "yoco_gret_group_norm_swish",
     "yoco_kv_quantize_fp8",
     "yoco_kv_quantize_fp8_workspace_bytes",
     "yoco_status_string",
@@ -53,6 +57,10 @@ _SIGS = {
     "yoco_cross_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "yoco_swa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "yoco_swa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "yoco_gret_prefill": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "yoco_gret_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "yoco_gret_decode": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _i, _i, _i, _vp]),
+    "yoco_gret_group_norm_swish": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
     "yoco_kv_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "yoco_kv_quantize_fp8_workspace_bytes": (_sz, [_i]),
     "yoco_status_string": (ctypes.c_char_p, [_i]),
@@ -212,6 +220,56 @@ def yoco_swa_decode(q, k_ring, v_ring, pos, k_new=None, v_new=None, o=None, lse=
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "yoco_swa_decode")
     return o
+
+
+def yoco_gret_prefill_workspace_bytes(B, H, N, d, chunk=256):
+    return lib().yoco_gret_prefill_workspace_bytes(B, H, N, d, chunk)
+
+
+def yoco_gret_prefill(q, k, v, gate_logit, tau, state_in=None, o=None, state_out=None, chunk=256, workspace=None,
+                      stream=None):
+    """Gated retention, chunkwise: q, k, v [B, H, N, d] bf16, gate_logit [B, H, N] f32; returns (o, state_out).
+    state_out is allocated ([B, H, d, d] f32) unless given; pass state_out=False to skip it."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    need = yoco_gret_prefill_workspace_bytes(B, H, N, d, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if state_out is None:
+        state_out = torch.empty(B, H, d, d, dtype=torch.float32, device=q.device)
+    elif state_out is False:
+        state_out = None
+    st = lib().yoco_gret_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate_logit), float(tau), _ptr(state_in), _ptr(o), _ptr(state_out),
+        B, H, N, d, int(chunk), _dtype_code(q), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "yoco_gret_prefill")
+    return o, state_out
+
+
+def yoco_gret_decode(q, k, v, gate_logit, tau, state, o=None, stream=None):
+    """Gated retention, one recurrent step: q, k, v [B, H, d]; gate_logit [B, H] f32; state [B, H, d, d] f32
+    (updated in place).  Returns o."""
+    B, H, d = q.shape
+    if o is None:
+        o = _torch().empty_like(q)
+    st = lib().yoco_gret_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(gate_logit), float(tau), _ptr(state), _ptr(o),
+                                B, H, d, _dtype_code(q), _stream(stream))
+    _check(st, "yoco_gret_decode")
+    return o
+
+
+def yoco_gret_group_norm_swish(y, g, out=None, eps=1e-6, stream=None):
+    """Per-head GroupNorm of y [B, H, N, d] times swish(g) ([B, N, H*d]); returns out [B, N, H*d]."""
+    B, H, N, d = y.shape
+    if out is None:
+        out = _torch().empty_like(g)
+    st = lib().yoco_gret_group_norm_swish(_ptr(y), _ptr(g), _ptr(out), B, H, N, d, float(eps), _dtype_code(y),
+                                          _stream(stream))
+    _check(st, "yoco_gret_group_norm_swish")
+    return out
 
 
 def yoco_kv_quantize_fp8_workspace_bytes(Hkv):

@@ -229,6 +229,103 @@ yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new,
   return launched(yoco::launch_decode(a, kind, kind, d, as_stream(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+struct GretLayout {
+  size_t lg2, lam, dR, rin, total;
+};
+
+bool gret_sizes_ok(int B, int H, int N, int d, int chunk) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || (chunk != 128 && chunk != 256)) return false;
+  const long long nc = (N + chunk - 1) / chunk;
+  return (long long)B * H <= 65535 && (long long)B * H * N <= kIntMax && nc * (chunk / 128) <= 65535;
+}
+
+GretLayout gret_layout(int B, int H, int N, int d, int chunk) {
+  GretLayout L{};
+  const size_t bh = (size_t)B * H, nc = (size_t)(N + chunk - 1) / chunk;
+  L.lg2 = 0;
+  L.lam = align16(bh * N * sizeof(float));
+  L.dR = L.lam + align16(bh * nc * sizeof(float));
+  L.rin = L.dR + align16(bh * nc * d * d * sizeof(float));
+  L.total = L.rin + align16(bh * nc * d * d * 2);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t yoco_gret_prefill_workspace_bytes(int B, int H, int N, int d, int chunk) {
+  if (!gret_sizes_ok(B, H, N, d, chunk)) return 0;
+  return gret_layout(B, H, N, d, chunk).total;
+}
+
+yoco_status yoco_gret_prefill(const void* q, const void* k, const void* v, const float* gate_logit, float tau,
+                              const float* state_in, void* o, float* state_out, int B, int H, int N, int d,
+                              int chunk, yoco_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !gate_logit || !o) return YOCO_ERR_NULL;
+  if (dtype != YOCO_BF16) return YOCO_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 1 || !(tau > 0.f)) return YOCO_ERR_SHAPE;
+  if (d != 64 && d != 128) return YOCO_ERR_UNSUPPORTED;
+  if (chunk != 128 && chunk != 256) return YOCO_ERR_UNSUPPORTED;
+  if (!gret_sizes_ok(B, H, N, d, chunk)) return YOCO_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(gate_logit, 4) ||
+      (state_in && !aligned(state_in, 4)) || (state_out && !aligned(state_out, 4)))
+    return YOCO_ERR_ALIGN;
+  const GretLayout L = gret_layout(B, H, N, d, chunk);
+  if (!workspace || workspace_bytes < L.total) return YOCO_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  yoco::GretArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate_logit;
+  a.inv_tau = 1.f / tau;
+  a.state_in = state_in;
+  a.o = o;
+  a.state_out = state_out;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.chunk = chunk;
+  a.nc = (N + chunk - 1) / chunk;
+  a.lg2 = reinterpret_cast<float*>(ws + L.lg2);
+  a.lam = reinterpret_cast<float*>(ws + L.lam);
+  a.dR = reinterpret_cast<float*>(ws + L.dR);
+  a.rin = ws + L.rin;
+  return launched(yoco::launch_gret_prefill(a, as_stream(stream)));
+}
+
+yoco_status yoco_gret_decode(const void* q, const void* k, const void* v, const float* gate_logit, float tau,
+                             float* state, void* o, int B, int H, int d, yoco_dtype dtype, void* stream) {
+  if (!q || !k || !v || !gate_logit || !state || !o) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (B < 1 || H < 1 || (long long)B * H > 65535 || !(tau > 0.f)) return YOCO_ERR_SHAPE;
+  if (d != 64 && d != 128) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4) || !aligned(gate_logit, 4) ||
+      !aligned(state, 4))
+    return YOCO_ERR_ALIGN;
+  yoco::GretDecodeArgs a{q, k, v, gate_logit, 1.f / tau, state, o, B, H, d};
+  return launched(yoco::launch_gret_decode(a, dtype == YOCO_BF16, as_stream(stream)));
+}
+
+yoco_status yoco_gret_group_norm_swish(const void* y, const void* g, void* out, int B, int H, int N, int d,
+                                       float eps, yoco_dtype dtype, void* stream) {
+  if (!y || !g || !out) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (B < 1 || H < 1 || N < 1 || !(eps >= 0.f) || isinf(eps)) return YOCO_ERR_SHAPE;
+  if (((long long)B * N * H + 3) / 4 > kIntMax) return YOCO_ERR_SHAPE;
+  if (d != 64 && d != 128) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(y, 4) || !aligned(g, 4) || !aligned(out, 4)) return YOCO_ERR_ALIGN;
+  yoco::GretNormArgs a{y, g, out, B, H, N, d, eps};
+  return launched(yoco::launch_gret_norm(a, dtype == YOCO_BF16, as_stream(stream)));
+}
+
 size_t yoco_kv_quantize_fp8_workspace_bytes(int Hkv) {
   if (Hkv < 1) return 0;
   return align16((size_t)Hkv * sizeof(uint32_t));

@@ -32,6 +32,7 @@
 //    XCDs round-robin), so each XCD's L2 holds one KV head's K/V.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tile_lds.hpp"
 
 namespace yoco {
 
@@ -57,99 +58,6 @@ struct AttnCfg {
   static_assert(PER_T >= 1 && BK * CH % NT == 0, "tile must split over the workgroup");
   static constexpr int MIN_WAVES_PER_EU = (RB == 2) ? 1 : 2;
 };
-
-// Row index permutation: swap bits 2 and 3.
-__device__ __forceinline__ int sigma(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-// XOR swizzles of the 16-byte chunk index within a tile row, chosen so that
-// the reads of one instruction spread over all banks whether the LDS serves
-// 8 or 16 lanes of 16-byte accesses per cycle.
-// K tile: a wave reads 32 rows at once in the permuted order sigma(r): rows
-// sigma(0..7) and sigma(0..15) map to distinct chunk columns.
-template <int CH>
-__device__ __forceinline__ int swz_k(int row) {
-  if constexpr (CH >= 16) return sigma(row) & 15;
-  else return (row & 3) | ((row >> 1) & 4);
-}
-// V tile: the transpose loads of 16 lanes read 4 consecutive rows x 32 bytes;
-// 32 lanes read the same 4 rows x 64 bytes.
-template <int CH>
-__device__ __forceinline__ int swz_v(int row) {
-  if constexpr (CH >= 16) return 4 * (row & 3) + 2 * ((row >> 1) & 1);
-  else return 2 * (row & 3);
-}
-
-template <typename T>
-__device__ __forceinline__ typename Elem<T>::frag load_frag_global(const T* p) {
-  typename Elem<T>::frag f;
-  if constexpr (sizeof(T) == 2) {
-    f = *reinterpret_cast<const bf16x8*>(p);
-  } else {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-    f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  }
-  return f;
-}
-
-// K fragment: elements [16c + 8g, 16c + 8g + 8) of LDS row `row`.
-template <typename T, int D>
-__device__ __forceinline__ typename Elem<T>::frag lds_frag_k(const char* tile, int row, int c, int g) {
-  using C = AttnCfg<T, D>;
-  const char* rowp = tile + row * C::CH * 16;
-  const int sw = swz_k<C::CH>(row);
-  typename Elem<T>::frag f;
-  if constexpr (sizeof(T) == 2) {
-    const int ch = 2 * c + g;
-    f = *reinterpret_cast<const bf16x8*>(rowp + ((ch ^ sw) << 4));
-  } else {
-    const int ch = 4 * c + 2 * g;
-    f32x4 a = *reinterpret_cast<const f32x4*>(rowp + ((ch ^ sw) << 4));
-    f32x4 b = *reinterpret_cast<const f32x4*>(rowp + (((ch + 1) ^ sw) << 4));
-    f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  }
-  return f;
-}
-
-// V^T fragment for the O^T = V^T P^T step: lane l (row = l%32 -> dim
-// db*32 + l%32; k = 8*(l/32) + j -> key 16c + 8*(l/32) + j).
-template <typename T, int D>
-__device__ __forceinline__ typename Elem<T>::frag lds_frag_vt(const char* tile, int c, int db, int l) {
-  using C = AttnCfg<T, D>;
-  typename Elem<T>::frag f;
-  if constexpr (sizeof(T) == 2) {
-    // ds_read_b64_tr_b16 works on groups of 16 lanes: lane i supplies the
-    // address of 4 consecutive 16-bit elements (row i/4, columns 4*(i%4)..+3
-    // of a 4x16 block); lane j receives column j of that block, i.e. the 4
-    // elements of rows 0..3 at column j.
-    const int G = l >> 4, j16 = l & 15;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int row = 16 * c + 8 * (G >> 1) + 4 * hh + (j16 >> 2);
-      const int col = db * 32 + 16 * (G & 1) + 4 * (j16 & 3);
-      const int ch = col >> 3;
-      const char* p = tile + row * C::CH * 16 + ((ch ^ swz_v<C::CH>(row)) << 4) + ((col & 7) << 1);
-      i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(p));
-      bf16x4 rb = __builtin_bit_cast(bf16x4, r);
-      f[4 * hh + 0] = rb[0];
-      f[4 * hh + 1] = rb[1];
-      f[4 * hh + 2] = rb[2];
-      f[4 * hh + 3] = rb[3];
-    }
-  } else {
-    const int g = l >> 5, col = db * 32 + (l & 31);
-    const int ch = col >> 2, off = (col & 3) << 2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 16 * c + 8 * g + j;
-      f[j] = *reinterpret_cast<const float*>(tile + row * C::CH * 16 + ((ch ^ swz_v<C::CH>(row)) << 4) + off);
-    }
-  }
-  return f;
-}
 
 // Scheduler hints for a run of NS matrix-core slots whose LDS operand (R
 // reads each) is fetched PD slots ahead: the reads of the first PD slots,
@@ -310,12 +218,12 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s[0][kb] = f32x16{};
 #pragma unroll
-        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_k<T, D>(ktile, (n % C::NKB) * 32 + krow, n / C::NKB, g);
+        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_k<T, C::CH>(ktile, (n % C::NKB) * 32 + krow, n / C::NKB, g);
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           if (n + PD < NS) {
             const int m = n + PD;
-            ring[m % (PD + 1)] = lds_frag_k<T, D>(ktile, (m % C::NKB) * 32 + krow, m / C::NKB, g);
+            ring[m % (PD + 1)] = lds_frag_k<T, C::CH>(ktile, (m % C::NKB) * 32 + krow, m / C::NKB, g);
           }
           s[0][n % C::NKB] = mma32(ring[n % (PD + 1)], qf[0][n / C::NKB], s[0][n % C::NKB]);
         }
@@ -329,7 +237,7 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
           const int krow = kb * 32 + sigma(r32);
 #pragma unroll
           for (int c = 0; c < C::NC; ++c) {
-            const frag kf = lds_frag_k<T, D>(ktile, krow, c, g);
+            const frag kf = lds_frag_k<T, C::CH>(ktile, krow, c, g);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mma32(kf, qf[rb][c], s[rb][kb]);
           }
@@ -405,12 +313,12 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
         constexpr int NS = C::NPC * C::NDB, PD = C::FRAG_AHEAD;
         frag ring[PD + 1];
 #pragma unroll
-        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_vt<T, D>(vtile, n / C::NDB, n % C::NDB, l);
+        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_vt<T, C::CH>(vtile, n / C::NDB, n % C::NDB, l);
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           if (n + PD < NS) {
             const int m = n + PD;
-            ring[m % (PD + 1)] = lds_frag_vt<T, D>(vtile, m / C::NDB, m % C::NDB, l);
+            ring[m % (PD + 1)] = lds_frag_vt<T, C::CH>(vtile, m / C::NDB, m % C::NDB, l);
           }
           acc_o[0][n % C::NDB] = mma32(ring[n % (PD + 1)], pf[0][n / C::NDB], acc_o[0][n % C::NDB]);
         }
@@ -421,7 +329,7 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
         for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
           for (int c = 0; c < C::NPC; ++c) {
-            const frag vf = lds_frag_vt<T, D>(vtile, c, db, l);
+            const frag vf = lds_frag_vt<T, C::CH>(vtile, c, db, l);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = mma32(vf, pf[rb][c], acc_o[rb][db]);
           }

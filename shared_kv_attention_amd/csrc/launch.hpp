@@ -61,6 +61,41 @@ struct RingAppendArgs {
   int row_bytes;       // d * element size (a multiple of 4)
 };
 
+struct GretArgs {
+  const void* q;           // [B, H, N, d] bf16
+  const void* k;
+  const void* v;
+  const float* gate;       // [B, H, N] gate logits z
+  float inv_tau;           // 1 / temperature
+  const float* state_in;   // [B, H, d, d] or null (zero state)
+  void* o;                 // [B, H, N, d] bf16
+  float* state_out;        // [B, H, d, d] or null
+  int B, H, N, d, chunk, nc;
+  float* lg2;              // workspace: [B, H, N] log2 decay, prefix sums within each chunk
+  float* lam;              // workspace: [B, H, nc] total decay of each chunk
+  float* dR;               // workspace: [B, H, nc, d, d] per-chunk state contributions
+  void* rin;               // workspace: [B, H, nc, d, d] bf16 state entering each chunk
+};
+
+struct GretDecodeArgs {
+  const void* q;           // [B, H, d]
+  const void* k;
+  const void* v;
+  const float* gate;       // [B, H] gate logits
+  float inv_tau;
+  float* state;            // [B, H, d, d] float32, updated in place
+  void* o;                 // [B, H, d]
+  int B, H, d;
+};
+
+struct GretNormArgs {
+  const void* y;           // [B, H, N, d]
+  const void* g;           // [B, N, H*d]
+  void* out;               // [B, N, H*d]
+  int B, H, N, d;
+  float eps;
+};
+
 struct QuantArgs {
   const void* kv;
   uint8_t* codes;
@@ -75,6 +110,9 @@ hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hi
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
+hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t stream);
+hipError_t launch_gret_decode(const GretDecodeArgs& a, bool is_bf16, hipStream_t stream);
+hipError_t launch_gret_norm(const GretNormArgs& a, bool is_bf16, hipStream_t stream);
 
 // Split plan of the decode kernel (host code, plan.cpp); the workspace size
 // follows from it.  At most kDecodeMaxSplits splits (the combine pass keeps one

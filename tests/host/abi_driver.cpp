@@ -2,6 +2,7 @@
 // valid argument sets must reach the launcher with the expected argument
 // block, invalid ones must return their status without launching, and the
 // decode workspace layout must fit in exactly the bytes the query returns.
+#include <array>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -17,6 +18,7 @@ extern DecodeArgs g_decode;
 extern ProjArgs g_proj;
 extern QuantArgs g_quant;
 extern RingAppendArgs g_ring;
+extern GretArgs g_gret;
 extern int g_decode_kinds[3];
 }  // namespace yoco
 
@@ -129,6 +131,32 @@ int main() {
     CHECK(yoco::g_launches == n + 1);
     std::free(ws);
   }
+
+  // ---- gated retention: the prefill workspace holds every region it is split into
+  for (const auto& s : {std::array<int, 5>{1, 24, 4096, 128, 256}, std::array<int, 5>{3, 2, 77, 64, 128},
+                        std::array<int, 5>{2, 4, 1, 128, 256}, std::array<int, 5>{1, 1, 300, 64, 256}}) {
+    const int B = s[0], H = s[1], N = s[2], d = s[3], chunk = s[4];
+    const size_t need = yoco_gret_prefill_workspace_bytes(B, H, N, d, chunk);
+    CHECK(need > 0 && need % 16 == 0);
+    unsigned char* ws = (unsigned char*)std::malloc(need);
+    n = yoco::g_launches;
+    CHECK(yoco_gret_prefill(P, P, P, (const float*)P, 4.f, nullptr, P, nullptr, B, H, N, d, chunk, YOCO_BF16, ws, need,
+                            nullptr) == YOCO_OK);
+    CHECK(yoco::g_launches == n + 1);
+    const yoco::GretArgs& a = yoco::g_gret;
+    const size_t bh = (size_t)B * H, nc = (size_t)(N + chunk - 1) / chunk;
+    CHECK(a.nc == (int)nc && a.inv_tau == 0.25f);
+    CHECK((unsigned char*)a.lg2 == ws);
+    CHECK((unsigned char*)(a.lg2 + bh * N) <= (unsigned char*)a.lam);
+    CHECK((unsigned char*)(a.lam + bh * nc) <= (unsigned char*)a.dR);
+    CHECK((unsigned char*)(a.dR + bh * nc * d * d) <= (unsigned char*)a.rin);
+    CHECK((unsigned char*)a.rin + bh * nc * d * d * 2 <= ws + need);
+    CHECK(yoco_gret_prefill(P, P, P, (const float*)P, 4.f, nullptr, P, nullptr, B, H, N, d, chunk, YOCO_BF16, ws,
+                            need - 1, nullptr) == YOCO_ERR_WORKSPACE);
+    std::free(ws);
+  }
+  CHECK(yoco_gret_prefill_workspace_bytes(1, 1, 10, 96, 256) == 0);
+  CHECK(yoco_gret_prefill_workspace_bytes(1, 1, 10, 64, 192) == 0);
 
   // ---- fp8 quantiser
   n = yoco::g_launches;

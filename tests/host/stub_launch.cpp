@@ -11,6 +11,9 @@ DecodeArgs g_decode;
 ProjArgs g_proj;
 QuantArgs g_quant;
 RingAppendArgs g_ring;
+GretArgs g_gret;
+GretDecodeArgs g_gret_dec;
+GretNormArgs g_gret_norm;
 int g_decode_kinds[3];
 
 hipError_t launch_attn(const AttnArgs& a, bool, int, bool, hipStream_t) { ++g_launches; g_attn = a; return hipSuccess; }
@@ -20,4 +23,7 @@ hipError_t launch_decode(const DecodeArgs& a, int qk, int kk, int d, hipStream_t
 hipError_t launch_kv_proj(const ProjArgs& a, bool, hipStream_t) { ++g_launches; g_proj = a; return hipSuccess; }
 hipError_t launch_quant_fp8(const QuantArgs& a, bool, hipStream_t) { ++g_launches; g_quant = a; return hipSuccess; }
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t) { ++g_launches; g_ring = a; return hipSuccess; }
+hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t) { ++g_launches; g_gret = a; return hipSuccess; }
+hipError_t launch_gret_decode(const GretDecodeArgs& a, bool, hipStream_t) { ++g_launches; g_gret_dec = a; return hipSuccess; }
+hipError_t launch_gret_norm(const GretNormArgs& a, bool, hipStream_t) { ++g_launches; g_gret_norm = a; return hipSuccess; }
 }  // namespace yoco

@@ -176,6 +176,56 @@ def test_swa_decode_workspace_covers_every_position(L):
         assert yk.yoco_swa_decode_workspace_bytes(*bad) == 0
 
 
+def gret(L, **kw):
+    a = dict(q=P, k=P, v=P, z=P, tau=4.0, s_in=None, o=P, s_out=None, B=1, H=2, N=300, d=128, chunk=256,
+             dt=yk.BF16, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.yoco_gret_prefill(a["q"], a["k"], a["v"], a["z"], a["tau"], a["s_in"], a["o"], a["s_out"], a["B"], a["H"],
+                               a["N"], a["d"], a["chunk"], a["dt"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(z=None), NULL), (dict(o=None), NULL),
+    (dict(dt=yk.F32), DTYPE), (dict(dt=yk.FP8_E4M3), DTYPE),
+    (dict(N=0), SHAPE), (dict(tau=0.0), SHAPE), (dict(tau=-1.0), SHAPE), (dict(tau=float("nan")), SHAPE),
+    (dict(d=96), UNSUP), (dict(chunk=64), UNSUP), (dict(chunk=512), UNSUP),
+    (dict(k=MIS), ALIGN), (dict(s_out=4096 + 2), ALIGN), (dict(ws=MIS), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=16), WS),
+])
+def test_gret_prefill_errors(L, kw, code):
+    assert gret(L, **kw) == code
+
+
+def test_gret_workspace_query(L):
+    need = yk.yoco_gret_prefill_workspace_bytes(1, 2, 300, 128, 256)
+    assert need >= 2 * 300 * 4 + 2 * 2 * 128 * 128 * 6 and need % 16 == 0
+    assert gret(L, wsb=need - 1) == WS
+    for bad in [(0, 2, 300, 128, 256), (1, 2, 0, 128, 256), (1, 2, 300, 32, 256), (1, 2, 300, 128, 100)]:
+        assert yk.yoco_gret_prefill_workspace_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(state=None), NULL), (dict(dt=yk.FP8_E4M3), DTYPE), (dict(B=0), SHAPE),
+    (dict(tau=0.0), SHAPE), (dict(d=32), UNSUP), (dict(state=4096 + 2), ALIGN),
+])
+def test_gret_decode_errors(L, kw, code):
+    a = dict(q=P, k=P, v=P, z=P, tau=4.0, state=P, o=P, B=2, H=3, d=128, dt=yk.BF16)
+    a.update(kw)
+    assert L.yoco_gret_decode(a["q"], a["k"], a["v"], a["z"], a["tau"], a["state"], a["o"], a["B"], a["H"], a["d"],
+                              a["dt"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(y=None), NULL), (dict(dt=yk.FP8_E4M3), DTYPE), (dict(N=0), SHAPE), (dict(eps=-1.0), SHAPE),
+    (dict(d=100), UNSUP), (dict(out=4096 + 1), ALIGN),
+])
+def test_gret_norm_errors(L, kw, code):
+    a = dict(y=P, g=P, out=P, B=2, H=3, N=5, d=64, eps=1e-6, dt=yk.F32)
+    a.update(kw)
+    assert L.yoco_gret_group_norm_swish(a["y"], a["g"], a["out"], a["B"], a["H"], a["N"], a["d"], a["eps"], a["dt"],
+                                        None) == code
+
+
 def quant(L, **kw):
     a = dict(kv=P, dt=yk.F32, codes=P, scale=P, B=2, Hkv=4, n=10, d=64, ws=P, wsb=64)
     a.update(kw)
