@@ -320,6 +320,72 @@ def run_generation(wl, dev, steps):
     }
 
 
+# ---------------------------------------------------------------- gated retention
+def run_gret(wl, dev, reps, decode_batch=16, chunk=256, tau=16.0):
+    """Gated-retention self-decoder layer (chunkwise prefill) at the 3B shape,
+    and its recurrent decode step.  Gate logits ~ N(3, 1) with tau 16 (decay
+    close to 1, the regime the temperature is there to produce)."""
+    B, N, H, d, wid = wl.batch, wl.seq, wl.n_heads, wl.head_dim, wl.wid
+    s = d ** -0.25
+    q = randn((B, H, N, d), seed_for(wid, 0), std=s, device=dev)
+    k = randn((B, H, N, d), seed_for(wid, 1), std=s, device=dev)
+    v = randn((B, H, N, d), seed_for(wid, 2), device=dev)
+    z = randn((B, H, N), seed_for(wid, 3), dtype="f32", device=dev) + 3.0
+    o = torch.empty_like(q)
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    ws = torch.empty(yk.yoco_gret_prefill_workspace_bytes(B, H, N, d, chunk), dtype=torch.uint8, device=dev)
+
+    def prefill():
+        yk.yoco_gret_prefill(q, k, v, z, tau, o=o, state_out=st, chunk=chunk, workspace=ws)
+
+    Bd = decode_batch
+    qd = randn((Bd, H, d), seed_for(wid, 4), std=s, device=dev)
+    kd = randn((Bd, H, d), seed_for(wid, 5), std=s, device=dev)
+    vd = randn((Bd, H, d), seed_for(wid, 6), device=dev)
+    zd = randn((Bd, H), seed_for(wid, 7), dtype="f32", device=dev) + 3.0
+    sd = randn((Bd, H, d, d), seed_for(wid, 8), std=0.1, dtype="f32", device=dev)
+    od = torch.empty_like(qd)
+
+    def decode():
+        yk.yoco_gret_decode(qd, kd, vd, zd, tau, sd, o=od)
+
+    res = {}
+    for name, fn in (("prefill", prefill), ("decode", decode)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        res[name] = sum(events_ms(ev)) / len(ev)
+    nc = (N + chunk - 1) // chunk
+    pairs = sum(min(chunk, N - c * chunk) * (min(chunk, N - c * chunk) + 1) // 2 for c in range(nc))
+    flops = B * H * (4.0 * d * pairs + 2 * 2.0 * N * d * d)      # inner QK^T and WV; cross Q R and state K^T V
+    pbytes = B * H * N * (4 * d * 2 + 4)                            # q, k, v, o (bf16) and the gate logits
+    dbytes = Bd * H * (2 * d * d * 4 + 4 * d * 2 + 4)               # state read + written, q, k, v, o, gate
+    pgbs = pbytes / (res["prefill"] * 1e-3) / 1e9
+    dgbs = dbytes / (res["decode"] * 1e-3) / 1e9
+    return {
+        "workload": wl.name,
+        "prefill": {"batch": B, "seq_len": N, "heads": H, "head_dim": d, "chunk": chunk,
+                    "ms_per_layer": res["prefill"], "TFLOP/s": flops / (res["prefill"] * 1e-3) / 1e12,
+                    "GB/s": pgbs,
+                    "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": pgbs / HBM_PEAK_GBS, "traffic": None},
+                    "flops_per_layer": flops, "bytes_per_layer": pbytes},
+        "decode": {"batch": Bd, "heads": H, "head_dim": d, "ms_per_step": res["decode"], "GB/s": dgbs,
+                   "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dgbs / HBM_PEAK_GBS, "traffic": None},
+                   "bytes_per_step": dbytes},
+        "timing": "HIP events around each call (prefill: 4 kernels; decode: 1 kernel)",
+    }
+
+
 # ---------------------------------------------------------------- early exit
 def run_early_exit(wl, dev, steps):
     """1M-token early-exit prefill: L_s SWA layers over all tokens, the global
@@ -413,6 +479,7 @@ def main():
                     help="skip the 1M-token early-exit flow measurement (allocates ~110 GB)")
     ap.add_argument("--extra-steps", type=int, default=3, help="steps of the 1M early-exit flow")
     ap.add_argument("--no-generation", action="store_true", help="skip the one-token generation step measurement")
+    ap.add_argument("--no-gret", action="store_true", help="skip the gated-retention measurement")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -501,6 +568,9 @@ def main():
     if not args.no_generation:
         wg = WORKLOADS["generation_32k_bf16"]
         out["generation"] = run_generation(wg, dev, wg.decode_steps)
+        torch.cuda.empty_cache()
+    if not args.no_gret:
+        out["gated_retention"] = run_gret(WORKLOADS["gret_3b_bf16"], dev, 20)
         torch.cuda.empty_cache()
     if not args.no_early_exit:
         out["early_exit_1m"] = run_early_exit(WORKLOADS["early_exit_1m_bf16"], dev, args.extra_steps)

@@ -11,18 +11,20 @@
 //   R  <- e^{L_last} R + sum_{m in chunk} e^{L_last - L_m} k_m^T v_m.
 //
 // Design (MI355X-first): instead of one workgroup walking a head's chunks in
-// order (only B*H workgroups), the prefill runs four launches that are each
+// order (only B*H workgroups), the prefill runs three launches that are each
 // parallel over chunks:
-//  1. gates:  per chunk, log2 decay prefix sums and the chunk's total decay;
-//  2. state:  per chunk, dR = K^T (V scaled by e^{L_last - L_m}) on the
+//  1. state:  per chunk, the log2 decay prefix sums and the chunk's total
+//             decay, then dR = K^T (V scaled by e^{L_last - L_m}) on the
 //             matrix cores (both operands read transposed from LDS);
-//  3. scan:   per (head, state element), R_c = e^{L_last} R_{c-1} + dR_c in
-//             float32, storing the state entering every chunk;
-//  4. output: per (chunk, 128 query rows), an attention-like tile loop with
+//  2. scan:   per (head, 32 x 32 block of the state), R_c = e^{L_last}
+//             R_{c-1} + dR_c in float32, storing the state entering every
+//             chunk transposed (through LDS) in the operand layout of 3;
+//  3. output: per (chunk, 128 query rows), an attention-like tile loop with
 //             decay weights e^{L_n - L_m} (formed per pair from the
 //             difference, so a strong gate can never overflow) instead of a
-//             softmax, and the cross-chunk term R^T Q^T on the same
-//             accumulator.
+//             softmax, with direct global -> LDS double-buffered K/V tiles,
+//             and the cross-chunk term R^T Q^T (fragments from L2) on the
+//             same accumulator.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_lds.hpp"
@@ -45,78 +47,81 @@ __device__ __forceinline__ float gate_log2(float z, float inv_tau) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. per-chunk inclusive prefix sums of log2 decay; total decay per chunk
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gret_gate_kernel(GretArgs a) {
-  __shared__ float buf[256];
-  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const int n = c * a.chunk + t;
-  const bool valid = t < a.chunk && n < a.N;
-  float x = valid ? gate_log2(a.gate[(size_t)bh * a.N + n], a.inv_tau) : 0.f;
-  buf[t] = x;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const float y = t >= off ? buf[t - off] : 0.f;
-    __syncthreads();
-    x += y;
-    buf[t] = x;
-    __syncthreads();
-  }
-  if (valid) a.lg2[(size_t)bh * a.N + n] = x;
-  const int last = min(a.chunk, a.N - c * a.chunk) - 1;
-  if (t == last) a.lam[(size_t)bh * a.nc + c] = __builtin_amdgcn_exp2f(x);
-}
-
-// Stage rows [r0, r0 + BK) of a [N, D] bf16 matrix into an LDS tile with the
-// transposed-read swizzle; rows >= N (or outside the chunk) become zero.  If
-// scale is given, row r is multiplied by scale(r) (float32, then bf16 RNE).
-template <int D, typename F>
-__device__ __forceinline__ void stage_rows_v(char* tile, const bf16* src, int r0, int rows_valid, F scale,
-                                             bool scaled) {
-  using C = GretCfg<D>;
-  for (int slot = threadIdx.x; slot < C::BK * C::CH; slot += 256) {
-    const int row = slot / C::CH, pch = slot % C::CH;   // physical chunk pch holds logical chunk pch ^ swz
-    const int lch = pch ^ swz_v<C::CH>(row);
-    u32x4 w{0, 0, 0, 0};
-    if (row < rows_valid) {
-      w = *reinterpret_cast<const u32x4*>(src + (size_t)(r0 + row) * D + lch * 8);
-      if (scaled) {
-        const float f = scale(row);
-        bf16x8 v = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)v[e] * f);
-        w = __builtin_bit_cast(u32x4, v);
-      }
-    }
-    *reinterpret_cast<u32x4*>(tile + row * C::CH * 16 + pch * 16) = w;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. per-chunk state contribution dR[dk][dv] = sum_m K[m][dk] V[m][dv] w_m
+// 1+2. per chunk: log2-decay prefix sums (written out for the output kernel)
+//      and the state contribution dR[dk][dv] = sum_m K[m][dk] V[m][dv] w_m,
+//      w_m = 2^{L_last - L_m}
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
   using C = GretCfg<D>;
   __shared__ __attribute__((aligned(16))) char kt[C::TILE], vt[C::TILE];
-  const int c = blockIdx.x, bh = blockIdx.y;
-  const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ float lgc[256];
+  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int l = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int c0 = c * a.chunk, clen = min(a.chunk, a.N - c0);
+
+  // inclusive prefix sum of the chunk's log2 decays (positions past the end add 0)
+  {
+    float x = t < clen ? gate_log2(a.gate[(size_t)bh * a.N + c0 + t], a.inv_tau) : 0.f;
+    lgc[t] = x;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const float y = t >= off ? lgc[t - off] : 0.f;
+      __syncthreads();
+      x += y;
+      lgc[t] = x;
+      __syncthreads();
+    }
+    if (t < clen) a.lg2[(size_t)bh * a.N + c0 + t] = x;
+    if (t == clen - 1) a.lam[(size_t)bh * a.nc + c] = __builtin_amdgcn_exp2f(x);
+  }
+  const float l_last = lgc[clen - 1];
+
   const bf16* kb = static_cast<const bf16*>(a.k) + ((size_t)bh * a.N + c0) * D;
   const bf16* vb = static_cast<const bf16*>(a.v) + ((size_t)bh * a.N + c0) * D;
-  const float* lg = a.lg2 + (size_t)bh * a.N + c0;
-  const float l_last = lg[clen - 1];
-
   constexpr int TILES = C::NDB * C::NDB, TPW = TILES / 4 > 0 ? TILES / 4 : 1;
   f32x16 acc[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
   const bool active = w * TPW < TILES;
 
-  for (int r0 = 0; r0 < clen; r0 += C::BK) {
+  // Each thread owns the same PER_T chunk slots of every tile; the raw chunks
+  // of tile r0 + BK are loaded into registers while tile r0 is multiplied.
+  constexpr int PER_T = C::BK * C::CH / 256;
+  u32x4 kraw[PER_T], vraw[PER_T];
+  auto fetch = [&](int r0) {
     const int rows = min(C::BK, clen - r0);
-    stage_rows_v<D>(kt, kb, r0, rows, [](int) { return 1.f; }, false);
-    stage_rows_v<D>(vt, vb, r0, rows, [&](int row) { return __builtin_amdgcn_exp2f(l_last - lg[r0 + row]); }, true);
+#pragma unroll
+    for (int r = 0; r < PER_T; ++r) {
+      const int slot = 256 * r + t, row = slot / C::CH, pch = slot % C::CH;
+      const int lch = pch ^ swz_v<C::CH>(row);
+      const size_t off = (size_t)(r0 + min(row, rows - 1)) * D + lch * 8;
+      kraw[r] = *reinterpret_cast<const u32x4*>(kb + off);
+      vraw[r] = *reinterpret_cast<const u32x4*>(vb + off);
+    }
+  };
+  auto put = [&](int r0) {   // rows past the chunk become zero; V rows scaled by 2^{L_last - L_m}
+    const int rows = min(C::BK, clen - r0);
+#pragma unroll
+    for (int r = 0; r < PER_T; ++r) {
+      const int slot = 256 * r + t, row = slot / C::CH;
+      u32x4 kw{0, 0, 0, 0}, vw{0, 0, 0, 0};
+      if (row < rows) {
+        kw = kraw[r];
+        const float f = __builtin_amdgcn_exp2f(l_last - lgc[r0 + row]);
+        bf16x8 v = __builtin_bit_cast(bf16x8, vraw[r]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)((float)v[e] * f);
+        vw = __builtin_bit_cast(u32x4, v);
+      }
+      *reinterpret_cast<u32x4*>(kt + slot * 16) = kw;
+      *reinterpret_cast<u32x4*>(vt + slot * 16) = vw;
+    }
+  };
+  fetch(0);
+  for (int r0 = 0; r0 < clen; r0 += C::BK) {
+    put(r0);
+    if (r0 + C::BK < clen) fetch(r0 + C::BK);
     __syncthreads();
     if (active) {
 #pragma unroll
@@ -145,34 +150,69 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. scan over chunks: rin_c = R_{c-1} (bf16), R_c = lam_c R_{c-1} + dR_c
+// 3. scan over chunks on 32 x 32 blocks of the state: R_c = lam_c R_{c-1} + dR_c
+//    in float32; the state entering chunk c is stored transposed in bf16
+//    (rinT[c][dv][dk], the operand layout of the output kernel's R^T Q^T)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gret_scan_kernel(GretArgs a) {
+  __shared__ bf16 tr[32][33];
   const int bh = blockIdx.y;
-  const int DD = a.d * a.d;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= DD) return;
-  float R = a.state_in ? a.state_in[(size_t)bh * DD + e] : 0.f;
-  for (int c = 0; c < a.nc; ++c) {
-    static_cast<bf16*>(a.rin)[((size_t)bh * a.nc + c) * DD + e] = (bf16)R;
-    R = a.lam[(size_t)bh * a.nc + c] * R + a.dR[((size_t)bh * a.nc + c) * DD + e];
+  const int nb = a.d / 32;
+  const int dk0 = (blockIdx.x / nb) * 32, dv0 = (blockIdx.x % nb) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // ty = 0..7
+  const size_t DD = (size_t)a.d * a.d;
+  float R[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t e = (size_t)(dk0 + ty + 8 * u) * a.d + dv0 + tx;
+    R[u] = a.state_in ? a.state_in[bh * DD + e] : 0.f;
   }
-  if (a.state_out) a.state_out[(size_t)bh * DD + e] = R;
+  bf16* rinT = static_cast<bf16*>(a.rin);
+  // this thread's dR elements of chunk c, loaded one chunk ahead
+  auto load_dR = [&](int c, float* x) {
+    const float* dR = a.dR + ((size_t)bh * a.nc + c) * DD;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = dR[(size_t)(dk0 + ty + 8 * u) * a.d + dv0 + tx];
+  };
+  float dcur[4], dnext[4];
+  load_dR(0, dcur);
+  for (int c = 0; c < a.nc; ++c) {
+    if (c + 1 < a.nc) load_dR(c + 1, dnext);
+    const float lam = a.lam[(size_t)bh * a.nc + c];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tr[ty + 8 * u][tx] = (bf16)R[u];   // tr[dk][dv]
+    __syncthreads();
+    bf16* dst = rinT + ((size_t)bh * a.nc + c) * DD;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[(size_t)(dv0 + ty + 8 * u) * a.d + dk0 + tx] = tr[tx][ty + 8 * u];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      R[u] = fmaf(lam, R[u], dcur[u]);
+      dcur[u] = dnext[u];
+    }
+  }
+  if (a.state_out) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a.state_out[bh * DD + (size_t)(dk0 + ty + 8 * u) * a.d + dv0 + tx] = R[u];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 4. outputs of 128 query rows of one chunk
+// 4. outputs of 128 query rows of one chunk; K/V tiles (and the keys' log2
+//    decays) are staged global -> LDS directly and double-buffered
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
   using C = GretCfg<D>;
-  __shared__ __attribute__((aligned(16))) char kt[C::TILE], vt[C::TILE], rt[D * D * 2];
-  __shared__ float lgt[C::BK];
+  constexpr int PER_T = C::BK * C::CH / 256;    // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) char kt0[C::TILE], vt0[C::TILE], kt1[C::TILE], vt1[C::TILE];
+  __shared__ __attribute__((aligned(16))) float lg0[C::BK], lg1[C::BK];
   const int nrb = a.chunk / 128;
   const int c = blockIdx.x / nrb, rb = blockIdx.x % nrb, bh = blockIdx.y;
   const int tid = threadIdx.x, l = tid & 63, g = l >> 5, r32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c0 = c * a.chunk, clen = min(a.chunk, a.N - c0);
+  const int c0 = c * a.chunk;
   const int q0 = c0 + rb * 128;                 // first query row of the workgroup
   if (q0 >= a.N) return;                        // whole workgroup past the end (uniform)
   const int wq0 = q0 + 32 * w;                  // first row of this wave
@@ -180,6 +220,43 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
   const bool row_ok = n < a.N;
   const bool wave_live = wq0 < a.N;
   const size_t hrow = (size_t)bh * a.N;
+  const int k_end = min(q0 + 127, a.N - 1);     // last key any row here can see
+  const int pw1 = min(wq0 + 31, a.N - 1);       // last row of this wave
+  const int ntiles = (k_end - c0) / C::BK + 1;
+
+  // ---- tile staging by DMA: slot P = 256 r + tid of a tile holds row P / CH
+  // at physical chunk P % CH; rows past k_end re-read row k_end (finite data,
+  // always masked: their keys lie after every row of the workgroup)
+  const char* kbase = static_cast<const char*>(a.k) + hrow * D * 2;
+  const char* vbase = static_cast<const char*>(a.v) + hrow * D * 2;
+  unsigned koff[PER_T], voff[PER_T];
+  int srow[PER_T];
+#pragma unroll
+  for (int r = 0; r < PER_T; ++r) {
+    const int slot = 256 * r + 64 * w + l;
+    const int row = slot / C::CH, pch = slot % C::CH;
+    srow[r] = row;
+    koff[r] = (unsigned)(row * D * 2 + ((pch ^ swz_k<C::CH>(row)) << 4));
+    voff[r] = (unsigned)(row * D * 2 + ((pch ^ swz_v<C::CH>(row)) << 4));
+  }
+  auto load_tile = [&](int t, char* kd, char* vd, float* lgd) {
+    const int k0 = c0 + t * C::BK;
+#pragma unroll
+    for (int r = 0; r < PER_T; ++r) {
+      const int over = k0 + srow[r] - k_end;
+      const unsigned back = over > 0 ? (unsigned)(over * D * 2) : 0u;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(kbase + (size_t)k0 * D * 2 + koff[r] - back),
+                                       (__attribute__((address_space(3))) void*)(kd + (256 * r + 64 * w) * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vbase + (size_t)k0 * D * 2 + voff[r] - back),
+                                       (__attribute__((address_space(3))) void*)(vd + (256 * r + 64 * w) * 16), 16, 0, 0);
+    }
+    if (w == 0) {
+      const int key = min(k0 + l, k_end);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(a.lg2 + hrow + key),
+                                       (__attribute__((address_space(3))) void*)lgd, 4, 0, 0);
+    }
+  };
+  load_tile(0, kt0, vt0, lg0);
 
   // query fragments (as for attention: row n, dims 16c + 8g + j)
   bf16x8 qf[C::NC];
@@ -191,72 +268,70 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
   }
   const float l_n = row_ok ? a.lg2[hrow + n] : 0.f;
 
-  // cross-chunk term: O^T = R^T Q^T, then column n scaled by 2^{L_n}
-  const bf16* rsrc = static_cast<const bf16*>(a.rin) + ((size_t)bh * a.nc + c) * D * D;
-  stage_rows_v<D>(rt, rsrc, 0, D, [](int) { return 1.f; }, false);
-  if constexpr (D > 64) stage_rows_v<D>(rt + 64 * D * 2, rsrc, 64, 64, [](int) { return 1.f; }, false);
-  __syncthreads();
+  // cross-chunk term O^T = R^T Q^T (R^T fragments straight from L2), then
+  // column n scaled by 2^{L_n}
   f32x16 acc[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    acc[db] = f32x16{};
-#pragma unroll
-    for (int cc = 0; cc < C::NC; ++cc) acc[db] = mma32(lds_frag_vt<bf16, C::CH>(rt, cc, db, l), qf[cc], acc[db]);
-  }
   {
+    const bf16* rT = static_cast<const bf16*>(a.rin) + ((size_t)bh * a.nc + c) * D * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const bf16* rrow = rT + (size_t)(db * 32 + r32) * D + 8 * g;
+      bf16x8 rf[C::NC];
+#pragma unroll
+      for (int cc = 0; cc < C::NC; ++cc) rf[cc] = *reinterpret_cast<const bf16x8*>(rrow + 16 * cc);
+      acc[db] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < C::NC; ++cc) acc[db] = mma32(rf[cc], qf[cc], acc[db]);
+    }
     const float f = __builtin_amdgcn_exp2f(l_n);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) acc[db] *= f;
   }
 
-  // inner-chunk term over key tiles [c0, last row of the workgroup]
-  const int k_end = min(q0 + 127, a.N - 1);     // last key any row here can see
-  const int pw1 = min(wq0 + 31, a.N - 1);       // last row of this wave
-  const bf16* kbase = static_cast<const bf16*>(a.k) + hrow * D;
-  const bf16* vbase = static_cast<const bf16*>(a.v) + hrow * D;
-  for (int k0 = c0; k0 <= k_end; k0 += C::BK) {
-    const int rows = min(C::BK, min(c0 + clen, k_end + 1) - k0);
-    __syncthreads();   // the previous tile (or R) is no longer read
-    // K tile with the K swizzle (read as the A operand in row order sigma)
-    for (int slot = tid; slot < C::BK * C::CH; slot += 256) {
-      const int row = slot / C::CH, pch = slot % C::CH;
-      const int lch = pch ^ swz_k<C::CH>(row);
-      u32x4 v4{0, 0, 0, 0};
-      if (row < rows) v4 = *reinterpret_cast<const u32x4*>(kbase + (size_t)(k0 + row) * D + lch * 8);
-      *reinterpret_cast<u32x4*>(kt + row * C::CH * 16 + pch * 16) = v4;
-    }
-    stage_rows_v<D>(vt, vbase + (size_t)k0 * D, 0, rows, [](int) { return 1.f; }, false);
-    if (tid < C::BK) lgt[tid] = tid < rows ? a.lg2[hrow + k0 + tid] : 0.f;
-    __syncthreads();
-    if (!wave_live || k0 > pw1) continue;       // every key of the tile is after this wave's rows
-
-    // S^T = K Q^T; element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8g + i%8
-    f32x16 s[2];
+  // one key tile: compute from (kt, vt, lgt) while tile t+1 streams into the other set
+  auto tile_step = [&](int t, const char* kt, const char* vt, const float* lgt, char* kn, char* vn, float* lgn)
+      __attribute__((always_inline)) {
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) load_tile(t + 1, kn, vn, lgn);
+    const int k0 = c0 + t * C::BK;
+    if (wave_live && k0 <= pw1) {
+      // S^T = K Q^T; element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8g + i%8
+      f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int krow = kb * 32 + sigma(r32);
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const int krow = kb * 32 + sigma(r32);
 #pragma unroll
-      for (int cc = 0; cc < C::NC; ++cc) s[kb] = mma32(lds_frag_k<bf16, C::CH>(kt, krow, cc, g), qf[cc], s[kb]);
-    }
-    // decay weights, masked by m <= n (a select: 2^{L_n - L_m} may overflow above the diagonal)
-    bf16x8 pf[4];
+        for (int cc = 0; cc < C::NC; ++cc) s[kb] = mma32(lds_frag_k<bf16, C::CH>(kt, krow, cc, g), qf[cc], s[kb]);
+      }
+      // decay weights, masked by m <= n (a select: 2^{L_n - L_m} may
+      // overflow above the diagonal)
+      bf16x8 pf[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-        const float wgt = s[kb][i] * __builtin_amdgcn_exp2f(l_n - lgt[off]);
-        const float p = (k0 + off <= n) ? wgt : 0.f;
-        pf[2 * kb + (i >> 3)][i & 7] = (bf16)p;
+        for (int i = 0; i < 16; ++i) {
+          const int off = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
+          const float wgt = s[kb][i] * __builtin_amdgcn_exp2f(l_n - lgt[off]);
+          pf[2 * kb + (i >> 3)][i & 7] = (bf16)((k0 + off <= n) ? wgt : 0.f);
+        }
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) acc[db] = mma32(lds_frag_vt<bf16, C::CH>(vt, cc, db, l), pf[cc], acc[db]);
       }
     }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) acc[db] = mma32(lds_frag_vt<bf16, C::CH>(vt, cc, db, l), pf[cc], acc[db]);
-    }
+    if (has_next) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, kt0, vt0, lg0, kt1, vt1, lg1);
+    if (t + 1 < ntiles) tile_step(t + 1, kt1, vt1, lg1, kt0, vt0, lg0);
   }
 
   if (row_ok) {
@@ -275,28 +350,38 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// recurrent step: S <- gamma S + k^T v; o = q S   (state float32 [dk][dv])
+// recurrent step: S <- gamma S + k^T v; o = q S   (state float32 [dk][dv]).
+// A workgroup serves 64 dv columns of one head; its 4 waves take a quarter of
+// the dk rows each and meet in LDS for o.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(64) void gret_decode_kernel(GretDecodeArgs a) {
-  const int bh = blockIdx.y;
-  const int j = blockIdx.x * 64 + threadIdx.x;   // this lane's dv column
-  const T* q = static_cast<const T*>(a.q) + (size_t)bh * a.d;
-  const T* k = static_cast<const T*>(a.k) + (size_t)bh * a.d;
-  const T* v = static_cast<const T*>(a.v) + (size_t)bh * a.d;
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gret_decode_kernel(GretDecodeArgs a) {
+  __shared__ float red[4][64];
+  constexpr int RPW = D / 4;                      // rows per wave
+  const int bh = blockIdx.y, l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = blockIdx.x * 64 + l;              // this lane's dv column
+  const T* q = static_cast<const T*>(a.q) + (size_t)bh * D;
+  const T* k = static_cast<const T*>(a.k) + (size_t)bh * D;
+  const T* v = static_cast<const T*>(a.v) + (size_t)bh * D;
   const float gam = __builtin_amdgcn_exp2f(gate_log2(a.gate[bh], a.inv_tau));
   const float vj = to_f32(v[j]);
-  float* S = a.state + (size_t)bh * a.d * a.d + j;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < a.d; i += 4) {
+  float* S = a.state + (size_t)bh * D * D + (size_t)(w * RPW) * D + j;
+  float sv[RPW];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float sn = fmaf(gam, S[(size_t)(i + u) * a.d], to_f32(k[i + u]) * vj);
-      S[(size_t)(i + u) * a.d] = sn;
-      acc[u] = fmaf(to_f32(q[i + u]), sn, acc[u]);
-    }
+  for (int i = 0; i < RPW; ++i) sv[i] = S[(size_t)i * D];
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = w * RPW + i;
+    const float sn = fmaf(gam, sv[i], to_f32(k[row]) * vj);
+    S[(size_t)i * D] = sn;
+    acc[i & 3] = fmaf(to_f32(q[row]), sn, acc[i & 3]);
   }
-  static_cast<T*>(a.o)[(size_t)bh * a.d + j] = from_f32<T>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  red[w][l] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (w == 0)
+    static_cast<T*>(a.o)[(size_t)bh * D + j] = from_f32<T>((red[0][l] + red[1][l]) + (red[2][l] + red[3][l]));
 }
 
 // ---------------------------------------------------------------------------
@@ -341,20 +426,26 @@ __global__ __launch_bounds__(256) void gret_norm_kernel(GretNormArgs a) {
 
 // ---------------------------------------------------------------------------
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(gret_gate_kernel, dim3(a.nc, a.B * a.H), dim3(256), 0, stream, a);
+  const dim3 heads(a.B * a.H);
   if (a.d == 128) hipLaunchKernelGGL(gret_state_kernel<128>, dim3(a.nc, a.B * a.H), dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(gret_state_kernel<64>, dim3(a.nc, a.B * a.H), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(gret_scan_kernel, dim3((a.d * a.d + 255) / 256, a.B * a.H), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(gret_scan_kernel, dim3((a.d / 32) * (a.d / 32), a.B * a.H), dim3(256), 0, stream, a);
   const int nblk = a.nc * (a.chunk / 128);
   if (a.d == 128) hipLaunchKernelGGL(gret_out_kernel<128>, dim3(nblk, a.B * a.H), dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(gret_out_kernel<64>, dim3(nblk, a.B * a.H), dim3(256), 0, stream, a);
+  (void)heads;
   return hipGetLastError();
 }
 
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool is_bf16, hipStream_t stream) {
   const dim3 grid(a.d / 64, a.B * a.H);
-  if (is_bf16) hipLaunchKernelGGL(gret_decode_kernel<bf16>, grid, dim3(64), 0, stream, a);
-  else hipLaunchKernelGGL(gret_decode_kernel<float>, grid, dim3(64), 0, stream, a);
+  if (a.d == 128) {
+    if (is_bf16) hipLaunchKernelGGL((gret_decode_kernel<bf16, 128>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((gret_decode_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((gret_decode_kernel<bf16, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((gret_decode_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

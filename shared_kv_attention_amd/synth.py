@@ -57,6 +57,10 @@ WORKLOADS = {
     # (hidden = 32 heads x 128), 16 cross-decoder layers over 32768 rows
     "generation_32k_bf16": Workload(6, "generation_32k_bf16", "bf16", 16, 32768, 4096, 32, 8, 128,
                                     16, 16, 1024, 0.02, decode_steps=16),
+    # gated-retention self-decoder layer at the 3B shape (24 heads of 128,
+    # chunk 256), and its recurrent decode step for 16 sequences
+    "gret_3b_bf16": Workload(7, "gret_3b_bf16", "bf16", 1, 4096, 3072, 24, 24, 128,
+                             8, 0, 0, 0.0, decode_steps=64),
 }
 
 
