@@ -13,18 +13,21 @@
 // Design (MI355X-first): instead of one workgroup walking a head's chunks in
 // order (only B*H workgroups), the prefill runs three launches that are each
 // parallel over chunks:
-//  1. state:  per chunk, the log2 decay prefix sums and the chunk's total
-//             decay, then dR = K^T (V scaled by e^{L_last - L_m}) on the
-//             matrix cores (both operands read transposed from LDS);
+//  1. state:  per chunk (8 waves), the log2 decay prefix sums and the
+//             chunk's total decay, then dR^T = (V scaled by e^{L_last - L_m})^T K
+//             on the matrix cores (both operands read transposed from LDS),
+//             stored [dv][dk];
 //  2. scan:   per (head, 32 x 32 block of the state), R_c = e^{L_last}
-//             R_{c-1} + dR_c in float32, storing the state entering every
-//             chunk transposed (through LDS) in the operand layout of 3;
-//  3. output: per (chunk, 128 query rows), an attention-like tile loop with
+//             R_{c-1} + dR_c in float32 with the chunks' dR loaded in
+//             groups ahead of use, storing the state entering every chunk
+//             as bf16 R^T [dv][dk], the operand layout of 3;
+//  3. output: per (chunk, 128 query rows), the cross-chunk term R^T Q^T
+//             (R^T staged in LDS), then an attention-like tile loop with
 //             decay weights e^{L_n - L_m} (formed per pair from the
 //             difference, so a strong gate can never overflow) instead of a
 //             softmax, with direct global -> LDS double-buffered K/V tiles,
-//             and the cross-chunk term R^T Q^T (fragments from L2) on the
-//             same accumulator.
+//             on the same accumulator.  The heavier second halves of the
+//             chunks (four key tiles instead of two) are dispatched first.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_lds.hpp"
@@ -48,11 +51,11 @@ __device__ __forceinline__ float gate_log2(float z, float inv_tau) {
 
 // ---------------------------------------------------------------------------
 // 1+2. per chunk: log2-decay prefix sums (written out for the output kernel)
-//      and the state contribution dR[dk][dv] = sum_m K[m][dk] V[m][dv] w_m,
-//      w_m = 2^{L_last - L_m}
+//      and the state contribution, stored transposed:
+//      dR^T[dv][dk] = sum_m V[m][dv] w_m K[m][dk],  w_m = 2^{L_last - L_m}
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
+__global__ __launch_bounds__(512) void gret_state_kernel(GretArgs a) {
   using C = GretCfg<D>;
   __shared__ __attribute__((aligned(16))) char kt[C::TILE], vt[C::TILE];
   __shared__ float lgc[256];
@@ -62,14 +65,15 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
 
   // inclusive prefix sum of the chunk's log2 decays (positions past the end add 0)
   {
+    const bool scan_t = t < 256;
     float x = t < clen ? gate_log2(a.gate[(size_t)bh * a.N + c0 + t], a.inv_tau) : 0.f;
-    lgc[t] = x;
+    if (scan_t) lgc[t] = x;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
-      const float y = t >= off ? lgc[t - off] : 0.f;
+      const float y = scan_t && t >= off ? lgc[t - off] : 0.f;
       __syncthreads();
       x += y;
-      lgc[t] = x;
+      if (scan_t) lgc[t] = x;
       __syncthreads();
     }
     if (t < clen) a.lg2[(size_t)bh * a.N + c0 + t] = x;
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
 
   const bf16* kb = static_cast<const bf16*>(a.k) + ((size_t)bh * a.N + c0) * D;
   const bf16* vb = static_cast<const bf16*>(a.v) + ((size_t)bh * a.N + c0) * D;
-  constexpr int TILES = C::NDB * C::NDB, TPW = TILES / 4 > 0 ? TILES / 4 : 1;
+  constexpr int TILES = C::NDB * C::NDB, TPW = TILES / 8 > 0 ? TILES / 8 : 1;
   f32x16 acc[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
@@ -87,13 +91,13 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
 
   // Each thread owns the same PER_T chunk slots of every tile; the raw chunks
   // of tile r0 + BK are loaded into registers while tile r0 is multiplied.
-  constexpr int PER_T = C::BK * C::CH / 256;
+  constexpr int PER_T = C::BK * C::CH / 512;
   u32x4 kraw[PER_T], vraw[PER_T];
   auto fetch = [&](int r0) {
     const int rows = min(C::BK, clen - r0);
 #pragma unroll
     for (int r = 0; r < PER_T; ++r) {
-      const int slot = 256 * r + t, row = slot / C::CH, pch = slot % C::CH;
+      const int slot = 512 * r + t, row = slot / C::CH, pch = slot % C::CH;
       const int lch = pch ^ swz_v<C::CH>(row);
       const size_t off = (size_t)(r0 + min(row, rows - 1)) * D + lch * 8;
       kraw[r] = *reinterpret_cast<const u32x4*>(kb + off);
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
     const int rows = min(C::BK, clen - r0);
 #pragma unroll
     for (int r = 0; r < PER_T; ++r) {
-      const int slot = 256 * r + t, row = slot / C::CH;
+      const int slot = 512 * r + t, row = slot / C::CH;
       u32x4 kw{0, 0, 0, 0}, vw{0, 0, 0, 0};
       if (row < rows) {
         kw = kraw[r];
@@ -129,7 +133,7 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
         const int tt = w * TPW + i, dkb = tt / C::NDB, dvb = tt % C::NDB;
 #pragma unroll
         for (int s = 0; s < C::BK / 16; ++s)
-          acc[i] = mma32(lds_frag_vt<bf16, C::CH>(kt, s, dkb, l), lds_frag_vt<bf16, C::CH>(vt, s, dvb, l), acc[i]);
+          acc[i] = mma32(lds_frag_vt<bf16, C::CH>(vt, s, dvb, l), lds_frag_vt<bf16, C::CH>(kt, s, dkb, l), acc[i]);
       }
     }
     __syncthreads();
@@ -142,8 +146,8 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
       const int tt = w * TPW + i, dkb = tt / C::NDB, dvb = tt % C::NDB;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int dk = dkb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        dst[dk * D + dvb * 32 + (l & 31)] = acc[i][e];
+        const int dv = dvb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+        dst[dv * D + dkb * 32 + (l & 31)] = acc[i][e];
       }
     }
   }
@@ -151,50 +155,57 @@ __global__ __launch_bounds__(256) void gret_state_kernel(GretArgs a) {
 
 // ---------------------------------------------------------------------------
 // 3. scan over chunks on 32 x 32 blocks of the state: R_c = lam_c R_{c-1} + dR_c
-//    in float32; the state entering chunk c is stored transposed in bf16
-//    (rinT[c][dv][dk], the operand layout of the output kernel's R^T Q^T)
+//    in float32, all in the transposed [dv][dk] layout (lanes along dk); the
+//    state entering chunk c is stored in bf16 (rinT[c][dv][dk], the operand
+//    layout of the output kernel's R^T Q^T).  No barriers: the loads of the
+//    next group of chunks stay in flight while the current one is summed.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gret_scan_kernel(GretArgs a) {
-  __shared__ bf16 tr[32][33];
+  constexpr int PF = 4;                      // chunks per prefetch group
   const int bh = blockIdx.y;
   const int nb = a.d / 32;
-  const int dk0 = (blockIdx.x / nb) * 32, dv0 = (blockIdx.x % nb) * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // ty = 0..7
+  const int dv0 = (blockIdx.x / nb) * 32, dk0 = (blockIdx.x % nb) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // dk0 + tx, dv0 + ty + 8u
   const size_t DD = (size_t)a.d * a.d;
   float R[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const size_t e = (size_t)(dk0 + ty + 8 * u) * a.d + dv0 + tx;
-    R[u] = a.state_in ? a.state_in[bh * DD + e] : 0.f;
-  }
-  bf16* rinT = static_cast<bf16*>(a.rin);
-  // this thread's dR elements of chunk c, loaded one chunk ahead
-  auto load_dR = [&](int c, float* x) {
-    const float* dR = a.dR + ((size_t)bh * a.nc + c) * DD;
+  for (int u = 0; u < 4; ++u)   // the state is [dk][dv] at the interface
+    R[u] = a.state_in ? a.state_in[bh * DD + (size_t)(dk0 + tx) * a.d + dv0 + ty + 8 * u] : 0.f;
+  const float* dRb = a.dR + (size_t)bh * a.nc * DD;
+  bf16* rinb = static_cast<bf16*>(a.rin) + (size_t)bh * a.nc * DD;
+  const float* lamb = a.lam + (size_t)bh * a.nc;
+  auto load = [&](int cb, float (&x)[PF][4]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = dR[(size_t)(dk0 + ty + 8 * u) * a.d + dv0 + tx];
+    for (int j = 0; j < PF; ++j)
+      if (cb + j < a.nc)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[j][u] = dRb[(size_t)(cb + j) * DD + (size_t)(dv0 + ty + 8 * u) * a.d + dk0 + tx];
   };
-  float dcur[4], dnext[4];
-  load_dR(0, dcur);
-  for (int c = 0; c < a.nc; ++c) {
-    if (c + 1 < a.nc) load_dR(c + 1, dnext);
-    const float lam = a.lam[(size_t)bh * a.nc + c];
+  auto step = [&](int cb, const float (&x)[PF][4]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) tr[ty + 8 * u][tx] = (bf16)R[u];   // tr[dk][dv]
-    __syncthreads();
-    bf16* dst = rinT + ((size_t)bh * a.nc + c) * DD;
+    for (int j = 0; j < PF; ++j) {
+      const int c = cb + j;
+      if (c < a.nc) {
+        const float lam = lamb[c];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dst[(size_t)(dv0 + ty + 8 * u) * a.d + dk0 + tx] = tr[tx][ty + 8 * u];
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      R[u] = fmaf(lam, R[u], dcur[u]);
-      dcur[u] = dnext[u];
+        for (int u = 0; u < 4; ++u) {
+          rinb[(size_t)c * DD + (size_t)(dv0 + ty + 8 * u) * a.d + dk0 + tx] = (bf16)R[u];
+          R[u] = fmaf(lam, R[u], x[j][u]);
+        }
+      }
     }
+  };
+  float xa[PF][4], xb[PF][4];
+  load(0, xa);
+  for (int cb = 0; cb < a.nc; cb += 2 * PF) {
+    load(cb + PF, xb);
+    step(cb, xa);
+    load(cb + 2 * PF, xa);
+    step(cb + PF, xb);
   }
   if (a.state_out) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a.state_out[bh * DD + (size_t)(dk0 + ty + 8 * u) * a.d + dv0 + tx] = R[u];
+    for (int u = 0; u < 4; ++u) a.state_out[bh * DD + (size_t)(dk0 + tx) * a.d + dv0 + ty + 8 * u] = R[u];
   }
 }
 
@@ -206,10 +217,18 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
   using C = GretCfg<D>;
   constexpr int PER_T = C::BK * C::CH / 256;    // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) char kt0[C::TILE], vt0[C::TILE], kt1[C::TILE], vt1[C::TILE];
+  __shared__ __attribute__((aligned(16))) char tiles[4 * C::TILE];
+  char* const kt0 = tiles;
+  char* const vt0 = tiles + C::TILE;
+  char* const kt1 = tiles + 2 * C::TILE;
+  char* const vt1 = tiles + 3 * C::TILE;
   __shared__ __attribute__((aligned(16))) float lg0[C::BK], lg1[C::BK];
   const int nrb = a.chunk / 128;
-  const int c = blockIdx.x / nrb, rb = blockIdx.x % nrb, bh = blockIdx.y;
+  // linear block index -> (row block, descending: the later rows see more keys; head; chunk)
+  const int nblk_bh = a.nc * a.B * a.H;
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int rb = nrb - 1 - lin / nblk_bh, rem = lin % nblk_bh;
+  const int bh = rem / a.nc, c = rem % a.nc;
   const int tid = threadIdx.x, l = tid & 63, g = l >> 5, r32 = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = c * a.chunk;
@@ -257,6 +276,17 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
     }
   };
   load_tile(0, kt0, vt0, lg0);
+  // R^T of the chunk (D rows) into the second buffer set, K-tile layout
+  {
+    const char* rbase = static_cast<const char*>(a.rin) + ((size_t)bh * a.nc + c) * D * D * 2;
+#pragma unroll
+    for (int h = 0; h < D / C::BK; ++h)
+#pragma unroll
+      for (int r = 0; r < PER_T; ++r)
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(rbase + h * C::TILE + koff[r]),
+                                         (__attribute__((address_space(3))) void*)(kt1 + h * C::TILE + (256 * r + 64 * w) * 16),
+                                         16, 0, 0);
+  }
 
   // query fragments (as for attention: row n, dims 16c + 8g + j)
   bf16x8 qf[C::NC];
@@ -268,17 +298,17 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
   }
   const float l_n = row_ok ? a.lg2[hrow + n] : 0.f;
 
-  // cross-chunk term O^T = R^T Q^T (R^T fragments straight from L2), then
-  // column n scaled by 2^{L_n}
+  // cross-chunk term O^T = R^T Q^T (R^T from LDS), then column n scaled by 2^{L_n}
   f32x16 acc[C::NDB];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   {
-    const bf16* rT = static_cast<const bf16*>(a.rin) + ((size_t)bh * a.nc + c) * D * D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16* rrow = rT + (size_t)(db * 32 + r32) * D + 8 * g;
+      const char* rt = kt1 + (db >> 1) * C::TILE;
       bf16x8 rf[C::NC];
 #pragma unroll
-      for (int cc = 0; cc < C::NC; ++cc) rf[cc] = *reinterpret_cast<const bf16x8*>(rrow + 16 * cc);
+      for (int cc = 0; cc < C::NC; ++cc) rf[cc] = lds_frag_k<bf16, C::CH>(rt, (db & 1) * 32 + r32, cc, g);
       acc[db] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < C::NC; ++cc) acc[db] = mma32(rf[cc], qf[cc], acc[db]);
@@ -327,8 +357,7 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
     __syncthreads();
   };
 
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  __syncthreads();   // R^T reads done before tile 1 overwrites it
   for (int t = 0; t < ntiles; t += 2) {
     tile_step(t, kt0, vt0, lg0, kt1, vt1, lg1);
     if (t + 1 < ntiles) tile_step(t + 1, kt1, vt1, lg1, kt0, vt0, lg0);
@@ -427,8 +456,8 @@ __global__ __launch_bounds__(256) void gret_norm_kernel(GretNormArgs a) {
 // ---------------------------------------------------------------------------
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t stream) {
   const dim3 heads(a.B * a.H);
-  if (a.d == 128) hipLaunchKernelGGL(gret_state_kernel<128>, dim3(a.nc, a.B * a.H), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(gret_state_kernel<64>, dim3(a.nc, a.B * a.H), dim3(256), 0, stream, a);
+  if (a.d == 128) hipLaunchKernelGGL(gret_state_kernel<128>, dim3(a.nc, a.B * a.H), dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL(gret_state_kernel<64>, dim3(a.nc, a.B * a.H), dim3(512), 0, stream, a);
   hipLaunchKernelGGL(gret_scan_kernel, dim3((a.d / 32) * (a.d / 32), a.B * a.H), dim3(256), 0, stream, a);
   const int nblk = a.nc * (a.chunk / 128);
   if (a.d == 128) hipLaunchKernelGGL(gret_out_kernel<128>, dim3(nblk, a.B * a.H), dim3(256), 0, stream, a);
