@@ -21,11 +21,18 @@ What the method computes:
   cross-decoder layer reads the whole global cache ([P seg. 4], [P seg. 26];
   [S §2], [S §3]).  Causality makes token-by-token generation reproduce the
   rows of a full forward over the same sequence.
-Readings taken: each attention keeps an output projection W_o; the SwiGLU
-feed-forward and the final norm are left out (position-wise, no sizes on the
-pages, and they cannot affect causality, sharing or early exit); the
-cross-decoder's residual stream continues from the self-decoder output, the
-same tensor the global K/V are projected from.
+* A self-decoder layer follows its attention with a SwiGLU feed-forward
+  ([P seg. 12]).
+Readings taken: each attention keeps an output projection W_o; layers are
+pre-norm residual, x + attention(norm x) then x + SwiGLU(norm x); the
+cross-decoder layers carry the same feed-forward (the pages describe only
+their attention); the feed-forward is optional here (BlockParams.swa_ffn /
+cross_ffn; absent in the smallest pins) and, when present, is SwiGLU(n) =
+W_down (silu(W_gate n) * (W_up n)) with silu(z) = z * sigmoid(z), its sizes
+chosen by the caller (the pages give none); the final norm before the output head is left out (the
+head is not part of the path); the cross-decoder's residual stream continues
+from the self-decoder output, the same tensor the global K/V are projected
+from.
 
 Position-wise products are computed row by row with one routine (a
 matrix-vector product), so that a row's value is bitwise the same whether or
@@ -43,7 +50,8 @@ import numpy as np
 from .attention import attend_row, cross_prefill_attention, ring_window, swa_attention
 from .projection import global_kv_proj, rmsnorm_row
 
-__all__ = ["BlockParams", "linear_rows", "yoco_block", "yoco_block_early_exit", "yoco_block_generate"]
+__all__ = ["BlockParams", "linear_rows", "silu", "swiglu_ffn_row", "yoco_block", "yoco_block_early_exit",
+           "yoco_block_generate"]
 
 
 @dataclass
@@ -61,7 +69,38 @@ class BlockParams:
     glob_wv: np.ndarray = None                               # [Hkv*d, D]
     cross_wq: List[np.ndarray] = field(default_factory=list)  # [Hq*d, D]
     cross_wo: List[np.ndarray] = field(default_factory=list)  # [D, Hq*d]
+    # optional SwiGLU feed-forward per layer: (w_gate [F, D], w_up [F, D], w_down [D, F])
+    swa_ffn: List[tuple] = field(default_factory=list)
+    cross_ffn: List[tuple] = field(default_factory=list)
     eps: float = 1e-6
+
+    def ffn(self, kind, layer):
+        lst = self.swa_ffn if kind == "swa" else self.cross_ffn
+        return lst[layer] if lst else None
+
+
+def silu(z):
+    """z * sigmoid(z), written so that no exponential overflows."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, z / (1.0 + e), z * e / (1.0 + e))
+
+
+def swiglu_ffn_row(x_row, ffn, eps):
+    """x + W_down (silu(W_gate n) * (W_up n)), n = rmsnorm(x), for one row."""
+    wg, wu, wd = ffn
+    n = rmsnorm_row(x_row, None, eps)
+    return x_row + wd @ (silu(wg @ n) * (wu @ n))
+
+
+def _ffn_rows(x, ffn, eps):
+    if ffn is None:
+        return x
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty_like(flat)
+    for r in range(flat.shape[0]):
+        out[r] = swiglu_ffn_row(flat[r], ffn, eps)
+    return out.reshape(x.shape)
 
 
 def linear_rows(x, w):
@@ -98,13 +137,14 @@ def _merge(t):
 def _self_decoder_and_projection(x, p):
     Hq, Hkv, d = p.n_heads, p.n_kv_heads, p.head_dim
     x = np.array(x, dtype=np.float64)
-    for wq, wk, wv, wo in zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo):
+    for layer, (wq, wk, wv, wo) in enumerate(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo)):
         n = _norm_rows(x, p.eps)
         q = _heads(linear_rows(n, wq), Hq, d)
         k = _heads(linear_rows(n, wk), Hkv, d)
         v = _heads(linear_rows(n, wv), Hkv, d)
         o, _ = swa_attention(q, k, v, p.window)
         x = x + linear_rows(_merge(o), wo)
+        x = _ffn_rows(x, p.ffn("swa", layer), p.eps)
     k_glob, v_glob = global_kv_proj(x, p.glob_wk, p.glob_wv, Hkv, d, eps=p.eps)
     return x, k_glob, v_glob
 
@@ -116,12 +156,13 @@ def yoco_block(x, p):
     """
     Hq, d = p.n_heads, p.head_dim
     x, k_glob, v_glob = _self_decoder_and_projection(x, p)
-    for wq, wo in zip(p.cross_wq, p.cross_wo):
+    for layer, (wq, wo) in enumerate(zip(p.cross_wq, p.cross_wo)):
         n = _norm_rows(x, p.eps)
         q = _heads(linear_rows(n, wq), Hq, d)
         # every cross layer reads the same k_glob / v_glob objects
         o, _ = cross_prefill_attention(q, k_glob, v_glob)
         x = x + linear_rows(_merge(o), wo)
+        x = _ffn_rows(x, p.ffn("cross", layer), p.eps)
     return x, (k_glob, v_glob)
 
 
@@ -136,7 +177,8 @@ def yoco_block_early_exit(x, p):
     g = Hq // Hkv
     scale = 1.0 / math.sqrt(d)
     last = x[:, N - 1, :].copy()
-    for wq, wo in zip(p.cross_wq, p.cross_wo):
+    for layer, (wq, wo) in enumerate(zip(p.cross_wq, p.cross_wo)):
+        ffn = p.ffn("cross", layer)
         new = np.empty_like(last)
         for b in range(B):
             n = rmsnorm_row(last[b], None, p.eps)
@@ -146,6 +188,8 @@ def yoco_block_early_exit(x, p):
                 o[h], _, _ = attend_row(q[h], k_glob[b, h // g, :N],
                                         v_glob[b, h // g, :N], scale)
             new[b] = last[b] + wo @ o.reshape(Hq * d)
+            if ffn is not None:
+                new[b] = swiglu_ffn_row(new[b], ffn, p.eps)
         last = new
     return last, (k_glob, v_glob)
 
@@ -174,7 +218,9 @@ def yoco_block_generate(x, p):
     for t in range(N):
         slots = [s for _, s in ring_window(t, W)]
         h_t = x[:, t, :].copy()
-        for (wq, wk, wv, wo), (kr, vr) in zip(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo), rings):
+        for layer, ((wq, wk, wv, wo), (kr, vr)) in enumerate(zip(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo),
+                                                                 rings)):
+            ffn = p.ffn("swa", layer)
             new = np.empty_like(h_t)
             for b in range(B):
                 n = rmsnorm_row(h_t[b], None, p.eps)
@@ -185,12 +231,15 @@ def yoco_block_generate(x, p):
                 for h in range(Hq):
                     o[h], _, _ = attend_row(q[h], kr[b, h // g, slots], vr[b, h // g, slots], scale)
                 new[b] = h_t[b] + wo @ o.reshape(Hq * d)
+                if ffn is not None:
+                    new[b] = swiglu_ffn_row(new[b], ffn, p.eps)
             h_t = new
         for b in range(B):
             k_row, v_row = global_kv_proj(h_t[b][None, None, :], p.glob_wk, p.glob_wv, Hkv, d, eps=p.eps)
             k_glob[b, :, t] = k_row[0, :, 0]
             v_glob[b, :, t] = v_row[0, :, 0]
-        for wq, wo in zip(p.cross_wq, p.cross_wo):
+        for layer, (wq, wo) in enumerate(zip(p.cross_wq, p.cross_wo)):
+            ffn = p.ffn("cross", layer)
             new = np.empty_like(h_t)
             for b in range(B):
                 n = rmsnorm_row(h_t[b], None, p.eps)
@@ -199,6 +248,8 @@ def yoco_block_generate(x, p):
                 for h in range(Hq):
                     o[h], _, _ = attend_row(q[h], k_glob[b, h // g, :t + 1], v_glob[b, h // g, :t + 1], scale)
                 new[b] = h_t[b] + wo @ o.reshape(Hq * d)
+                if ffn is not None:
+                    new[b] = swiglu_ffn_row(new[b], ffn, p.eps)
             h_t = new
         out[:, t, :] = h_t
     return out, (k_glob, v_glob), rings

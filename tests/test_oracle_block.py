@@ -6,7 +6,10 @@
   duplicated copies, bitwise;
 * causality of the whole block, bitwise;
 * library routine: an independent float64 torch composition (rms_norm,
-  linear, scaled_dot_product_attention with explicit masks).
+  linear, scaled_dot_product_attention with explicit masks, silu for the
+  SwiGLU feed-forward), with and without the feed-forward;
+* the SwiGLU pieces: silu against torch's over the whole float64 range, and
+  the feed-forward's early-exit and causality identities.
 """
 import math
 
@@ -20,19 +23,23 @@ from oracle.block import BlockParams, linear_rows
 RNG = np.random.default_rng(2024)
 
 
-def make_params(D=32, Hq=4, Hkv=2, d=8, Ls=2, Lc=2, W=5, std=None):
+def make_params(D=32, Hq=4, Hkv=2, d=8, Ls=2, Lc=2, W=5, std=None, ffn_dim=None):
     std = std or 1 / math.sqrt(D)
     r = lambda *s: RNG.standard_normal(s) * std  # noqa: E731
+    ffn = (lambda: (r(ffn_dim, D), r(ffn_dim, D), r(D, ffn_dim) * math.sqrt(D / ffn_dim))) if ffn_dim else None
     return BlockParams(
         n_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=W,
         swa_wq=[r(Hq * d, D) for _ in range(Ls)], swa_wk=[r(Hkv * d, D) for _ in range(Ls)],
         swa_wv=[r(Hkv * d, D) for _ in range(Ls)], swa_wo=[r(D, Hq * d) for _ in range(Ls)],
         glob_wk=r(Hkv * d, D), glob_wv=r(Hkv * d, D),
-        cross_wq=[r(Hq * d, D) for _ in range(Lc)], cross_wo=[r(D, Hq * d) for _ in range(Lc)])
+        cross_wq=[r(Hq * d, D) for _ in range(Lc)], cross_wo=[r(D, Hq * d) for _ in range(Lc)],
+        swa_ffn=[ffn() for _ in range(Ls)] if ffn else [],
+        cross_ffn=[ffn() for _ in range(Lc)] if ffn else [])
 
 
-def test_early_exit_is_bitwise_exact():
-    p = make_params()
+@pytest.mark.parametrize("ffn_dim", [None, 24])
+def test_early_exit_is_bitwise_exact(ffn_dim):
+    p = make_params(ffn_dim=ffn_dim)
     x = RNG.standard_normal((2, 23, 32))
     full, _ = oracle.yoco_block(x, p)
     last, _ = oracle.yoco_block_early_exit(x, p)
@@ -56,9 +63,10 @@ def test_sharing_equals_duplicated_caches_bitwise():
     assert np.array_equal(out, xs)
 
 
+@pytest.mark.parametrize("ffn_dim", [None, 40])
 @pytest.mark.parametrize("t_star", [3, 15])
-def test_block_causality_bitwise(t_star):
-    p = make_params()
+def test_block_causality_bitwise(t_star, ffn_dim):
+    p = make_params(ffn_dim=ffn_dim)
     x = RNG.standard_normal((1, 20, 32))
     x2 = x.copy()
     x2[:, t_star + 1:] = 1e4
@@ -79,22 +87,67 @@ def _torch_block(x, p):
     causal = ii[None, :] <= ii[:, None]
     F = torch.nn.functional
     split = lambda y, h: y.view(B, N, h, d).permute(0, 2, 1, 3)  # noqa: E731
-    for wq, wk, wv, wo in zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo):
+    def ffn(X, w):
+        if w is None:
+            return X
+        n = F.rms_norm(X, (D,), eps=p.eps)
+        return X + F.linear(F.silu(F.linear(n, t(w[0]))) * F.linear(n, t(w[1])), t(w[2]))
+
+    for layer, (wq, wk, wv, wo) in enumerate(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo)):
         n = F.rms_norm(X, (D,), eps=p.eps)
         q, k, v = split(F.linear(n, t(wq)), Hq), split(F.linear(n, t(wk)), Hkv), split(F.linear(n, t(wv)), Hkv)
         o = F.scaled_dot_product_attention(q, k.repeat_interleave(g, 1), v.repeat_interleave(g, 1), attn_mask=swa)
         X = X + F.linear(o.permute(0, 2, 1, 3).reshape(B, N, Hq * d), t(wo))
+        X = ffn(X, p.swa_ffn[layer] if p.swa_ffn else None)
     n = F.rms_norm(X, (D,), eps=p.eps)
     K, V = split(F.linear(n, t(p.glob_wk)), Hkv), split(F.linear(n, t(p.glob_wv)), Hkv)
-    for wq, wo in zip(p.cross_wq, p.cross_wo):
+    for layer, (wq, wo) in enumerate(zip(p.cross_wq, p.cross_wo)):
         q = split(F.linear(F.rms_norm(X, (D,), eps=p.eps), t(wq)), Hq)
         o = F.scaled_dot_product_attention(q, K.repeat_interleave(g, 1), V.repeat_interleave(g, 1), attn_mask=causal)
         X = X + F.linear(o.permute(0, 2, 1, 3).reshape(B, N, Hq * d), t(wo))
+        X = ffn(X, p.cross_ffn[layer] if p.cross_ffn else None)
     return X.numpy()
 
 
-def test_block_matches_independent_torch_composition():
-    p = make_params(D=48, Hq=6, Hkv=2, d=8, Ls=2, Lc=3, W=7)
+@pytest.mark.parametrize("ffn_dim", [None, 56])
+def test_block_matches_independent_torch_composition(ffn_dim):
+    p = make_params(D=48, Hq=6, Hkv=2, d=8, Ls=2, Lc=3, W=7, ffn_dim=ffn_dim)
     x = RNG.standard_normal((2, 30, 48))
     out, _ = oracle.yoco_block(x, p)
     assert np.max(np.abs(out - _torch_block(x, p))) < 1e-11
+
+
+def test_feed_forward_changes_the_block():
+    """The feed-forward is really applied (a dropped term would leave the
+    block equal to the attention-only one)."""
+    p = make_params(ffn_dim=24)
+    x = RNG.standard_normal((1, 9, 32))
+    with_ffn, _ = oracle.yoco_block(x, p)
+    p.swa_ffn, p.cross_ffn = [], []
+    without, _ = oracle.yoco_block(x, p)
+    assert np.max(np.abs(with_ffn - without)) > 1e-2
+
+
+def test_silu_matches_torch_over_the_float64_range():
+    z = np.concatenate([np.linspace(-800, 800, 3201), RNG.standard_normal(200) * 6, [0.0, -0.0, 1e-300, -1e-300]])
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    with np.errstate(over="raise", invalid="raise", divide="raise"):
+        got = oracle.silu(z)
+    assert np.allclose(got, ref, rtol=1e-15, atol=1e-300)
+    # closed forms: silu(0) = 0, silu(z) -> z for z >> 0, -> 0 for z << 0
+    assert oracle.silu(0.0) == 0.0 and oracle.silu(800.0) == 800.0 and oracle.silu(-800.0) == 0.0
+
+
+def test_swiglu_row_brute_force():
+    D, F = 5, 3
+    wg, wu, wd = RNG.standard_normal((F, D)), RNG.standard_normal((F, D)), RNG.standard_normal((D, F))
+    x = RNG.standard_normal(D)
+    ms = sum(v * v for v in x) / D
+    n = [v / math.sqrt(ms + 1e-6) for v in x]
+    hid = []
+    for j in range(F):
+        a = sum(wg[j, i] * n[i] for i in range(D))
+        b = sum(wu[j, i] * n[i] for i in range(D))
+        hid.append(a / (1 + math.exp(-a)) * b)
+    ref = [x[i] + sum(wd[i, j] * hid[j] for j in range(F)) for i in range(D)]
+    assert np.allclose(oracle.swiglu_ffn_row(x, (wg, wu, wd), 1e-6), ref, atol=1e-13)

@@ -91,9 +91,9 @@ def test_ring_decode_brute_force():
         assert lse[0, h] == pytest.approx(m + math.log(tot), abs=1e-13)
 
 
-@pytest.mark.parametrize("W,N", [(5, 23), (32, 9)])
-def test_generation_equals_full_forward_bitwise(W, N):
-    p = make_params(W=W)
+@pytest.mark.parametrize("W,N,ffn_dim", [(5, 23, None), (32, 9, None), (4, 13, 24)])
+def test_generation_equals_full_forward_bitwise(W, N, ffn_dim):
+    p = make_params(W=W, ffn_dim=ffn_dim)
     x = RNG.standard_normal((2, N, 32))
     full, (kg, vg) = oracle.yoco_block(x, p)
     gen, (kg2, vg2), rings = oracle.yoco_block_generate(x, p)
@@ -102,7 +102,7 @@ def test_generation_equals_full_forward_bitwise(W, N):
     # each ring holds the last W positions' K/V of its layer (slot t mod W):
     # recompute the self-decoder layer inputs of the full forward
     h = np.array(x, dtype=np.float64)
-    for (wq, wk, wv, wo), (kr, vr) in zip(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo), rings):
+    for layer, ((wq, wk, wv, wo), (kr, vr)) in enumerate(zip(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo), rings)):
         n = _norm_rows(h, p.eps)
         k = _heads(linear_rows(n, wk), p.n_kv_heads, p.head_dim)
         v = _heads(linear_rows(n, wv), p.n_kv_heads, p.head_dim)
@@ -111,8 +111,9 @@ def test_generation_equals_full_forward_bitwise(W, N):
             assert np.array_equal(vr[:, :, t % W], v[:, :, t])
         q = _heads(linear_rows(n, wq), p.n_heads, p.head_dim)
         o, _ = oracle.swa_attention(q, k, v, W)
-        from oracle.block import _merge
+        from oracle.block import _merge, _ffn_rows
         h = h + linear_rows(_merge(o), wo)
+        h = _ffn_rows(h, p.ffn("swa", layer), p.eps)
 
 
 def test_generation_catches_a_wrong_slot():
