@@ -235,6 +235,56 @@ yoco_status yoco_gret_group_norm_swish(const void* y, const void* g, void* out, 
                                        int d, float eps, yoco_dtype dtype, void* stream);
 
 /*
+ * Block layer glue: pre-norm Q/K/V projection of one attention layer.
+ * Source: podcast segment 12 (a self-decoder layer runs its attention on the
+ * normalised input, plus a residual; a cross-decoder layer keeps only its own
+ * query projection).  Normalisation read as RMSNorm, as for the global
+ * projection:
+ *   n_t = x_t / sqrt(mean_j x_tj^2 + eps) * gamma,
+ *   q[b,h,t,c] = sum_j n_bt,j W_q[h*d+c, j]       (k, v likewise)
+ *   x          [B, N, D];  norm_w [D] or NULL (gamma = 1)
+ *   w_q        [Hq*d, D];  q_out [B, Hq, N, d]
+ *   w_k, w_v   [Hkv*d, D]; k_out, v_out [B, Hkv, N, d]; Hkv = 0 (all four
+ *              NULL) projects q only, as a cross-decoder layer does
+ * Requires D % 64 == 0, D <= 65536, d in {64, 128}; one dtype (F32 or BF16)
+ * for every tensor.  Numerics as yoco_global_kv_proj.
+ */
+yoco_status yoco_qkv_proj(const void* x, const void* norm_w, const void* w_q, const void* w_k,
+                          const void* w_v, void* q_out, void* k_out, void* v_out, int B, int N,
+                          int D, int Hq, int Hkv, int d, float eps, yoco_dtype dtype, void* stream);
+
+/*
+ * Block layer glue: the SwiGLU feed-forward's gated hidden activations.
+ * Source: podcast segment 12 (each layer's attention is followed by a SwiGLU
+ * feed-forward; the sizes are the caller's, the pages give none).
+ *   h[b,t,j] = silu(n_bt . W_gate[j]) * (n_bt . W_up[j]),  silu(z) = z / (1 + e^-z),
+ *   n = RMSNorm(x) * gamma as above.
+ *   x [B, N, D]; norm_w [D] or NULL; w_gate, w_up [F, D]; h [B, N, F]
+ * Requires D % 64 == 0, D <= 65536, F % 4 == 0.  h is rounded to the dtype
+ * (it feeds yoco_linear_residual with W_down).
+ */
+yoco_status yoco_swiglu(const void* x, const void* norm_w, const void* w_gate, const void* w_up,
+                        void* h, int B, int N, int D, int F, float eps, yoco_dtype dtype,
+                        void* stream);
+
+/*
+ * Block layer glue: a residual product, y += a W^T, row by row.
+ * Source: podcast segment 12 (every sub-layer adds its result to the
+ * residual stream): the attention output projection W_o and the
+ * feed-forward's W_down.
+ *   a_heads == 0: a [B, N, K], row (b, n) is a[b, n, :]
+ *   a_heads  > 0: a [B, a_heads, N, K / a_heads] head-major (an attention
+ *                 output); row (b, n) is the concatenation over heads h of
+ *                 a[b, h, n, :]
+ *   w [F, K];  y [B, N, F] read and updated in place (the residual stream);
+ *   y must not overlap a or w.
+ * Requires K % 64 == 0 (and (K / a_heads) % 64 == 0), K <= 65536, F % 4 == 0.
+ * With BF16, y + a W^T is formed in float32 and rounded once.
+ */
+yoco_status yoco_linear_residual(const void* a, int a_heads, const void* w, void* y, int B, int N,
+                                 int K, int F, yoco_dtype dtype, void* stream);
+
+/*
  * Quantise a K or V tensor to an 8-bit cache.
  * Source: podcast segments 1 and 24 (8-bit KV cache as the deployed form);
  * the format is fixed here: OCP e4m3fn, one float32 scale per KV head over

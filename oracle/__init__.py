@@ -51,7 +51,7 @@ from .fp8 import (  # noqa: F401
     quantize_kv_fp8,
     dequantize_kv_fp8,
 )
-from .block import BlockParams, silu, swiglu_ffn_row, yoco_block, yoco_block_early_exit, yoco_block_generate  # noqa: F401
+from .block import BlockParams, linear_rows, silu, swiglu_hidden_row, swiglu_ffn_row, yoco_block, yoco_block_early_exit, yoco_block_generate  # noqa: F401
 from .memory import yoco_kv_cache_bytes, transformer_kv_cache_bytes  # noqa: F401
 from .retention import (  # noqa: F401
     gret_log_decay,

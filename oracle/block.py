@@ -50,7 +50,7 @@ import numpy as np
 from .attention import attend_row, cross_prefill_attention, ring_window, swa_attention
 from .projection import global_kv_proj, rmsnorm_row
 
-__all__ = ["BlockParams", "linear_rows", "silu", "swiglu_ffn_row", "yoco_block", "yoco_block_early_exit",
+__all__ = ["BlockParams", "linear_rows", "silu", "swiglu_hidden_row", "swiglu_ffn_row", "yoco_block", "yoco_block_early_exit",
            "yoco_block_generate"]
 
 
@@ -86,11 +86,17 @@ def silu(z):
     return np.where(z >= 0, z / (1.0 + e), z * e / (1.0 + e))
 
 
+def swiglu_hidden_row(x_row, w_gate, w_up, gamma=None, eps=1e-6):
+    """The feed-forward's hidden activations for one row: silu(W_gate n) * (W_up n),
+    n = rmsnorm(x) * gamma."""
+    n = rmsnorm_row(x_row, gamma, eps)
+    return silu(w_gate @ n) * (w_up @ n)
+
+
 def swiglu_ffn_row(x_row, ffn, eps):
     """x + W_down (silu(W_gate n) * (W_up n)), n = rmsnorm(x), for one row."""
     wg, wu, wd = ffn
-    n = rmsnorm_row(x_row, None, eps)
-    return x_row + wd @ (silu(wg @ n) * (wu @ n))
+    return x_row + wd @ swiglu_hidden_row(x_row, wg, wu, None, eps)
 
 
 def _ffn_rows(x, ffn, eps):

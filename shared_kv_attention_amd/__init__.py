@@ -32,6 +32,9 @@ __all__ = [
     "yoco_gret_prefill_workspace_bytes",
     "yoco_gret_decode",
     "yoco_gret_group_norm_swish",
+    "yoco_qkv_proj",
+    "yoco_swiglu",
+    "yoco_linear_residual",
     "yoco_kv_quantize_fp8",
     "yoco_kv_quantize_fp8_workspace_bytes",
     "yoco_status_string",
@@ -61,6 +64,9 @@ _SIGS = {
     "yoco_gret_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "yoco_gret_decode": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _i, _i, _i, _vp]),
     "yoco_gret_group_norm_swish": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_qkv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_swiglu": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_linear_residual": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "yoco_kv_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "yoco_kv_quantize_fp8_workspace_bytes": (_sz, [_i]),
     "yoco_status_string": (ctypes.c_char_p, [_i]),
@@ -145,6 +151,52 @@ def yoco_global_kv_proj(x, w_k, w_v, k_out, v_out, pos0=0, norm_w=None, eps=1e-6
                                    B, N, D, Hkv, d, n_cap, pos0, eps, _dtype_code(x), _stream(stream))
     _check(st, "yoco_global_kv_proj")
     return k_out, v_out
+
+
+def yoco_qkv_proj(x, w_q, head_dim, w_k=None, w_v=None, q_out=None, k_out=None, v_out=None, norm_w=None,
+                  eps=1e-6, stream=None):
+    """Pre-norm Q/K/V projection: q [B, Hq, N, d] = heads(RMSNorm(x) @ W_q^T), k and v likewise
+    ([B, Hkv, N, d]); w_k = w_v = None projects q only.  Returns (q, k, v) (k, v None for q only)."""
+    torch = _torch()
+    B, N, D = x.shape
+    d = int(head_dim)
+    Hq = w_q.shape[0] // d
+    Hkv = 0 if w_k is None else w_k.shape[0] // d
+    if q_out is None:
+        q_out = torch.empty(B, Hq, N, d, dtype=x.dtype, device=x.device)
+    if Hkv > 0:
+        if k_out is None:
+            k_out = torch.empty(B, Hkv, N, d, dtype=x.dtype, device=x.device)
+        if v_out is None:
+            v_out = torch.empty(B, Hkv, N, d, dtype=x.dtype, device=x.device)
+    st = lib().yoco_qkv_proj(_ptr(x), _ptr(norm_w), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(q_out),
+                             _ptr(k_out if Hkv else None), _ptr(v_out if Hkv else None), B, N, D, Hq, Hkv, d,
+                             float(eps), _dtype_code(x), _stream(stream))
+    _check(st, "yoco_qkv_proj")
+    return q_out, (k_out if Hkv else None), (v_out if Hkv else None)
+
+
+def yoco_swiglu(x, w_gate, w_up, h=None, norm_w=None, eps=1e-6, stream=None):
+    """h [B, N, F] = silu(RMSNorm(x) @ W_gate^T) * (RMSNorm(x) @ W_up^T)."""
+    torch = _torch()
+    B, N, D = x.shape
+    F = w_gate.shape[0]
+    if h is None:
+        h = torch.empty(B, N, F, dtype=x.dtype, device=x.device)
+    st = lib().yoco_swiglu(_ptr(x), _ptr(norm_w), _ptr(w_gate), _ptr(w_up), _ptr(h), B, N, D, F, float(eps),
+                           _dtype_code(x), _stream(stream))
+    _check(st, "yoco_swiglu")
+    return h
+
+
+def yoco_linear_residual(a, w, y, a_heads=0, stream=None):
+    """y [B, N, F] += rows(a) @ W^T in place; a [B, N, K], or head-major [B, H, N, K/H] with a_heads = H."""
+    B, N, F = y.shape
+    K = w.shape[1]
+    st = lib().yoco_linear_residual(_ptr(a), int(a_heads), _ptr(w), _ptr(y), B, N, K, F, _dtype_code(y),
+                                    _stream(stream))
+    _check(st, "yoco_linear_residual")
+    return y
 
 
 def yoco_swa_attn(q, k, v, window, o=None, lse=None, softmax_scale=0.0, stream=None):

@@ -84,6 +84,86 @@ yoco_status yoco_global_kv_proj(const void* x, const void* norm_w, const void* w
   return launched(yoco::launch_kv_proj(a, dtype == YOCO_BF16, as_stream(stream)));
 }
 
+static bool lin_sizes_ok(int B, int N, int K, int F, int fpt) {
+  if (B < 1 || N < 1 || K < 1 || F < 1) return false;
+  const long long M = (long long)B * N;
+  if (M > kIntMax) return false;
+  return ((M + 127) / 128) * (((long long)F + fpt - 1) / fpt) <= kIntMax;
+}
+
+yoco_status yoco_qkv_proj(const void* x, const void* norm_w, const void* w_q, const void* w_k, const void* w_v,
+                          void* q_out, void* k_out, void* v_out, int B, int N, int D, int Hq, int Hkv, int d,
+                          float eps, yoco_dtype dtype, void* stream) {
+  if (!x || !w_q || !q_out) return YOCO_ERR_NULL;
+  if (Hkv > 0 && (!w_k || !w_v || !k_out || !v_out)) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (Hq < 1 || Hkv < 0 || !(eps >= 0.f) || isinf(eps)) return YOCO_ERR_SHAPE;
+  if ((long long)(Hq + 2LL * Hkv) * d > kIntMax) return YOCO_ERR_SHAPE;
+  if (!head_dim_ok(d)) return YOCO_ERR_UNSUPPORTED;
+  const int F = (Hq + 2 * Hkv) * d;
+  if (!lin_sizes_ok(B, N, D, F, 128)) return YOCO_ERR_SHAPE;
+  if (D % 64 != 0 || D > 65536) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(q_out, 16) || (norm_w && !aligned(norm_w, 16)) ||
+      (Hkv > 0 && (!aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))))
+    return YOCO_ERR_ALIGN;
+  yoco::LinArgs a{};
+  a.x = x;
+  a.norm_w = norm_w;
+  a.w0 = w_q;
+  a.w1 = Hkv > 0 ? w_k : nullptr;
+  a.w2 = Hkv > 0 ? w_v : nullptr;
+  a.y0 = q_out;
+  a.y1 = Hkv > 0 ? k_out : nullptr;
+  a.y2 = Hkv > 0 ? v_out : nullptr;
+  a.B = B; a.N = N; a.K = D; a.F = F;
+  a.x_heads = 0;
+  a.f1 = Hkv > 0 ? Hq * d : F;
+  a.f2 = Hkv > 0 ? (Hq + Hkv) * d : F;
+  a.h0 = Hq; a.h1 = Hkv; a.d = d;
+  a.norm = 1;
+  a.eps = eps;
+  return launched(yoco::launch_linear(a, yoco::kLinQKV, dtype == YOCO_BF16, as_stream(stream)));
+}
+
+yoco_status yoco_swiglu(const void* x, const void* norm_w, const void* w_gate, const void* w_up, void* h, int B,
+                        int N, int D, int F, float eps, yoco_dtype dtype, void* stream) {
+  if (!x || !w_gate || !w_up || !h) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (!(eps >= 0.f) || isinf(eps)) return YOCO_ERR_SHAPE;
+  if (!lin_sizes_ok(B, N, D, F, 64) || F % 4 != 0) return YOCO_ERR_SHAPE;
+  if (D % 64 != 0 || D > 65536) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(h, 16) ||
+      (norm_w && !aligned(norm_w, 16)))
+    return YOCO_ERR_ALIGN;
+  yoco::LinArgs a{};
+  a.x = x;
+  a.norm_w = norm_w;
+  a.w0 = w_gate;
+  a.w1 = w_up;
+  a.y0 = h;
+  a.B = B; a.N = N; a.K = D; a.F = F;
+  a.norm = 1;
+  a.eps = eps;
+  return launched(yoco::launch_linear(a, yoco::kLinSwiGLU, dtype == YOCO_BF16, as_stream(stream)));
+}
+
+yoco_status yoco_linear_residual(const void* x, int a_heads, const void* w, void* y, int B, int N, int K, int F,
+                                 yoco_dtype dtype, void* stream) {
+  if (!x || !w || !y) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (a_heads < 0 || !lin_sizes_ok(B, N, K, F, 128) || F % 4 != 0) return YOCO_ERR_SHAPE;
+  if (a_heads > 0 && K % a_heads != 0) return YOCO_ERR_SHAPE;
+  if (K % 64 != 0 || K > 65536 || (a_heads > 0 && (K / a_heads) % 64 != 0)) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return YOCO_ERR_ALIGN;
+  yoco::LinArgs a{};
+  a.x = x;
+  a.w0 = w;
+  a.y0 = y;
+  a.B = B; a.N = N; a.K = K; a.F = F;
+  a.x_heads = a_heads;
+  return launched(yoco::launch_linear(a, yoco::kLinResidual, dtype == YOCO_BF16, as_stream(stream)));
+}
+
 static yoco_status attn_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                                int Hkv, int Nq, int n_kv, int kv_rows, int q_offset, int d, int window,
                                bool swa, float softmax_scale, yoco_dtype dtype, void* stream) {

@@ -52,6 +52,27 @@ struct ProjArgs {
   float eps;
 };
 
+// Position-wise block layers (linear.hip).  Weight matrices are [rows, K]
+// ("out x in"); x rows are [K] (row-major [B*N, K]) or, with x_heads > 0,
+// gathered from a head-major [B, x_heads, N, K / x_heads] tensor.
+enum { kLinQKV = 0, kLinSwiGLU = 1, kLinResidual = 2 };
+struct LinArgs {
+  const void* x;
+  const void* norm_w;  // [K] gain or null (QKV / SwiGLU with norm)
+  const void* w0;      // QKV: W_q; SwiGLU: W_gate; residual: W
+  const void* w1;      // QKV: W_k (or null); SwiGLU: W_up
+  const void* w2;      // QKV: W_v (or null)
+  void* y0;            // QKV: q [B, h0, N, d]; SwiGLU: h [B*N, F]; residual: y [B*N, F] (+=)
+  void* y1;            // QKV: k [B, h1, N, d]
+  void* y2;            // QKV: v [B, h1, N, d]
+  int B, N, K, F;      // F: output features (QKV: (h0 + 2 h1) d; SwiGLU: hidden size)
+  int x_heads;         // 0 or the head count of a head-major x
+  int f1, f2;          // QKV: first k feature, first v feature (F when absent)
+  int h0, h1, d;       // QKV: q heads, k/v heads, head dim
+  int norm;            // fused RMSNorm of the x rows (QKV, SwiGLU)
+  float eps;
+};
+
 struct RingAppendArgs {
   const void* k_new;   // [B, Hkv, d]
   const void* v_new;
@@ -108,6 +129,7 @@ struct QuantArgs {
 hipError_t launch_attn(const AttnArgs& a, bool is_bf16, int d, bool swa, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hipStream_t stream);
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream);
+hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t stream);
 hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t stream);

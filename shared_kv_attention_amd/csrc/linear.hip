@@ -1,0 +1,341 @@
+// Position-wise layers of a YOCO block on the matrix cores: the pre-norm
+// Q/K/V projection, the SwiGLU feed-forward's gate/up product, and the
+// residual products (attention output projection, feed-forward down
+// projection).
+//
+// What is computed (YOCO podcast transcript, segment 12: each layer runs its
+// attention on the normalised input plus a residual, followed by a SwiGLU
+// feed-forward; a cross-decoder layer keeps only its own query projection):
+// with n_t = x_t / sqrt(mean(x_t^2) + eps) * gamma for token t,
+//   QKV:     q[b, h, t, c] = n_t . W_q[h*d + c]   (k, v likewise, head-major)
+//   SwiGLU:  h_t[j] = silu(n_t . W_gate[j]) * (n_t . W_up[j]),  silu(z) = z sigmoid(z)
+//   residual: y_t += a_t W^T, where a_t is a row of a [B, N, K] matrix or the
+//            concatenation over heads of a head-major [B, H, N, K/H] tensor
+//            (the attention output feeding W_o).
+//
+// Design (MI355X-first), one kernel template for the three forms:
+//  * C^T = W X^T on 32x32x16 bf16 MFMA (32x32x2 f32 for float32): 128
+//    features x 128 tokens per 256-thread workgroup, 4 waves of 64 x 64, k in
+//    stages of 128 bytes per row, double-buffered LDS in distinct objects with
+//    XOR-swizzled 16-byte chunks.  Each lane's results are 4 consecutive
+//    features of one token, so every epilogue stores 4 contiguous values.
+//  * W tiles go global -> LDS directly; X passes through registers, where the
+//    RMSNorm sum of squares is taken from the values being moved (X is read
+//    once) and the row factor is applied to the float32 accumulator.  The
+//    head-major gather of the attention output is a per-stage address.
+//  * SwiGLU: a tile's 128 weight rows are 32 gate rows, the 32 matching up
+//    rows, and again, so one wave holds gate and up of the same (feature,
+//    token) pairs in two accumulators and the activation is formed in
+//    registers; the hidden activations are written once.
+//  * Feature tiles are split evenly over the 8 XCDs when they divide, so each
+//    XCD keeps its slice of W in its own L2 while the token tiles stream.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace yoco {
+
+template <typename T>
+struct LinCfg {
+  static constexpr int E = Elem<T>::bytes;
+  static constexpr int BKK = 128 / E;            // k elements per stage (128-byte rows)
+  static constexpr int PER_T = 128 * 8 / 256;    // 16-byte chunks per thread per operand (= 4)
+  static constexpr int NKS = BKK / 16;           // matrix-core k steps per stage
+  static constexpr int TILE_BYTES = 128 * 128;
+};
+
+// 16-byte chunk swizzle within a 128-byte row: the 32 rows a wave reads at
+// once spread over all LDS banks.
+__device__ __forceinline__ int lin_swz(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::frag lin_frag(const char* tile, int row, int kc, int g) {
+  const char* rowp = tile + row * 128;
+  const int sw = lin_swz(row);
+  typename Elem<T>::frag f;
+  if constexpr (sizeof(T) == 2) {
+    f = *reinterpret_cast<const bf16x8*>(rowp + (((2 * kc + g) ^ sw) << 4));
+  } else {
+    const int ch = 4 * kc + 2 * g;
+    f32x4 a = *reinterpret_cast<const f32x4*>(rowp + ((ch ^ sw) << 4));
+    f32x4 b = *reinterpret_cast<const f32x4*>(rowp + (((ch + 1) ^ sw) << 4));
+    f = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ float lin_sumsq(u32x4 w) {
+  float s = 0.f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wi = w[i];
+      const bf16x2 x = __builtin_bit_cast(bf16x2, wi);
+      s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);   // bf16 squares are exact in float32
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = __uint_as_float(w[i]);
+      s = fmaf(x, x, s);
+    }
+  }
+  return s;
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 lin_gain(u32x4 w, u32x4 gw) {
+  u32x4 r;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(w[i] << 16) * __uint_as_float(gw[i] << 16);
+      const float hi = __uint_as_float(w[i] & 0xFFFF0000u) * __uint_as_float(gw[i] & 0xFFFF0000u);
+      bf16x2 p{(bf16)lo, (bf16)hi};
+      r[i] = __builtin_bit_cast(uint32_t, p);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(__uint_as_float(w[i]) * __uint_as_float(gw[i]));
+  }
+  return r;
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.f + __expf(-z)); }
+
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float v0, float v1, float v2, float v3) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 v{(bf16)v0, (bf16)v1, (bf16)v2, (bf16)v3};
+    *reinterpret_cast<bf16x4*>(dst) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T* src) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(src);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  } else {
+    return *reinterpret_cast<const f32x4*>(src);
+  }
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
+  using C = LinCfg<T>;
+  __shared__ __attribute__((aligned(16))) char wbuf0[C::TILE_BYTES], xbuf0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char wbuf1[C::TILE_BYTES], xbuf1[C::TILE_BYTES];
+  __shared__ float rs_lds[128];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 5, r32 = l & 31;
+  const int wf = w >> 1, wt = w & 1;
+  const int M = a.B * a.N;
+  // features per tile: 128 weight rows; for SwiGLU they are 64 hidden features
+  constexpr int FPT = MODE == kLinSwiGLU ? 64 : 128;
+  const int nft = (a.F + FPT - 1) / FPT;
+  const int id = blockIdx.x;
+  int tt, ft;
+  if (nft % 8 == 0) {
+    const int per = nft / 8, xcd = id & 7, sl = id >> 3;
+    ft = xcd * per + sl % per;
+    tt = sl / per;
+  } else {
+    ft = id % nft;
+    tt = id / nft;
+  }
+  const int t0 = tt * 128;
+
+  // staging: chunk slot P = 256 r + tid holds tile row P / 8 at physical
+  // chunk P % 8; rows past the end are clamped (finite data, never stored)
+  const int srow0 = tid >> 3, sch = tid & 7;
+  const char* wsrc[C::PER_T];
+  size_t xoff[C::PER_T];
+#pragma unroll
+  for (int r = 0; r < C::PER_T; ++r) {
+    const int slot = 256 * r + 64 * w + l;
+    const int row = slot >> 3, pch = slot & 7;
+    const void* wm;
+    int fr;
+    if constexpr (MODE == kLinSwiGLU) {
+      const int hf = min(ft * 64 + (row >> 6) * 32 + (row & 31), a.F - 1);
+      wm = (row & 32) ? a.w1 : a.w0;
+      fr = hf;
+    } else {
+      const int f = min(ft * 128 + row, a.F - 1);
+      if (MODE == kLinQKV && f >= a.f2) { wm = a.w2; fr = f - a.f2; }
+      else if (MODE == kLinQKV && f >= a.f1) { wm = a.w1; fr = f - a.f1; }
+      else { wm = a.w0; fr = f; }
+    }
+    wsrc[r] = static_cast<const char*>(wm) + (size_t)fr * a.K * C::E + ((pch ^ lin_swz(row)) << 4);
+    const int trow = min(t0 + srow0 + 32 * r, M - 1);
+    if (a.x_heads > 0) {
+      const int dh = a.K / a.x_heads, bb = trow / a.N, n = trow % a.N;
+      xoff[r] = ((size_t)bb * a.x_heads * a.N + n) * dh * C::E + sch * 16;
+    } else {
+      xoff[r] = (size_t)trow * a.K * C::E + sch * 16;
+    }
+  }
+  const char* xbase = static_cast<const char*>(a.x);
+  auto x_stage_off = [&](int ks) -> size_t {
+    const int k0 = ks * C::BKK;
+    if (a.x_heads > 0) {
+      const int dh = a.K / a.x_heads, h = k0 / dh, c0 = k0 % dh;
+      return ((size_t)h * a.N * dh + c0) * C::E;
+    }
+    return (size_t)k0 * C::E;
+  };
+
+  float ss[C::PER_T];
+#pragma unroll
+  for (int r = 0; r < C::PER_T; ++r) ss[r] = 0.f;
+  u32x4 xr[C::PER_T];
+  auto load_stage = [&](int ks, char* wdst) {
+    const size_t koff = (size_t)ks * C::BKK * C::E;
+    const size_t xo = x_stage_off(ks);
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(wsrc[r] + koff),
+                                       (__attribute__((address_space(3))) void*)(wdst + (256 * r + 64 * w) * 16),
+                                       16, 0, 0);
+      xr[r] = *reinterpret_cast<const u32x4*>(xbase + xoff[r] + xo);
+    }
+  };
+  const bool norm = MODE != kLinResidual && a.norm;
+  auto store_stage = [&](char* xdst, int ks) {
+    u32x4 gw{0, 0, 0, 0};
+    const bool gain = norm && a.norm_w != nullptr;
+    if (gain)
+      gw = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.norm_w) + (size_t)ks * C::BKK * C::E + sch * 16);
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      const int row = srow0 + 32 * r;
+      if (norm) ss[r] += lin_sumsq<T>(xr[r]);
+      const u32x4 xv = gain ? lin_gain<T>(xr[r], gw) : xr[r];
+      *reinterpret_cast<u32x4*>(xdst + row * 128 + ((sch ^ lin_swz(row)) << 4)) = xv;
+    }
+  };
+  // the direct W writes into LDS land asynchronously: wait before the barrier
+  auto landed = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
+
+  const int nks = a.K / C::BKK;
+  auto kstep = [&](int ks, const char* wt_tile, const char* xt_tile, char* wn, char* xn) __attribute__((always_inline)) {
+    const bool has_next = ks + 1 < nks;
+    if (has_next) load_stage(ks + 1, wn);
+#pragma unroll
+    for (int kc = 0; kc < C::NKS; ++kc) {
+      typename Elem<T>::frag af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = lin_frag<T>(wt_tile, wf * 64 + i * 32 + r32, kc, g);
+        bfr[i] = lin_frag<T>(xt_tile, wt * 64 + i * 32 + r32, kc, g);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma32(af[i], bfr[jj], acc[i][jj]);
+    }
+    if (has_next) {
+      store_stage(xn, ks + 1);
+      landed();
+    }
+    __syncthreads();
+  };
+  load_stage(0, wbuf0);
+  store_stage(xbuf0, 0);
+  landed();
+  __syncthreads();
+  for (int ks = 0; ks < nks; ks += 2) {
+    kstep(ks, wbuf0, xbuf0, wbuf1, xbuf1);
+    if (ks + 1 < nks) kstep(ks + 1, wbuf1, xbuf1, wbuf0, xbuf0);
+  }
+
+  if (norm) {
+    // the 8 threads of a staging row hold partial sums of squares
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      float s = ss[r];
+      s += dpp_f32<kDppQuadSwap1>(s);
+      s += dpp_f32<kDppQuadSwap2>(s);
+      s += dpp_f32<kDppRowHalfMirror>(s);
+      if (sch == 0) rs_lds[srow0 + 32 * r] = 1.0f / sqrtf(s / (float)a.K + a.eps);
+    }
+    __syncthreads();
+  }
+
+  // acc[i][jj][e] = C^T[tile row wf*64 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*64 + jj*32 + r32]
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int tl = wt * 64 + jj * 32 + r32;
+    const int tok = t0 + tl;
+    if (tok >= M) continue;
+    const float rs = norm ? rs_lds[tl] : 1.f;
+    const int bb = tok / a.N, n = tok % a.N;
+    if constexpr (MODE == kLinSwiGLU) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int hf = ft * 64 + wf * 32 + 8 * qd + 4 * g;
+        if (hf >= a.F) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = silu_f32(acc[0][jj][4 * qd + e] * rs) * (acc[1][jj][4 * qd + e] * rs);
+        store4<T>(static_cast<T*>(a.y0) + (size_t)tok * a.F + hf, v[0], v[1], v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int f = ft * 128 + wf * 64 + i * 32 + 8 * qd + 4 * g;
+          if (f >= a.F) continue;
+          const float v0 = acc[i][jj][4 * qd] * rs, v1 = acc[i][jj][4 * qd + 1] * rs;
+          const float v2 = acc[i][jj][4 * qd + 2] * rs, v3 = acc[i][jj][4 * qd + 3] * rs;
+          if constexpr (MODE == kLinQKV) {
+            void* out;
+            int fr, H;
+            if (f >= a.f2) { out = a.y2; fr = f - a.f2; H = a.h1; }
+            else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; }
+            else { out = a.y0; fr = f; H = a.h0; }
+            const int hh = fr / a.d, c = fr % a.d;
+            store4<T>(static_cast<T*>(out) + ((size_t)(bb * H + hh) * a.N + n) * a.d + c, v0, v1, v2, v3);
+          } else {
+            T* dst = static_cast<T*>(a.y0) + (size_t)tok * a.F + f;
+            const f32x4 old = load4<T>(dst);
+            store4<T>(dst, old[0] + v0, old[1] + v1, old[2] + v2, old[3] + v3);
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t stream) {
+  const int M = a.B * a.N;
+  const int fpt = mode == kLinSwiGLU ? 64 : 128;
+  const long long tiles = (long long)((M + 127) / 128) * ((a.F + fpt - 1) / fpt);
+  const dim3 grid((unsigned)tiles);
+#define YOCO_LIN(T, MD) hipLaunchKernelGGL((linear_kernel<T, MD>), grid, dim3(256), 0, stream, a)
+  if (is_bf16) {
+    if (mode == kLinQKV) YOCO_LIN(bf16, kLinQKV);
+    else if (mode == kLinSwiGLU) YOCO_LIN(bf16, kLinSwiGLU);
+    else YOCO_LIN(bf16, kLinResidual);
+  } else {
+    if (mode == kLinQKV) YOCO_LIN(float, kLinQKV);
+    else if (mode == kLinSwiGLU) YOCO_LIN(float, kLinSwiGLU);
+    else YOCO_LIN(float, kLinResidual);
+  }
+#undef YOCO_LIN
+  return hipGetLastError();
+}
+
+}  // namespace yoco

@@ -39,13 +39,14 @@ class Workload:
     window: int              # sliding window (0 when unused)
     weight_std: float
     decode_steps: int = 0
+    ffn_dim: int = 0         # SwiGLU hidden size of the block layers (0: no feed-forward)
 
 
 WORKLOADS = {
     "tiny_block_f32": Workload(1, "tiny_block_f32", "f32", 1, 256, 256, 4, 1, 64,
-                               2, 2, 32, 1.0 / 16.0),
+                               2, 2, 32, 1.0 / 16.0, ffn_dim=768),
     "prefill_3b_bf16": Workload(2, "prefill_3b_bf16", "bf16", 1, 4096, 3072, 24, 8, 128,
-                                8, 8, 1024, 0.02),
+                                8, 8, 1024, 0.02, ffn_dim=8192),
     "decode_32k_bf16": Workload(3, "decode_32k_bf16", "bf16", 16, 32768, 0, 32, 8, 128,
                                 0, 16, 0, 0.0, decode_steps=128),
     "early_exit_1m_bf16": Workload(4, "early_exit_1m_bf16", "bf16", 1, 1 << 20, 4096, 32, 8,

@@ -19,6 +19,8 @@ extern ProjArgs g_proj;
 extern QuantArgs g_quant;
 extern RingAppendArgs g_ring;
 extern GretArgs g_gret;
+extern LinArgs g_lin;
+extern int g_lin_mode;
 extern int g_decode_kinds[3];
 }  // namespace yoco
 
@@ -157,6 +159,24 @@ int main() {
   }
   CHECK(yoco_gret_prefill_workspace_bytes(1, 1, 10, 96, 256) == 0);
   CHECK(yoco_gret_prefill_workspace_bytes(1, 1, 10, 64, 192) == 0);
+
+  // ---- block layer glue: the argument block each form reaches its kernel with
+  n = yoco::g_launches;
+  CHECK(yoco_qkv_proj(P, nullptr, P, P, P, P, P, P, 2, 9, 256, 4, 1, 64, 1e-6f, YOCO_F32, nullptr) == YOCO_OK);
+  CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.F == 384 && yoco::g_lin.f1 == 256 && yoco::g_lin.f2 == 320);
+  CHECK(yoco::g_lin.h0 == 4 && yoco::g_lin.h1 == 1 && yoco::g_lin.norm == 1 && yoco::g_lin.K == 256);
+  CHECK(yoco_qkv_proj(P, nullptr, P, nullptr, nullptr, P, nullptr, nullptr, 1, 5, 128, 3, 0, 128, 1e-6f, YOCO_BF16,
+                      nullptr) == YOCO_OK);
+  CHECK(yoco::g_lin.F == 384 && yoco::g_lin.f1 == 384 && yoco::g_lin.f2 == 384 && yoco::g_lin.w1 == nullptr);
+  CHECK(yoco_qkv_proj(P, nullptr, P, nullptr, P, P, P, P, 1, 5, 128, 3, 1, 128, 1e-6f, YOCO_BF16, nullptr) ==
+        YOCO_ERR_NULL);
+  CHECK(yoco_swiglu(P, nullptr, P, P, P, 1, 7, 192, 344, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_lin_mode == yoco::kLinSwiGLU && yoco::g_lin.F == 344 && yoco::g_lin.K == 192 && yoco::g_lin.norm == 1);
+  CHECK(yoco_linear_residual(P, 4, P, P, 2, 3, 512, 256, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_lin_mode == yoco::kLinResidual && yoco::g_lin.x_heads == 4 && yoco::g_lin.norm == 0);
+  CHECK(yoco_linear_residual(P, 3, P, P, 2, 3, 512, 256, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_linear_residual(P, 0, P, M, 2, 3, 512, 256, YOCO_BF16, nullptr) == YOCO_ERR_ALIGN);
+  CHECK(yoco::g_launches == n + 4);
 
   // ---- fp8 quantiser
   n = yoco::g_launches;

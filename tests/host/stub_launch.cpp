@@ -14,6 +14,8 @@ RingAppendArgs g_ring;
 GretArgs g_gret;
 GretDecodeArgs g_gret_dec;
 GretNormArgs g_gret_norm;
+LinArgs g_lin;
+int g_lin_mode = -1;
 int g_decode_kinds[3];
 
 hipError_t launch_attn(const AttnArgs& a, bool, int, bool, hipStream_t) { ++g_launches; g_attn = a; return hipSuccess; }
@@ -26,4 +28,7 @@ hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t) { ++g_launch
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t) { ++g_launches; g_gret = a; return hipSuccess; }
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool, hipStream_t) { ++g_launches; g_gret_dec = a; return hipSuccess; }
 hipError_t launch_gret_norm(const GretNormArgs& a, bool, hipStream_t) { ++g_launches; g_gret_norm = a; return hipSuccess; }
+hipError_t launch_linear(const LinArgs& a, int mode, bool, hipStream_t) {
+  ++g_launches; g_lin = a; g_lin_mode = mode; return hipSuccess;
+}
 }  // namespace yoco

@@ -226,6 +226,46 @@ def test_gret_norm_errors(L, kw, code):
                                         None) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(wq=None), NULL), (dict(qo=None), NULL), (dict(wk=None), NULL), (dict(vo=None), NULL),
+    (dict(dt=yk.FP8_E4M3), DTYPE), (dict(B=0), SHAPE), (dict(N=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=-1), SHAPE),
+    (dict(eps=float("inf")), SHAPE), (dict(d=32), UNSUP), (dict(D=96), UNSUP), (dict(D=65600), UNSUP),
+    (dict(x=MIS), ALIGN), (dict(g=MIS), ALIGN), (dict(ko=MIS), ALIGN),
+    # a q-only (cross layer) call ignores the k/v pointers
+    (dict(Hkv=0, wk=None, wv=None, ko=None, vo=None, x=MIS), ALIGN),
+])
+def test_qkv_proj_errors(L, kw, code):
+    a = dict(x=P, g=None, wq=P, wk=P, wv=P, qo=P, ko=P, vo=P, B=1, N=8, D=128, Hq=4, Hkv=2, d=64, eps=1e-6,
+             dt=yk.BF16)
+    a.update(kw)
+    assert L.yoco_qkv_proj(a["x"], a["g"], a["wq"], a["wk"], a["wv"], a["qo"], a["ko"], a["vo"], a["B"], a["N"],
+                           a["D"], a["Hq"], a["Hkv"], a["d"], a["eps"], a["dt"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(wu=None), NULL), (dict(h=None), NULL), (dict(dt=yk.FP8_E4M3), DTYPE),
+    (dict(N=0), SHAPE), (dict(F=0), SHAPE), (dict(F=66), SHAPE), (dict(eps=-1.0), SHAPE),
+    (dict(D=100), UNSUP), (dict(h=MIS), ALIGN), (dict(wg=MIS), ALIGN),
+])
+def test_swiglu_errors(L, kw, code):
+    a = dict(x=P, g=None, wg=P, wu=P, h=P, B=2, N=8, D=128, F=344, eps=1e-6, dt=yk.F32)
+    a.update(kw)
+    assert L.yoco_swiglu(a["x"], a["g"], a["wg"], a["wu"], a["h"], a["B"], a["N"], a["D"], a["F"], a["eps"], a["dt"],
+                         None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=None), NULL), (dict(y=None), NULL), (dict(dt=7), DTYPE), (dict(B=0), SHAPE), (dict(F=6), SHAPE),
+    (dict(heads=-1), SHAPE), (dict(heads=3), SHAPE), (dict(K=96), UNSUP), (dict(heads=8), UNSUP),
+    (dict(y=MIS), ALIGN), (dict(w=MIS), ALIGN),
+])
+def test_linear_residual_errors(L, kw, code):
+    a = dict(a=P, heads=2, w=P, y=P, B=1, N=16, K=256, F=128, dt=yk.BF16)
+    a.update(kw)
+    assert L.yoco_linear_residual(a["a"], a["heads"], a["w"], a["y"], a["B"], a["N"], a["K"], a["F"], a["dt"],
+                                  None) == code
+
+
 def quant(L, **kw):
     a = dict(kv=P, dt=yk.F32, codes=P, scale=P, B=2, Hkv=4, n=10, d=64, ws=P, wsb=64)
     a.update(kw)

@@ -1,0 +1,275 @@
+"""GPU parity of the block's position-wise layers (yoco_qkv_proj, yoco_swiglu,
+yoco_linear_residual) against the float64 oracle, and the tiny float32 YOCO
+block run wholly on the GPU (every norm, projection, attention, feed-forward
+and residual add in libyoco) against the oracle block, full forward and early
+exit.
+
+Tolerances: float32 |out - ref| <= 1e-5 max(1, |ref|) (values O(1)).  bf16:
+these outputs are unnormalised products (a SwiGLU activation reaches ~10), so
+every element must satisfy |out - ref| <= 8e-3 |ref| + 2e-2 rms(ref) and every
+row a relative L2 error <= 1e-2: the bf16 output rounding is at most
+2^-8 |ref|; with a norm gain, x * gamma is rounded to bf16 before the product,
+which perturbs each pre-activation by about 2^-8 / sqrt(3) of its rms, and
+SwiGLU multiplies two pre-activations (so the perturbation is scaled by the
+other factor, up to ~4); an indexing mistake gives errors of the order of the
+values themselves."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.block import BlockParams
+import shared_kv_attention_amd as yk
+from shared_kv_attention_amd.synth import WORKLOADS, randn, seed_for
+from _tol import check, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def glue_check(out, ref, dt, what):
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    assert np.all(np.isfinite(out)), f"{what}: non-finite"
+    err = np.abs(out - ref)
+    if dt == "f32":
+        bound = 1e-5 * np.maximum(1.0, np.abs(ref))
+        worst = np.argmax(err - bound)
+        assert np.all(err <= bound), f"{what}: err {err.flat[worst]:.3e} at |ref| {abs(ref.flat[worst]):.3e}"
+        return
+    rms = np.sqrt(np.mean(ref ** 2))
+    bound = 8e-3 * np.abs(ref) + 2e-2 * rms
+    worst = np.argmax(err - bound)
+    assert np.all(err <= bound), f"{what}: err {err.flat[worst]:.3e} > {bound.flat[worst]:.3e}"
+    rows = ref.reshape(-1, ref.shape[-1])
+    rel = np.linalg.norm((out - ref).reshape(rows.shape), axis=1) / np.maximum(np.linalg.norm(rows, axis=1), 1e-30)
+    assert rel.max() <= 1e-2, f"{what}: row relative L2 {rel.max():.3e}"
+
+
+def _tdt(dt):
+    return torch.float32 if dt == "f32" else torch.bfloat16
+
+
+def _gain(D, seed, dt):
+    return (1 + 0.5 * randn((D,), seed, dtype=dt, device=DEV).float()).to(_tdt(dt))
+
+
+QKV_CASES = [
+    # B, N, D, Hq, Hkv, d, gain, dtype
+    (1, 77, 256, 4, 1, 64, False, "f32"),
+    (2, 200, 384, 3, 1, 128, True, "bf16"),
+    (1, 1, 128, 2, 0, 64, False, "bf16"),        # q only, one token
+    (1, 300, 192, 6, 2, 64, True, "f32"),
+    (3, 129, 512, 8, 0, 128, False, "bf16"),     # cross-layer query projection
+]
+
+
+@pytest.mark.parametrize("B,N,D,Hq,Hkv,d,gain,dt", QKV_CASES)
+def test_qkv_proj_matches_oracle(B, N, D, Hq, Hkv, d, gain, dt):
+    print(f"qkv_proj B={B} N={N} D={D} Hq={Hq} Hkv={Hkv} d={d} gain={gain} {dt}", flush=True)
+    s = 1.0 / math.sqrt(D)
+    x = randn((B, N, D), 3000 + N, dtype=dt, device=DEV)
+    wq = randn((Hq * d, D), 3001, std=s, dtype=dt, device=DEV)
+    wk = randn((Hkv * d, D), 3002, std=s, dtype=dt, device=DEV) if Hkv else None
+    wv = randn((Hkv * d, D), 3003, std=s, dtype=dt, device=DEV) if Hkv else None
+    g = _gain(D, 3004, dt) if gain else None
+    q, k, v = yk.yoco_qkv_proj(x, wq, d, wk, wv, norm_w=g)
+    torch.cuda.synchronize()
+    g64 = None if g is None else to64(g)
+    rq, _ = oracle.global_kv_proj(to64(x), to64(wq), to64(wq), Hq, d, gamma=g64)
+    glue_check(to64(q), rq, dt, "q")
+    if Hkv:
+        rk, rv = oracle.global_kv_proj(to64(x), to64(wk), to64(wv), Hkv, d, gamma=g64)
+        glue_check(to64(k), rk, dt, "k")
+        glue_check(to64(v), rv, dt, "v")
+    else:
+        assert k is None and v is None
+
+
+SWIGLU_CASES = [
+    # B, N, D, F, gain, dtype
+    (1, 77, 256, 768, False, "f32"),
+    (2, 130, 384, 344, True, "bf16"),     # F not a multiple of the 64-feature tile
+    (1, 1, 128, 64, False, "bf16"),
+    (1, 257, 192, 520, True, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,N,D,F,gain,dt", SWIGLU_CASES)
+def test_swiglu_matches_oracle(B, N, D, F, gain, dt):
+    print(f"swiglu B={B} N={N} D={D} F={F} gain={gain} {dt}", flush=True)
+    s = 1.0 / math.sqrt(D)
+    x = randn((B, N, D), 3100 + N, dtype=dt, device=DEV)
+    wg = randn((F, D), 3101, std=s, dtype=dt, device=DEV)
+    wu = randn((F, D), 3102, std=s, dtype=dt, device=DEV)
+    g = _gain(D, 3103, dt) if gain else None
+    h = yk.yoco_swiglu(x, wg, wu, norm_w=g)
+    torch.cuda.synchronize()
+    xg, wg64, wu64 = to64(x), to64(wg), to64(wu)
+    g64 = None if g is None else to64(g)
+    ref = np.stack([np.stack([oracle.swiglu_hidden_row(xg[b, n], wg64, wu64, g64) for n in range(N)])
+                    for b in range(B)])
+    glue_check(to64(h), ref, dt, "swiglu h")
+
+
+RES_CASES = [
+    # B, N, K, F, a_heads, dtype
+    (1, 77, 256, 256, 4, "f32"),      # W_o over a head-major attention output (4 heads of 64)
+    (2, 130, 384, 192, 3, "bf16"),    # 3 heads of 128
+    (1, 200, 768, 256, 0, "f32"),     # W_down over row-major activations
+    (3, 1, 512, 128, 0, "bf16"),
+    (1, 300, 1024, 520, 0, "bf16"),   # F not a multiple of the 128-feature tile
+]
+
+
+@pytest.mark.parametrize("B,N,K,F,a_heads,dt", RES_CASES)
+def test_linear_residual_matches_oracle(B, N, K, F, a_heads, dt):
+    print(f"linear_residual B={B} N={N} K={K} F={F} heads={a_heads} {dt}", flush=True)
+    if a_heads:
+        a = randn((B, a_heads, N, K // a_heads), 3200 + N, dtype=dt, device=DEV)
+        rows = to64(a).transpose(0, 2, 1, 3).reshape(B, N, K)     # the concatenation over heads
+    else:
+        a = randn((B, N, K), 3200 + N, dtype=dt, device=DEV)
+        rows = to64(a)
+    w = randn((F, K), 3201, std=1.0 / math.sqrt(K), dtype=dt, device=DEV)
+    y = randn((B, N, F), 3202, dtype=dt, device=DEV)
+    y0 = to64(y)
+    yk.yoco_linear_residual(a, w, y, a_heads=a_heads)
+    torch.cuda.synchronize()
+    ref = y0 + oracle.linear_rows(rows, to64(w))
+    glue_check(to64(y), ref, dt, "y + a W^T")
+
+
+def test_linear_residual_accumulates_in_place_twice():
+    """Two residual products into the same stream add both terms."""
+    B, N, K, F = 1, 65, 256, 128
+    a1 = randn((B, N, K), 3301, dtype="f32", device=DEV)
+    a2 = randn((B, N, K), 3302, dtype="f32", device=DEV)
+    w = randn((F, K), 3303, std=1 / 16, dtype="f32", device=DEV)
+    y = randn((B, N, F), 3304, dtype="f32", device=DEV)
+    y0 = to64(y)
+    yk.yoco_linear_residual(a1, w, y)
+    yk.yoco_linear_residual(a2, w, y)
+    torch.cuda.synchronize()
+    ref = y0 + oracle.linear_rows(to64(a1), to64(w)) + oracle.linear_rows(to64(a2), to64(w))
+    glue_check(to64(y), ref, "f32", "two residual products")
+
+
+# ---------------------------------------------------------------- the whole block on the GPU
+def _params(wl, with_ffn=True):
+    D, Hq, Hkv, d, F = wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.ffn_dim
+    idx = iter(range(1, 1000))
+    dt = "f32" if wl.dtype == "f32" else "bf16"
+    r = lambda *shape, std=wl.weight_std: randn(shape, seed_for(wl.wid, next(idx)), std=std, dtype=dt,  # noqa: E731
+                                                device=DEV)
+    ffn = lambda: (r(F, D), r(F, D), r(D, F, std=wl.weight_std * math.sqrt(D / F)))  # noqa: E731
+    gp = dict(
+        swa=[(r(Hq * d, D), r(Hkv * d, D), r(Hkv * d, D), r(D, Hq * d)) for _ in range(wl.n_self_layers)],
+        glob=(r(Hkv * d, D), r(Hkv * d, D)),
+        cross=[(r(Hq * d, D), r(D, Hq * d)) for _ in range(wl.n_cross_layers)])
+    gp["swa_ffn"] = [ffn() for _ in range(wl.n_self_layers)] if with_ffn else []
+    gp["cross_ffn"] = [ffn() for _ in range(wl.n_cross_layers)] if with_ffn else []
+    c = lambda t: to64(t)  # noqa: E731
+    p = BlockParams(
+        n_heads=Hq, n_kv_heads=Hkv, head_dim=d, window=wl.window,
+        swa_wq=[c(w[0]) for w in gp["swa"]], swa_wk=[c(w[1]) for w in gp["swa"]],
+        swa_wv=[c(w[2]) for w in gp["swa"]], swa_wo=[c(w[3]) for w in gp["swa"]],
+        glob_wk=c(gp["glob"][0]), glob_wv=c(gp["glob"][1]),
+        cross_wq=[c(w[0]) for w in gp["cross"]], cross_wo=[c(w[1]) for w in gp["cross"]],
+        swa_ffn=[tuple(c(t) for t in f) for f in gp["swa_ffn"]],
+        cross_ffn=[tuple(c(t) for t in f) for f in gp["cross_ffn"]])
+    return gp, p
+
+
+def _gpu_ffn(x, f):
+    if f is not None:
+        h = yk.yoco_swiglu(x, f[0], f[1])
+        yk.yoco_linear_residual(h, f[2], x)
+
+
+def gpu_block(x, gp, wl, early_exit=False):
+    """The block on the GPU, x [B, N, D] updated in place; returns (x or its
+    last row after the cross layers, K, V)."""
+    Hq, Hkv, d, W = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    B, N, D = x.shape
+    for layer, (wq, wk, wv, wo) in enumerate(gp["swa"]):
+        q, k, v = yk.yoco_qkv_proj(x, wq, d, wk, wv)
+        o = yk.yoco_swa_attn(q, k, v, W)
+        yk.yoco_linear_residual(o, wo, x, a_heads=Hq)
+        _gpu_ffn(x, gp["swa_ffn"][layer] if gp["swa_ffn"] else None)
+    kc = torch.empty(B, Hkv, N, d, dtype=x.dtype, device=DEV)
+    vc = torch.empty_like(kc)
+    yk.yoco_global_kv_proj(x, gp["glob"][0], gp["glob"][1], kc, vc)
+    if early_exit:
+        last = x[:, N - 1:N].contiguous()
+        for layer, (wq, wo) in enumerate(gp["cross"]):
+            q, _, _ = yk.yoco_qkv_proj(last, wq, d)
+            o = yk.yoco_cross_attn_decode(q.reshape(B, Hq, d).contiguous(), kc, vc, N)
+            yk.yoco_linear_residual(o.reshape(B, Hq, 1, d), wo, last, a_heads=Hq)
+            _gpu_ffn(last, gp["cross_ffn"][layer] if gp["cross_ffn"] else None)
+        return last[:, 0], kc, vc
+    for layer, (wq, wo) in enumerate(gp["cross"]):
+        q, _, _ = yk.yoco_qkv_proj(x, wq, d)
+        o = yk.yoco_cross_attn_prefill(q, kc, vc)
+        yk.yoco_linear_residual(o, wo, x, a_heads=Hq)
+        _gpu_ffn(x, gp["cross_ffn"][layer] if gp["cross_ffn"] else None)
+    return x, kc, vc
+
+
+@pytest.mark.parametrize("with_ffn", [True, False])
+def test_tiny_block_wholly_on_gpu_matches_oracle(with_ffn):
+    wl = WORKLOADS["tiny_block_f32"]
+    print(f"tiny block on the GPU, ffn={with_ffn}", flush=True)
+    gp, p = _params(wl, with_ffn)
+    x = randn((wl.batch, wl.seq, wl.hidden), seed_for(wl.wid, 0), dtype="f32", device=DEV)
+    x64 = to64(x)
+    out, kc, vc = gpu_block(x.clone(), gp, wl)
+    last, _, _ = gpu_block(x.clone(), gp, wl, early_exit=True)
+    torch.cuda.synchronize()
+    ref, (rk, rv) = oracle.yoco_block(x64, p)
+    check(to64(kc), rk, "f32", "shared K")
+    check(to64(vc), rv, "f32", "shared V")
+    check(to64(out), ref, "f32", "block output")
+    ref_last, _ = oracle.yoco_block_early_exit(x64, p)
+    assert np.array_equal(ref_last, ref[:, -1])          # the oracle's own identity
+    check(to64(last), ref_last, "f32", "early-exit last row")
+
+
+def test_block_glue_at_the_3b_shape_sampled_rows():
+    """The 3B-shaped layer glue in the launch configuration the benchmark times
+    (D 3072, 24/8 heads of 128, N 4096, SwiGLU 8192), bf16, checked on
+    sampled tokens."""
+    wl = WORKLOADS["prefill_3b_bf16"]
+    B, N, D, Hq, Hkv, d, F = wl.batch, wl.seq, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.ffn_dim
+    x = randn((B, N, D), 3400, device=DEV)
+    wq = randn((Hq * d, D), 3401, std=wl.weight_std, device=DEV)
+    wk = randn((Hkv * d, D), 3402, std=wl.weight_std, device=DEV)
+    wv = randn((Hkv * d, D), 3403, std=wl.weight_std, device=DEV)
+    wo = randn((D, Hq * d), 3404, std=wl.weight_std, device=DEV)
+    wg = randn((F, D), 3405, std=wl.weight_std, device=DEV)
+    wu = randn((F, D), 3406, std=wl.weight_std, device=DEV)
+    wd = randn((D, F), 3407, std=wl.weight_std, device=DEV)
+    q, k, v = yk.yoco_qkv_proj(x, wq, d, wk, wv)
+    h = yk.yoco_swiglu(x, wg, wu)
+    y1 = x.clone()
+    yk.yoco_linear_residual(q, wo, y1, a_heads=Hq)
+    y2 = x.clone()
+    yk.yoco_linear_residual(h, wd, y2)
+    torch.cuda.synchronize()
+    rows = [0, 1, 127, 128, 2047, 3001, N - 1]
+    x64 = to64(x)[:, rows]
+    rq, _ = oracle.global_kv_proj(x64, to64(wq), to64(wq), Hq, d)
+    rk, rv = oracle.global_kv_proj(x64, to64(wk), to64(wv), Hkv, d)
+    glue_check(to64(q)[:, :, rows], rq, "bf16", "q (3B)")
+    glue_check(to64(k)[:, :, rows], rk, "bf16", "k (3B)")
+    glue_check(to64(v)[:, :, rows], rv, "bf16", "v (3B)")
+    wg64, wu64 = to64(wg), to64(wu)
+    rh = np.stack([oracle.swiglu_hidden_row(x64[0, i], wg64, wu64) for i in range(len(rows))])[None]
+    glue_check(to64(h)[:, rows], rh, "bf16", "swiglu h (3B)")
+    # the residual products, from the GPU's own q and h (bf16 inputs, exact in float64)
+    q_rows = to64(q)[:, :, rows].transpose(0, 2, 1, 3).reshape(B, len(rows), Hq * d)
+    glue_check(to64(y1)[:, rows], x64 + oracle.linear_rows(q_rows, to64(wo)), "bf16", "x + o W_o^T (3B)")
+    glue_check(to64(y2)[:, rows], x64 + oracle.linear_rows(to64(h)[:, rows], to64(wd)), "bf16", "x + h W_down^T (3B)")
