@@ -387,6 +387,143 @@ def run_gret(wl, dev, reps, decode_batch=16, chunk=256, tau=16.0):
     }
 
 
+# ---------------------------------------------------------------- whole block
+class BlockForward:
+    """The 3B-shaped YOCO block with every step on the GPU: per self-decoder
+    layer the pre-norm Q/K/V projection, sliding-window attention, the output
+    projection (residual) and the SwiGLU feed-forward (gate/up, then down with
+    the residual); the global KV projection; per cross-decoder layer the query
+    projection, causal cross attention over the shared cache, the output
+    projection and the feed-forward.  Early exit runs the cross-decoder for
+    the last position only."""
+
+    def __init__(self, wl, dev):
+        self.wl = wl
+        B, N, D, Hq, Hkv, d, F = wl.batch, wl.seq, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.ffn_dim
+        idx = iter(range(300, 1000))
+        r = lambda *shape, std=wl.weight_std: randn(shape, seed_for(wl.wid, next(idx)), std=std, device=dev)  # noqa: E731
+        ffn = lambda: (r(F, D), r(F, D), r(D, F, std=wl.weight_std * (D / F) ** 0.5))  # noqa: E731
+        self.x0 = randn((B, N, D), seed_for(wl.wid, 299), device=dev)
+        self.x = torch.empty_like(self.x0)
+        self.swa = [(r(Hq * d, D), r(Hkv * d, D), r(Hkv * d, D), r(D, Hq * d), ffn()) for _ in range(wl.n_self_layers)]
+        self.glob = (r(Hkv * d, D), r(Hkv * d, D))
+        self.cross = [(r(Hq * d, D), r(D, Hq * d), ffn()) for _ in range(wl.n_cross_layers)]
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.q = torch.empty(B, Hq, N, d, **bf)
+        self.k = torch.empty(B, Hkv, N, d, **bf)
+        self.v = torch.empty(B, Hkv, N, d, **bf)
+        self.o = torch.empty(B, Hq, N, d, **bf)
+        self.h = torch.empty(B, N, F, **bf)
+        self.kc = torch.empty(B, Hkv, N, d, **bf)
+        self.vc = torch.empty(B, Hkv, N, d, **bf)
+        self.last = torch.empty(B, 1, D, **bf)
+        self.q1 = torch.empty(B, Hq, 1, d, **bf)
+        self.o1 = torch.empty(B, Hq, d, **bf)
+        self.h1 = torch.empty(B, 1, F, **bf)
+        self.ws = torch.empty(yk.yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, N, d), dtype=torch.uint8,
+                              device=dev)
+        g = lambda m, n_, k: 2.0 * m * n_ * k  # noqa: E731
+        M = B * N
+        self.flops = {
+            "qkv_proj": wl.n_self_layers * g(M, (Hq + 2 * Hkv) * d, D) + wl.n_cross_layers * g(M, Hq * d, D),
+            "swa_attn": wl.n_self_layers * attn_flops(swa_pairs(N, wl.window), Hq, d, B),
+            "kv_proj": proj_flops(B, N, D, Hkv * d),
+            "cross_attn": wl.n_cross_layers * attn_flops(causal_pairs(N), Hq, d, B),
+            "out_proj": (wl.n_self_layers + wl.n_cross_layers) * g(M, D, Hq * d),
+            "swiglu": (wl.n_self_layers + wl.n_cross_layers) * g(M, 2 * F, D),
+            "down_proj": (wl.n_self_layers + wl.n_cross_layers) * g(M, D, F),
+        }
+        L_c = wl.n_cross_layers
+        self.flops_early_exit = (sum(v for k_, v in self.flops.items() if k_ != "cross_attn")
+                                 - L_c * (g(M - B, Hq * d, D) + g(M - B, D, Hq * d) + g(M - B, 2 * F, D)
+                                          + g(M - B, D, F))
+                                 + L_c * attn_flops(N, Hq, d, B))
+
+    def _t(self, ev, key, fn):
+        if ev is None:
+            fn()
+            return
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        ev.setdefault(key, []).append((s, e))
+
+    def run(self, early_exit=False, ev=None):
+        wl = self.wl
+        B, N, Hq, d = wl.batch, wl.seq, wl.n_heads, wl.head_dim
+        x = self.x
+        x.copy_(self.x0)
+        t = self._t
+        for wq, wk, wv, wo, (wg, wu, wd) in self.swa:
+            t(ev, "qkv_proj", lambda: yk.yoco_qkv_proj(x, wq, d, wk, wv, q_out=self.q, k_out=self.k, v_out=self.v))
+            t(ev, "swa_attn", lambda: yk.yoco_swa_attn(self.q, self.k, self.v, wl.window, o=self.o))
+            t(ev, "out_proj", lambda: yk.yoco_linear_residual(self.o, wo, x, a_heads=Hq))
+            t(ev, "swiglu", lambda: yk.yoco_swiglu(x, wg, wu, h=self.h))
+            t(ev, "down_proj", lambda: yk.yoco_linear_residual(self.h, wd, x))
+        t(ev, "kv_proj", lambda: yk.yoco_global_kv_proj(x, self.glob[0], self.glob[1], self.kc, self.vc))
+        if early_exit:
+            last = self.last
+            last.copy_(x[:, N - 1:N])
+            for wq, wo, (wg, wu, wd) in self.cross:
+                yk.yoco_qkv_proj(last, wq, d, q_out=self.q1)
+                yk.yoco_cross_attn_decode(self.q1.view(B, Hq, d), self.kc, self.vc, N, o=self.o1, workspace=self.ws)
+                yk.yoco_linear_residual(self.o1.view(B, Hq, 1, d), wo, last, a_heads=Hq)
+                yk.yoco_swiglu(last, wg, wu, h=self.h1)
+                yk.yoco_linear_residual(self.h1, wd, last)
+            return
+        for wq, wo, (wg, wu, wd) in self.cross:
+            t(ev, "qkv_proj", lambda: yk.yoco_qkv_proj(x, wq, d, q_out=self.q))
+            t(ev, "cross_attn", lambda: yk.yoco_cross_attn_prefill(self.q, self.kc, self.vc, o=self.o))
+            t(ev, "out_proj", lambda: yk.yoco_linear_residual(self.o, wo, x, a_heads=Hq))
+            t(ev, "swiglu", lambda: yk.yoco_swiglu(x, wg, wu, h=self.h))
+            t(ev, "down_proj", lambda: yk.yoco_linear_residual(self.h, wd, x))
+
+
+def run_block(wl, dev, steps):
+    blk = BlockForward(wl, dev)
+    res = {}
+    for mode in ("full", "early_exit"):
+        for _ in range(2):
+            blk.run(early_exit=mode == "early_exit")
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            blk.run(early_exit=mode == "early_exit")
+        b.record()
+        torch.cuda.synchronize()
+        res[mode] = events_ms([(a, b)])[0] / steps
+    ev = {}
+    blk.run(ev=ev)
+    torch.cuda.synchronize()
+    parts = {}
+    for key, pairs in ev.items():
+        ms = sum(events_ms(pairs))
+        tf = blk.flops[key] / (ms * 1e-3) / 1e12
+        parts[key] = {"ms": ms, "calls": len(pairs), "TFLOP/s": tf, "frac_mfma_peak": tf / BF16_PEAK_TFLOPS}
+    total = sum(blk.flops.values())
+    tokens = wl.batch * wl.seq
+    out = {
+        "workload": wl.name,
+        "config": {"batch": wl.batch, "seq_len": wl.seq, "hidden": wl.hidden, "q_heads": wl.n_heads,
+                   "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "ffn_dim": wl.ffn_dim,
+                   "self_layers": wl.n_self_layers, "cross_layers": wl.n_cross_layers, "window": wl.window},
+        "ms_per_forward": res["full"],
+        "tokens_per_s": tokens / (res["full"] * 1e-3),
+        "TFLOP/s": total / (res["full"] * 1e-3) / 1e12,
+        "flops_per_forward": total,
+        "parts": parts,
+        "early_exit": {"ms_per_prefill": res["early_exit"], "tokens_per_s": tokens / (res["early_exit"] * 1e-3),
+                       "TFLOP/s": blk.flops_early_exit / (res["early_exit"] * 1e-3) / 1e12,
+                       "speedup_vs_full": res["full"] / res["early_exit"]},
+        "timing": ("HIP events around back-to-back forwards (the input copy included); parts: events around "
+                   "each call of one forward"),
+    }
+    del blk
+    return out
+
+
 # ---------------------------------------------------------------- early exit
 def run_early_exit(wl, dev, steps):
     """1M-token early-exit prefill: L_s SWA layers over all tokens, the global
@@ -481,6 +618,8 @@ def main():
     ap.add_argument("--extra-steps", type=int, default=3, help="steps of the 1M early-exit flow")
     ap.add_argument("--no-generation", action="store_true", help="skip the one-token generation step measurement")
     ap.add_argument("--no-gret", action="store_true", help="skip the gated-retention measurement")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the whole-block measurement (3B shape with all layer glue on the GPU)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -569,6 +708,9 @@ def main():
     if not args.no_generation:
         wg = WORKLOADS["generation_32k_bf16"]
         out["generation"] = run_generation(wg, dev, wg.decode_steps)
+        torch.cuda.empty_cache()
+    if not args.no_block:
+        out["block_prefill"] = run_block(wl, dev, 3)
         torch.cuda.empty_cache()
     if not args.no_gret:
         out["gated_retention"] = run_gret(WORKLOADS["gret_3b_bf16"], dev, 50)
