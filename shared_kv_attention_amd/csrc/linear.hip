@@ -13,12 +13,16 @@
 //            concatenation over heads of a head-major [B, H, N, K/H] tensor
 //            (the attention output feeding W_o).
 //
-// Design (MI355X-first), one kernel template for the three forms:
-//  * C^T = W X^T on 32x32x16 bf16 MFMA (32x32x2 f32 for float32): 128
-//    features x 128 tokens per 256-thread workgroup, 4 waves of 64 x 64, k in
-//    stages of 128 bytes per row, double-buffered LDS in distinct objects with
-//    XOR-swizzled 16-byte chunks.  Each lane's results are 4 consecutive
-//    features of one token, so every epilogue stores 4 contiguous values.
+// Design (MI355X-first), one kernel template per tile shape for the three forms:
+//  * C^T = W X^T on 32x32x16 bf16 MFMA (32x32x2 f32 for float32).  Each
+//    lane's results are 4 consecutive features of one token, so every
+//    epilogue stores 4 contiguous values.
+//  * bf16 with at least 512 tokens: the wide tile further below (256 x 256,
+//    4 waves of 128 x 128, a 4-stage ring of direct loads).  float32, and
+//    bf16 with fewer tokens (one-token decode steps, where a wide tile would
+//    leave most of the chip idle): 128 features x 128 tokens per 256-thread
+//    workgroup, 4 waves of 64 x 64, k in stages of 128 bytes per row,
+//    double-buffered LDS in distinct objects with XOR-swizzled 16-byte chunks.
 //  * W tiles go global -> LDS directly; X passes through registers, where the
 //    RMSNorm sum of squares is taken from the values being moved (X is read
 //    once) and the row factor is applied to the float32 accumulator.  The
@@ -101,7 +105,9 @@ __device__ __forceinline__ u32x4 lin_gain(u32x4 w, u32x4 gw) {
   return r;
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.f + __expf(-z)); }
+// z * sigmoid(z); the fast division is exact enough for float32 and bf16 outputs
+// (a denominator that overflows gives 0, the limit for z -> -inf)
+__device__ __forceinline__ float silu_f32(float z) { return __fdividef(z, 1.f + __expf(-z)); }
 
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float v0, float v1, float v2, float v3) {
@@ -319,13 +325,327 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 form with a wide tile: 256 weight rows x 256 tokens per workgroup, 4
+// waves of 128 x 128 (a 4 x 4 block of 32x32 MFMA tiles, the accumulators in
+// the matrix-core register file), k in stages of 32 through a 4-stage LDS
+// ring filled by direct global -> LDS loads three stages ahead.  Per k step a
+// wave reads 8 fragments for 16 MFMAs (0.5 KB of LDS per MFMA, half the 64 x 64
+// tile's), and the loads in flight cover the HBM latency.  The RMSNorm sums of
+// squares are taken from the staged token rows in LDS; a norm gain is staged
+// with each k slice and applied to the token fragments in registers (x * gamma
+// rounded to bf16, as in the 128 x 128 form).
+// ---------------------------------------------------------------------------
+namespace wide {
+constexpr int TM = 256;                 // weight rows per tile
+constexpr int TN = 256;                 // tokens per tile
+constexpr int BK = 32;                  // k per stage: 64 bytes per row
+constexpr int NST = 4;                  // ring stages
+constexpr int OPB = 256 * 64;           // one operand of one stage (bytes)
+constexpr int GB = 256;                 // per-wave gain slice of one stage (64 bytes used)
+constexpr int STB = 2 * OPB + 4 * GB;   // one stage
+}  // namespace wide
+
+// 16-byte chunk swizzle for 64-byte rows: rows r, r+4, r+8, r+12 (which share
+// a group of banks) hold a given chunk at four different positions.
+__device__ __forceinline__ int wswz(int row) { return (row >> 2) & 3; }
+
+__device__ __forceinline__ bf16x8 wide_frag(const char* op, int row, int kc, int g) {
+  return *reinterpret_cast<const bf16x8*>(op + row * 64 + (((2 * kc + g) ^ wswz(row)) << 4));
+}
+
+// One direct global -> LDS load of 16 bytes per lane: lane l writes LDS bytes
+// [m0 + 16 l, m0 + 16 l + 16).  Written in inline assembly so that the
+// compiler's wait insertion does not drain the ring before every LDS read (it
+// cannot tell the four stages apart); the ring's waits are explicit.
+__device__ __forceinline__ void dma16(const void* src, unsigned m0) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(m0)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, unsigned m0) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(m0)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int MODE, bool GAIN>
+__global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
+  using namespace wide;
+  extern __shared__ __attribute__((aligned(16))) char ring[];   // NST * STB bytes, then rs[256]
+  float* rs_lds = reinterpret_cast<float*>(ring + NST * STB);
+  constexpr bool NORM = MODE != kLinResidual;
+  constexpr int PER = 8 + (GAIN ? 1 : 0);   // loads per thread per stage
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, r32 = l & 31;
+  const int wf = w >> 1, wt = w & 1;
+  const int M = a.B * a.N;
+  constexpr int FPT = MODE == kLinSwiGLU ? 128 : 256;   // output features per tile
+  const int nft = (a.F + FPT - 1) / FPT;
+  const int id = blockIdx.x;
+  int tt, ft;
+  if (nft % 8 == 0) {
+    const int per = nft / 8, xcd = id & 7, sl = id >> 3;
+    ft = xcd * per + sl % per;
+    tt = sl / per;
+  } else {
+    ft = id % nft;
+    tt = id / nft;
+  }
+  const int t0 = tt * TN;
+
+  // staging addresses: slot P = 256 r + tid of an operand holds row P / 4 at
+  // physical chunk P % 4 (logical chunk (P % 4) ^ wswz(row)); rows past the
+  // end are clamped (finite data, never stored)
+  const char* wsrc[4];
+  const char* xsrc[4];
+  const int dh = a.x_heads > 0 ? a.K / a.x_heads : a.K;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int slot = 256 * r + tid;
+    const int row = slot >> 2, lch = (slot & 3) ^ wswz(row);
+    const void* wm;
+    int fr;
+    if constexpr (MODE == kLinSwiGLU) {
+      const int blk = (row >> 5) & 3;
+      fr = min(ft * 128 + (row >> 7) * 64 + (blk >> 1) * 32 + (row & 31), a.F - 1);
+      wm = (blk & 1) ? a.w1 : a.w0;
+    } else {
+      const int f = min(ft * TM + row, a.F - 1);
+      if (MODE == kLinQKV && f >= a.f2) { wm = a.w2; fr = f - a.f2; }
+      else if (MODE == kLinQKV && f >= a.f1) { wm = a.w1; fr = f - a.f1; }
+      else { wm = a.w0; fr = f; }
+    }
+    wsrc[r] = static_cast<const char*>(wm) + (size_t)fr * a.K * 2 + lch * 16;
+    const int trow = min(t0 + row, M - 1);
+    if (a.x_heads > 0) {
+      const int bb = trow / a.N, n = trow % a.N;
+      xsrc[r] = static_cast<const char*>(a.x) + ((size_t)bb * a.x_heads * a.N + n) * dh * 2 + lch * 16;
+    } else {
+      xsrc[r] = static_cast<const char*>(a.x) + (size_t)trow * a.K * 2 + lch * 16;
+    }
+  }
+  const unsigned ring_base = (unsigned)(uintptr_t)ring;
+  const int nks = a.K / BK;
+  auto issue = [&](int ks) {
+    const unsigned sb = ring_base + (unsigned)((ks & (NST - 1)) * STB);
+    const size_t wo = (size_t)ks * BK * 2;
+    size_t xo = wo;
+    if (a.x_heads > 0) {
+      const int k0 = ks * BK, h = k0 / dh, c0 = k0 % dh;
+      xo = ((size_t)h * a.N * dh + c0) * 2;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (unsigned)((256 * r + 64 * w) * 16));
+      dma16(wsrc[r] + wo, m0);
+      dma16(xsrc[r] + xo, m0 + OPB);
+    }
+    if constexpr (GAIN) {
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (unsigned)(2 * OPB + w * GB));
+      dma4(static_cast<const char*>(a.norm_w) + wo + 4 * min(l, 15), m0);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  float ss = 0.f;
+
+  // Fragments of one k step (16 deep) of a stage: 4 weight rows blocks, 4 token blocks.
+  struct Frags {
+    bf16x8 a[4], b[4];
+  };
+  auto read_frags = [&](int ks, int kc, Frags& f) __attribute__((always_inline)) {
+    const char* S = ring + (ks & (NST - 1)) * STB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = wide_frag(S, wf * 128 + i * 32 + r32, kc, g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = wide_frag(S + OPB, wt * 128 + j * 32 + r32, kc, g);
+    if constexpr (GAIN) {
+      const bf16x8 gm = *reinterpret_cast<const bf16x8*>(S + 2 * OPB + w * GB + (kc * 16 + 8 * g) * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f.b[j][e] = (bf16)((float)f.b[j][e] * (float)gm[e]);
+    }
+  };
+  auto mma_frags = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma32(f.a[i], f.b[j], acc[i][j]);
+  };
+  // stage ks has landed (in every wave) once at most min(2, nks - 1 - ks)
+  // later stages are in flight and the waves have met
+  auto landed = [&](int ks) __attribute__((always_inline)) {
+    const int ahead = min(2, nks - 1 - ks);
+    if (ahead == 2) vm_wait<2 * PER>();
+    else if (ahead == 1) vm_wait<PER>();
+    else vm_wait<0>();
+    lds_barrier();
+  };
+
+  // Pipeline: the fragments of the next k step are read while the current
+  // one's 16 MFMAs run; the wait for the next stage (and the refill of the
+  // slot every wave has finished reading) sits between a stage's two k steps.
+  issue(0);
+  if (nks > 1) issue(1);
+  if (nks > 2) issue(2);
+  auto norm_sums = [&](int ks) __attribute__((always_inline)) {
+    if constexpr (NORM) {
+      const char* Xt = ring + (ks & (NST - 1)) * STB + OPB;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Xt + tid * 64 + ((c ^ wswz(tid)) << 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wi = v[i];
+          const bf16x2 x = __builtin_bit_cast(bf16x2, wi);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+        }
+      }
+    }
+  };
+  landed(0);
+  Frags f0, f1;
+  read_frags(0, 0, f0);
+  // the last stage is peeled off so that the loop body has no join of LDS
+  // read streams (a join makes the compiler drain the prefetched fragments)
+  // (the scheduling groups alternate MFMAs with the next block's LDS reads,
+  // one read per MFMA, so the reads neither queue up in bursts nor leave the
+  // matrix core idle; the waits before a block's first MFMA cover only the
+  // older fragments)
+  constexpr int NR = NORM ? 12 : 8;
+  for (int ks = 0; ks + 1 < nks; ++ks) {
+    read_frags(ks, 1, f1);
+    norm_sums(ks);
+    mma_frags(f0);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16 - NR, 0);
+    landed(ks + 1);                     // also: every wave is done with stage ks - 1
+    if (ks + 3 < nks) issue(ks + 3);    // into the slot of stage ks - 1
+    read_frags(ks + 1, 0, f0);
+    mma_frags(f1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+  }
+  read_frags(nks - 1, 1, f1);
+  mma_frags(f0);
+  norm_sums(nks - 1);
+  mma_frags(f1);
+
+  if constexpr (NORM) {
+    rs_lds[tid] = 1.0f / sqrtf(ss / (float)a.K + a.eps);   // thread tid staged token t0 + tid
+    lds_barrier();
+  }
+
+  // acc[i][j][e] = C^T[tile row wf*128 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*128 + j*32 + r32]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tl = wt * 128 + j * 32 + r32;
+    const int tok = t0 + tl;
+    if (tok >= M) continue;
+    const float rs = NORM ? rs_lds[tl] : 1.f;
+    const int bb = tok / a.N, n = tok % a.N;
+    if constexpr (MODE == kLinSwiGLU) {
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int hf = ft * 128 + wf * 64 + (i >> 1) * 32 + 8 * qd + 4 * g;
+          if (hf >= a.F) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = silu_f32(acc[i][j][4 * qd + e] * rs) * (acc[i + 1][j][4 * qd + e] * rs);
+          store4<bf16>(static_cast<bf16*>(a.y0) + (size_t)tok * a.F + hf, v[0], v[1], v[2], v[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const int f = ft * TM + wf * 128 + i * 32 + 8 * qd + 4 * g;
+          if (f >= a.F) continue;
+          const float v0 = acc[i][j][4 * qd] * rs, v1 = acc[i][j][4 * qd + 1] * rs;
+          const float v2 = acc[i][j][4 * qd + 2] * rs, v3 = acc[i][j][4 * qd + 3] * rs;
+          if constexpr (MODE == kLinQKV) {
+            void* out;
+            int fr, H;
+            if (f >= a.f2) { out = a.y2; fr = f - a.f2; H = a.h1; }
+            else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; }
+            else { out = a.y0; fr = f; H = a.h0; }
+            const int hh = fr / a.d, c = fr % a.d;
+            store4<bf16>(static_cast<bf16*>(out) + ((size_t)(bb * H + hh) * a.N + n) * a.d + c, v0, v1, v2, v3);
+          } else {
+            bf16* dst = static_cast<bf16*>(a.y0) + (size_t)tok * a.F + f;
+            const f32x4 old = load4<bf16>(dst);
+            store4<bf16>(dst, old[0] + v0, old[1] + v1, old[2] + v2, old[3] + v3);
+          }
+        }
+      }
+    }
+  }
+}
+
+constexpr int kWideLds = wide::NST * wide::STB + 256 * 4;
+
 hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t stream) {
   const int M = a.B * a.N;
+  if (is_bf16 && M >= 512) {
+    const int fpt = mode == kLinSwiGLU ? 128 : 256;
+    const long long tiles = (long long)((M + 255) / 256) * ((a.F + fpt - 1) / fpt);
+    const dim3 grid((unsigned)tiles);
+    const bool gain = mode != kLinResidual && a.norm_w != nullptr;
+#define YOCO_WIDE(MD, G)                                                                             \
+  do {                                                                                               \
+    static bool attr_set = false;                                                                     \
+    if (!attr_set) {                                                                                  \
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_wide_kernel<MD, G>),            \
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);                       \
+      attr_set = true;                                                                                \
+    }                                                                                                 \
+    hipLaunchKernelGGL((linear_wide_kernel<MD, G>), grid, dim3(256), kWideLds, stream, a);            \
+  } while (0)
+    if (mode == kLinQKV) { if (gain) YOCO_WIDE(kLinQKV, true); else YOCO_WIDE(kLinQKV, false); }
+    else if (mode == kLinSwiGLU) { if (gain) YOCO_WIDE(kLinSwiGLU, true); else YOCO_WIDE(kLinSwiGLU, false); }
+    else YOCO_WIDE(kLinResidual, false);
+#undef YOCO_WIDE
+    return hipGetLastError();
+  }
   const int fpt = mode == kLinSwiGLU ? 64 : 128;
   const long long tiles = (long long)((M + 127) / 128) * ((a.F + fpt - 1) / fpt);
   const dim3 grid((unsigned)tiles);
 #define YOCO_LIN(T, MD) hipLaunchKernelGGL((linear_kernel<T, MD>), grid, dim3(256), 0, stream, a)
-  if (is_bf16) {
+  if (is_bf16) {   // fewer than 512 tokens: the 128 x 128 tile keeps more workgroups busy
     if (mode == kLinQKV) YOCO_LIN(bf16, kLinQKV);
     else if (mode == kLinSwiGLU) YOCO_LIN(bf16, kLinSwiGLU);
     else YOCO_LIN(bf16, kLinResidual);
