@@ -63,12 +63,13 @@ struct LinArgs {
   const void* w1;      // QKV: W_k (or null); SwiGLU: W_up
   const void* w2;      // QKV: W_v (or null)
   void* y0;            // QKV: q [B, h0, N, d]; SwiGLU: h [B*N, F]; residual: y [B*N, F] (+=)
-  void* y1;            // QKV: k [B, h1, N, d]
-  void* y2;            // QKV: v [B, h1, N, d]
+  void* y1;            // QKV: k [B, h1, kv_rows, d], rows [kv_pos0, kv_pos0 + N)
+  void* y2;            // QKV: v [B, h1, kv_rows, d], likewise
   int B, N, K, F;      // F: output features (QKV: (h0 + 2 h1) d; SwiGLU: hidden size)
   int x_heads;         // 0 or the head count of a head-major x
   int f1, f2;          // QKV: first k feature, first v feature (F when absent)
   int h0, h1, d;       // QKV: q heads, k/v heads, head dim
+  int kv_rows, kv_pos0;  // QKV: rows per head of the k/v buffers, first row written
   int norm;            // fused RMSNorm of the x rows (QKV, SwiGLU)
   float eps;
 };

@@ -309,11 +309,12 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
           if constexpr (MODE == kLinQKV) {
             void* out;
             int fr, H;
-            if (f >= a.f2) { out = a.y2; fr = f - a.f2; H = a.h1; }
-            else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; }
+            size_t rows = (size_t)a.N, row0 = 0;
+            if (f >= a.f2) { out = a.y2; fr = f - a.f2; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
+            else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
             else { out = a.y0; fr = f; H = a.h0; }
             const int hh = fr / a.d, c = fr % a.d;
-            store4<T>(static_cast<T*>(out) + ((size_t)(bb * H + hh) * a.N + n) * a.d + c, v0, v1, v2, v3);
+            store4<T>(static_cast<T*>(out) + (((size_t)bb * H + hh) * rows + row0 + n) * a.d + c, v0, v1, v2, v3);
           } else {
             T* dst = static_cast<T*>(a.y0) + (size_t)tok * a.F + f;
             const f32x4 old = load4<T>(dst);
@@ -338,12 +339,14 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
 // ---------------------------------------------------------------------------
 namespace wide {
 constexpr int TM = 256;                 // weight rows per tile
-constexpr int TN = 256;                 // tokens per tile
 constexpr int BK = 32;                  // k per stage: 64 bytes per row
 constexpr int NST = 4;                  // ring stages
-constexpr int OPB = 256 * 64;           // one operand of one stage (bytes)
+constexpr int OPW = 256 * 64;           // the weight operand of one stage (bytes)
 constexpr int GB = 256;                 // per-wave gain slice of one stage (64 bytes used)
-constexpr int STB = 2 * OPB + 4 * GB;   // one stage
+template <int TN>
+constexpr int stage_bytes() { return OPW + TN * 64 + 4 * GB; }
+template <int TN>
+constexpr int lds_bytes() { return NST * stage_bytes<TN>() + 512 * 4; }   // ring, then rs[256], ssp[256]
 }  // namespace wide
 
 // 16-byte chunk swizzle for 64-byte rows: rows r, r+4, r+8, r+12 (which share
@@ -384,13 +387,20 @@ template <int N>
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int MODE, bool GAIN>
+// TN tokens per tile (256, or 128 when that keeps more of the chip busy):
+// 4 waves as 2 (weight-row halves of 128) x 2 (token halves of TN / 2).
+template <int MODE, bool GAIN, int TN>
 __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   using namespace wide;
-  extern __shared__ __attribute__((aligned(16))) char ring[];   // NST * STB bytes, then rs[256]
+  constexpr int STB = stage_bytes<TN>();
+  constexpr int NJ = TN / 64;             // 32-token blocks per wave
+  constexpr int XR = TN / 64;             // token-operand loads per thread per stage
+  constexpr int TPT = 256 / TN;           // threads per token for the norm sums
+  extern __shared__ __attribute__((aligned(16))) char ring[];
   float* rs_lds = reinterpret_cast<float*>(ring + NST * STB);
+  float* ssp_lds = rs_lds + 256;
   constexpr bool NORM = MODE != kLinResidual;
-  constexpr int PER = 8 + (GAIN ? 1 : 0);   // loads per thread per stage
+  constexpr int PER = 4 + XR + (GAIN ? 1 : 0);   // loads per thread per stage
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, r32 = l & 31;
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   // physical chunk P % 4 (logical chunk (P % 4) ^ wswz(row)); rows past the
   // end are clamped (finite data, never stored)
   const char* wsrc[4];
-  const char* xsrc[4];
+  const char* xsrc[XR];
   const int dh = a.x_heads > 0 ? a.K / a.x_heads : a.K;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -433,12 +443,14 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
       else { wm = a.w0; fr = f; }
     }
     wsrc[r] = static_cast<const char*>(wm) + (size_t)fr * a.K * 2 + lch * 16;
-    const int trow = min(t0 + row, M - 1);
-    if (a.x_heads > 0) {
-      const int bb = trow / a.N, n = trow % a.N;
-      xsrc[r] = static_cast<const char*>(a.x) + ((size_t)bb * a.x_heads * a.N + n) * dh * 2 + lch * 16;
-    } else {
-      xsrc[r] = static_cast<const char*>(a.x) + (size_t)trow * a.K * 2 + lch * 16;
+    if (r < XR) {
+      const int trow = min(t0 + row, M - 1);
+      if (a.x_heads > 0) {
+        const int bb = trow / a.N, n = trow % a.N;
+        xsrc[r] = static_cast<const char*>(a.x) + ((size_t)bb * a.x_heads * a.N + n) * dh * 2 + lch * 16;
+      } else {
+        xsrc[r] = static_cast<const char*>(a.x) + (size_t)trow * a.K * 2 + lch * 16;
+      }
     }
   }
   const unsigned ring_base = (unsigned)(uintptr_t)ring;
@@ -455,35 +467,35 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
     for (int r = 0; r < 4; ++r) {
       const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (unsigned)((256 * r + 64 * w) * 16));
       dma16(wsrc[r] + wo, m0);
-      dma16(xsrc[r] + xo, m0 + OPB);
+      if (r < XR) dma16(xsrc[r] + xo, m0 + OPW);
     }
     if constexpr (GAIN) {
-      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (unsigned)(2 * OPB + w * GB));
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (unsigned)(OPW + TN * 64 + w * GB));
       dma4(static_cast<const char*>(a.norm_w) + wo + 4 * min(l, 15), m0);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
   float ss = 0.f;
 
-  // Fragments of one k step (16 deep) of a stage: 4 weight rows blocks, 4 token blocks.
+  // Fragments of one k step (16 deep) of a stage: 4 weight-row blocks, NJ token blocks.
   struct Frags {
-    bf16x8 a[4], b[4];
+    bf16x8 a[4], b[NJ];
   };
   auto read_frags = [&](int ks, int kc, Frags& f) __attribute__((always_inline)) {
     const char* S = ring + (ks & (NST - 1)) * STB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.a[i] = wide_frag(S, wf * 128 + i * 32 + r32, kc, g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = wide_frag(S + OPB, wt * 128 + j * 32 + r32, kc, g);
+    for (int j = 0; j < NJ; ++j) f.b[j] = wide_frag(S + OPW, wt * (TN / 2) + j * 32 + r32, kc, g);
     if constexpr (GAIN) {
-      const bf16x8 gm = *reinterpret_cast<const bf16x8*>(S + 2 * OPB + w * GB + (kc * 16 + 8 * g) * 2);
+      const bf16x8 gm = *reinterpret_cast<const bf16x8*>(S + OPW + TN * 64 + w * GB + (kc * 16 + 8 * g) * 2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e) f.b[j][e] = (bf16)((float)f.b[j][e] * (float)gm[e]);
     }
@@ -492,7 +504,7 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma32(f.a[i], f.b[j], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mma32(f.a[i], f.b[j], acc[i][j]);
   };
   // stage ks has landed (in every wave) once at most min(2, nks - 1 - ks)
   // later stages are in flight and the waves have met
@@ -503,19 +515,15 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
     else vm_wait<0>();
     lds_barrier();
   };
-
-  // Pipeline: the fragments of the next k step are read while the current
-  // one's 16 MFMAs run; the wait for the next stage (and the refill of the
-  // slot every wave has finished reading) sits between a stage's two k steps.
-  issue(0);
-  if (nks > 1) issue(1);
-  if (nks > 2) issue(2);
+  // sums of squares of the staged token rows: token tid % TN, chunks of part tid / TN
   auto norm_sums = [&](int ks) __attribute__((always_inline)) {
     if constexpr (NORM) {
-      const char* Xt = ring + (ks & (NST - 1)) * STB + OPB;
+      const char* Xt = ring + (ks & (NST - 1)) * STB + OPW;
+      const int tk = tid % TN, part = tid / TN;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(Xt + tid * 64 + ((c ^ wswz(tid)) << 4));
+      for (int cc = 0; cc < 4 / TPT; ++cc) {
+        const int c = part * (4 / TPT) + cc;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(Xt + tk * 64 + ((c ^ wswz(tk)) << 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t wi = v[i];
@@ -525,36 +533,45 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
       }
     }
   };
+
+  // Pipeline: the fragments of the next k step are read while the current
+  // one's MFMAs run; the wait for the next stage (and the refill of the slot
+  // every wave has finished reading) sits between a stage's two k steps.  The
+  // last stage is peeled off so that the loop body has no join of LDS read
+  // streams (a join makes the compiler drain the prefetched fragments).  The
+  // scheduling groups alternate MFMAs with the next block's LDS reads, one
+  // read per MFMA, so the reads neither queue up in bursts nor leave the
+  // matrix core idle.
+  issue(0);
+  if (nks > 1) issue(1);
+  if (nks > 2) issue(2);
   landed(0);
   Frags f0, f1;
   read_frags(0, 0, f0);
-  // the last stage is peeled off so that the loop body has no join of LDS
-  // read streams (a join makes the compiler drain the prefetched fragments)
-  // (the scheduling groups alternate MFMAs with the next block's LDS reads,
-  // one read per MFMA, so the reads neither queue up in bursts nor leave the
-  // matrix core idle; the waits before a block's first MFMA cover only the
-  // older fragments)
-  constexpr int NR = NORM ? 12 : 8;
+  constexpr int NM = 4 * NJ;                                 // MFMAs per k step
+  constexpr int NR0 = 4 + NJ + (NORM ? 4 / TPT : 0);         // LDS reads in the first half
+  constexpr int NR1 = 4 + NJ;
+  static_assert(NR0 <= NM && NR1 <= NM, "one read per MFMA");
   for (int ks = 0; ks + 1 < nks; ++ks) {
     read_frags(ks, 1, f1);
     norm_sums(ks);
     mma_frags(f0);
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
+    for (int q = 0; q < NR0; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16 - NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR0, 0);
     landed(ks + 1);                     // also: every wave is done with stage ks - 1
     if (ks + 3 < nks) issue(ks + 3);    // into the slot of stage ks - 1
     read_frags(ks + 1, 0, f0);
     mma_frags(f1);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NR1; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR1, 1);
   }
   read_frags(nks - 1, 1, f1);
   mma_frags(f0);
@@ -562,14 +579,21 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   mma_frags(f1);
 
   if constexpr (NORM) {
-    rs_lds[tid] = 1.0f / sqrtf(ss / (float)a.K + a.eps);   // thread tid staged token t0 + tid
+    ssp_lds[tid] = ss;
+    lds_barrier();
+    if (tid < TN) {
+      float t = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < TPT; ++pp) t += ssp_lds[pp * TN + tid];
+      rs_lds[tid] = 1.0f / sqrtf(t / (float)a.K + a.eps);
+    }
     lds_barrier();
   }
 
-  // acc[i][j][e] = C^T[tile row wf*128 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*128 + j*32 + r32]
+  // acc[i][j][e] = C^T[tile row wf*128 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*TN/2 + j*32 + r32]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tl = wt * 128 + j * 32 + r32;
+  for (int j = 0; j < NJ; ++j) {
+    const int tl = wt * (TN / 2) + j * 32 + r32;
     const int tok = t0 + tl;
     if (tok >= M) continue;
     const float rs = NORM ? rs_lds[tl] : 1.f;
@@ -600,11 +624,12 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
           if constexpr (MODE == kLinQKV) {
             void* out;
             int fr, H;
-            if (f >= a.f2) { out = a.y2; fr = f - a.f2; H = a.h1; }
-            else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; }
+            size_t rows = (size_t)a.N, row0 = 0;
+            if (f >= a.f2) { out = a.y2; fr = f - a.f2; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
+            else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
             else { out = a.y0; fr = f; H = a.h0; }
             const int hh = fr / a.d, c = fr % a.d;
-            store4<bf16>(static_cast<bf16*>(out) + ((size_t)(bb * H + hh) * a.N + n) * a.d + c, v0, v1, v2, v3);
+            store4<bf16>(static_cast<bf16*>(out) + (((size_t)bb * H + hh) * rows + row0 + n) * a.d + c, v0, v1, v2, v3);
           } else {
             bf16* dst = static_cast<bf16*>(a.y0) + (size_t)tok * a.F + f;
             const f32x4 old = load4<bf16>(dst);
@@ -616,36 +641,61 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   }
 }
 
-constexpr int kWideLds = wide::NST * wide::STB + 256 * 4;
+// Number of compute units (queried once per process; every GPU it runs on is
+// the same model).
+static int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <int MODE, bool GAIN, int TN>
+static void launch_wide(const LinArgs& a, long long tiles, hipStream_t stream) {
+  constexpr int lds = wide::lds_bytes<TN>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_wide_kernel<MODE, GAIN, TN>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((linear_wide_kernel<MODE, GAIN, TN>), dim3((unsigned)tiles), dim3(256), lds, stream, a);
+}
+
+template <int MODE, bool GAIN>
+static void launch_wide_tn(const LinArgs& a, hipStream_t stream) {
+  // tokens per tile: the one that leaves fewer compute units idle in the last
+  // round of workgroups (one workgroup per CU), the narrower tile counted at
+  // 0.9 of the wide one's rate (it reads 1.5x the LDS bytes per MFMA)
+  const int M = a.B * a.N, cus = cu_count();
+  constexpr int FPT = MODE == kLinSwiGLU ? 128 : 256;
+  const long long nft = (a.F + FPT - 1) / FPT;
+  const long long t256 = (long long)((M + 255) / 256) * nft, t128 = (long long)((M + 127) / 128) * nft;
+  auto eff = [&](long long t, double rate) { return rate * (double)t / (double)(((t + cus - 1) / cus) * cus); };
+  if (eff(t256, 1.0) >= eff(t128, 0.9)) launch_wide<MODE, GAIN, 256>(a, t256, stream);
+  else launch_wide<MODE, GAIN, 128>(a, t128, stream);
+}
 
 hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t stream) {
   const int M = a.B * a.N;
-  if (is_bf16 && M >= 512) {
-    const int fpt = mode == kLinSwiGLU ? 128 : 256;
-    const long long tiles = (long long)((M + 255) / 256) * ((a.F + fpt - 1) / fpt);
-    const dim3 grid((unsigned)tiles);
+  if (is_bf16 && M >= 256) {
     const bool gain = mode != kLinResidual && a.norm_w != nullptr;
-#define YOCO_WIDE(MD, G)                                                                             \
-  do {                                                                                               \
-    static bool attr_set = false;                                                                     \
-    if (!attr_set) {                                                                                  \
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_wide_kernel<MD, G>),            \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);                       \
-      attr_set = true;                                                                                \
-    }                                                                                                 \
-    hipLaunchKernelGGL((linear_wide_kernel<MD, G>), grid, dim3(256), kWideLds, stream, a);            \
-  } while (0)
-    if (mode == kLinQKV) { if (gain) YOCO_WIDE(kLinQKV, true); else YOCO_WIDE(kLinQKV, false); }
-    else if (mode == kLinSwiGLU) { if (gain) YOCO_WIDE(kLinSwiGLU, true); else YOCO_WIDE(kLinSwiGLU, false); }
-    else YOCO_WIDE(kLinResidual, false);
-#undef YOCO_WIDE
+    if (mode == kLinQKV) { if (gain) launch_wide_tn<kLinQKV, true>(a, stream); else launch_wide_tn<kLinQKV, false>(a, stream); }
+    else if (mode == kLinSwiGLU) { if (gain) launch_wide_tn<kLinSwiGLU, true>(a, stream); else launch_wide_tn<kLinSwiGLU, false>(a, stream); }
+    else launch_wide_tn<kLinResidual, false>(a, stream);
     return hipGetLastError();
   }
   const int fpt = mode == kLinSwiGLU ? 64 : 128;
   const long long tiles = (long long)((M + 127) / 128) * ((a.F + fpt - 1) / fpt);
   const dim3 grid((unsigned)tiles);
 #define YOCO_LIN(T, MD) hipLaunchKernelGGL((linear_kernel<T, MD>), grid, dim3(256), 0, stream, a)
-  if (is_bf16) {   // fewer than 512 tokens: the 128 x 128 tile keeps more workgroups busy
+  if (is_bf16) {   // fewer than 256 tokens: the 128 x 128 tile keeps more workgroups busy
     if (mode == kLinQKV) YOCO_LIN(bf16, kLinQKV);
     else if (mode == kLinSwiGLU) YOCO_LIN(bf16, kLinSwiGLU);
     else YOCO_LIN(bf16, kLinResidual);

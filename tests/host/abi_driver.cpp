@@ -50,6 +50,11 @@ int main() {
   CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 100, 2, 64, 32, 3, 1e-6f, YOCO_F32, nullptr) == YOCO_ERR_UNSUPPORTED);
   CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, NAN, YOCO_F32, nullptr) == YOCO_ERR_SHAPE);
   CHECK(yoco::g_launches == n + 1);
+  // bf16 with 16384 tokens or more goes to the block-layer GEMM's Q/K/V form with no query heads
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.F == 256 && yoco::g_lin.f1 == 0 && yoco::g_lin.f2 == 128);
+  CHECK(yoco::g_lin.h1 == 2 && yoco::g_lin.kv_rows == 9100 && yoco::g_lin.kv_pos0 == 7 && yoco::g_lin.norm == 1);
+  CHECK(yoco::g_lin.w0 == nullptr && yoco::g_lin.y0 == nullptr && yoco::g_launches == n + 2);
 
   // ---- sliding window and cross prefill
   n = yoco::g_launches;
