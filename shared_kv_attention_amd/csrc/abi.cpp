@@ -80,12 +80,13 @@ yoco_status yoco_global_kv_proj(const void* x, const void* norm_w, const void* w
   if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
       (norm_w && !aligned(norm_w, 16)))
     return YOCO_ERR_ALIGN;
-  if (dtype == YOCO_BF16 && (long long)B * N >= 16384) {
-    // long prompts: the block-layer GEMM in its Q/K/V form with no query
-    // heads (wide bf16 tiles; measured 18.7 vs 22.9 ms at 2^20 tokens).  Up to
-    // a few thousand tokens the 128 x 128 kernel below, two workgroups per CU,
-    // hides latency better (72 vs 80 us at 4096 tokens), and it serves float32
-    // and the one-token appends.
+  if (dtype == YOCO_BF16 && ((long long)B * N >= 16384 || (long long)B * N <= 64)) {
+    // the block-layer GEMM in its Q/K/V form with no query heads: for long
+    // prompts its wide bf16 tiles (measured 18.7 vs 22.9 ms at 2^20 tokens),
+    // for a few tokens (the one-token append of generation) its form that
+    // spreads K over many waves.  In between, the 128 x 128 kernel below, two
+    // workgroups per CU, hides latency better (72 vs 80 us at 4096 tokens); it
+    // also serves float32.
     yoco::LinArgs a{};
     a.x = x;
     a.norm_w = norm_w;

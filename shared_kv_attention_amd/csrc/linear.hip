@@ -682,8 +682,151 @@ static void launch_wide_tn(const LinArgs& a, hipStream_t stream) {
   else launch_wide<MODE, GAIN, 128>(a, t128, stream);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 form for a handful of tokens (one-token decode steps, the early-exit
+// last row): the product is bound by reading W once, so a workgroup takes 16
+// weight rows and spreads their K range over 16 waves (every load in flight at
+// once); each wave forms a 16 x 16 block (16 rows x the tokens, padded to 16)
+// on 16x16x32 MFMA, the 16 partial blocks are summed in LDS, and the epilogue
+// runs per (row, token).  SwiGLU: the 16 rows are 8 gate rows and the 8
+// matching up rows.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyWaves = 16;
+constexpr int kSkinnyMaxTokens = 64;
+
+template <int MODE, bool GAIN>
+__global__ __launch_bounds__(1024, 1) void linear_skinny_kernel(LinArgs a) {
+  __shared__ float part[kSkinnyWaves][256];
+  __shared__ float ssp[kSkinnyWaves][64];
+  __shared__ float rs[16];
+  constexpr bool NORM = MODE != kLinResidual;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int lr = l & 15, lk = l >> 4;   // MFMA lane roles: row / token l % 16, k group l / 16
+  const int M = a.B * a.N;
+  const int tg0 = blockIdx.y * 16;
+  const int fg = blockIdx.x;
+
+  // A operand: weight row of MFMA row lr
+  const bf16* wrow;
+  if constexpr (MODE == kLinSwiGLU) {
+    const int hf = min(fg * 8 + (lr & 7), a.F - 1);
+    wrow = static_cast<const bf16*>(lr >= 8 ? a.w1 : a.w0) + (size_t)hf * a.K;
+  } else {
+    const int f = min(fg * 16 + lr, a.F - 1);
+    const void* wm;
+    int fr;
+    if (MODE == kLinQKV && f >= a.f2) { wm = a.w2; fr = f - a.f2; }
+    else if (MODE == kLinQKV && f >= a.f1) { wm = a.w1; fr = f - a.f1; }
+    else { wm = a.w0; fr = f; }
+    wrow = static_cast<const bf16*>(wm) + (size_t)fr * a.K;
+  }
+  // B operand: token tg0 + lr (zero when past the end)
+  const int tok = tg0 + lr;
+  const bool tok_ok = tok < M;
+  const int tcl = min(tok, M - 1);
+  const int dh = a.x_heads > 0 ? a.K / a.x_heads : a.K;
+  const bf16* xrow = static_cast<const bf16*>(a.x) +
+                     (a.x_heads > 0 ? ((size_t)(tcl / a.N) * a.x_heads * a.N + tcl % a.N) * dh : (size_t)tcl * a.K);
+  auto xat = [&](int k) -> const bf16* {   // element k of this token's row
+    if (a.x_heads > 0) return xrow + (size_t)(k / dh) * a.N * dh + k % dh;
+    return xrow + k;
+  };
+
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+  float ssl = 0.f;
+  const int nk = a.K / 32;
+  constexpr int U = 4;
+  for (int ks0 = w; ks0 < nk; ks0 += kSkinnyWaves * U) {
+    bf16x8 wa[U], xb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u * kSkinnyWaves;
+      const int k = (ks < nk ? ks : nk - 1) * 32 + lk * 8;
+      wa[u] = *reinterpret_cast<const bf16x8*>(wrow + k);
+      xb[u] = *reinterpret_cast<const bf16x8*>(xat(k));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u * kSkinnyWaves;
+      if (ks >= nk) break;
+      bf16x8 x = tok_ok ? xb[u] : bf16x8{};
+      if constexpr (NORM) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 p{x[e], x[e + 1]};
+          ssl = __builtin_amdgcn_fdot2_f32_bf16(p, p, ssl, false);
+        }
+      }
+      if constexpr (GAIN) {
+        const bf16x8 gm = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.norm_w) + ks * 32 + lk * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (bf16)((float)x[e] * (float)gm[e]);
+      }
+      acc = mma16(wa[u], x, acc);
+    }
+  }
+  // acc[i] = C[row 4*lk + i][token lr]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[w][(4 * lk + i) * 16 + lr] = acc[i];
+  ssp[w][l] = ssl;
+  __syncthreads();
+  if (NORM && tid < 16) {
+    float t = 0.f;
+    for (int ww = 0; ww < kSkinnyWaves; ++ww)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) t += ssp[ww][g4 * 16 + tid];
+    rs[tid] = 1.0f / sqrtf(t / (float)a.K + a.eps);
+  }
+  __syncthreads();
+  // epilogue: thread e -> (row e / 16, token e % 16)
+  const int row = tid >> 4, t = tid & 15, tk = tg0 + t;
+  if (tid >= (MODE == kLinSwiGLU ? 128 : 256) || tk >= M) return;
+  auto sum_rows = [&](int r) {
+    float v = 0.f;
+    for (int ww = 0; ww < kSkinnyWaves; ++ww) v += part[ww][r * 16 + t];
+    return NORM ? v * rs[t] : v;
+  };
+  const int bb = tk / a.N, n = tk % a.N;
+  if constexpr (MODE == kLinSwiGLU) {
+    const int hf = fg * 8 + row;
+    if (hf < a.F) {
+      const float gt = sum_rows(row), up = sum_rows(row + 8);
+      static_cast<bf16*>(a.y0)[(size_t)tk * a.F + hf] = (bf16)(silu_f32(gt) * up);
+    }
+  } else {
+    const int f = fg * 16 + row;
+    if (f >= a.F) return;
+    const float v = sum_rows(row);
+    if constexpr (MODE == kLinQKV) {
+      void* out;
+      int fr, H;
+      size_t rows = (size_t)a.N, row0 = 0;
+      if (f >= a.f2) { out = a.y2; fr = f - a.f2; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
+      else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
+      else { out = a.y0; fr = f; H = a.h0; }
+      const int hh = fr / a.d, c = fr % a.d;
+      static_cast<bf16*>(out)[(((size_t)bb * H + hh) * rows + row0 + n) * a.d + c] = (bf16)v;
+    } else {
+      bf16* dst = static_cast<bf16*>(a.y0) + (size_t)tk * a.F + f;
+      *dst = (bf16)((float)*dst + v);
+    }
+  }
+}
+
 hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t stream) {
   const int M = a.B * a.N;
+  if (is_bf16 && M <= kSkinnyMaxTokens) {
+    const int groups = mode == kLinSwiGLU ? (a.F + 7) / 8 : (a.F + 15) / 16;
+    const dim3 grid((unsigned)groups, (unsigned)((M + 15) / 16));
+    const bool gain = mode != kLinResidual && a.norm_w != nullptr;
+#define YOCO_SK(MD, G) hipLaunchKernelGGL((linear_skinny_kernel<MD, G>), grid, dim3(1024), 0, stream, a)
+    if (mode == kLinQKV) { if (gain) YOCO_SK(kLinQKV, true); else YOCO_SK(kLinQKV, false); }
+    else if (mode == kLinSwiGLU) { if (gain) YOCO_SK(kLinSwiGLU, true); else YOCO_SK(kLinSwiGLU, false); }
+    else YOCO_SK(kLinResidual, false);
+#undef YOCO_SK
+    return hipGetLastError();
+  }
   if (is_bf16 && M >= 256) {
     const bool gain = mode != kLinResidual && a.norm_w != nullptr;
     if (mode == kLinQKV) { if (gain) launch_wide_tn<kLinQKV, true>(a, stream); else launch_wide_tn<kLinQKV, false>(a, stream); }
@@ -695,7 +838,7 @@ hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t s
   const long long tiles = (long long)((M + 127) / 128) * ((a.F + fpt - 1) / fpt);
   const dim3 grid((unsigned)tiles);
 #define YOCO_LIN(T, MD) hipLaunchKernelGGL((linear_kernel<T, MD>), grid, dim3(256), 0, stream, a)
-  if (is_bf16) {   // fewer than 256 tokens: the 128 x 128 tile keeps more workgroups busy
+  if (is_bf16) {   // 65 to 255 tokens: the 128 x 128 tile keeps more workgroups busy
     if (mode == kLinQKV) YOCO_LIN(bf16, kLinQKV);
     else if (mode == kLinSwiGLU) YOCO_LIN(bf16, kLinSwiGLU);
     else YOCO_LIN(bf16, kLinResidual);

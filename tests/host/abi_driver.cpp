@@ -42,9 +42,9 @@ int main() {
 
   // ---- global KV projection
   n = yoco::g_launches;
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 100, 128, 2, 64, 132, 3, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
   CHECK(yoco::g_launches == n + 1);
-  CHECK(yoco::g_proj.B == 2 && yoco::g_proj.N == 10 && yoco::g_proj.pos0 == 3 && yoco::g_proj.n_cap == 32);
+  CHECK(yoco::g_proj.B == 2 && yoco::g_proj.N == 100 && yoco::g_proj.pos0 == 3 && yoco::g_proj.n_cap == 132);
   CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 12, 3, 1e-6f, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
   CHECK(yoco_global_kv_proj(P, M, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, 1e-6f, YOCO_F32, nullptr) == YOCO_ERR_ALIGN);
   CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 100, 2, 64, 32, 3, 1e-6f, YOCO_F32, nullptr) == YOCO_ERR_UNSUPPORTED);
@@ -55,6 +55,9 @@ int main() {
   CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.F == 256 && yoco::g_lin.f1 == 0 && yoco::g_lin.f2 == 128);
   CHECK(yoco::g_lin.h1 == 2 && yoco::g_lin.kv_rows == 9100 && yoco::g_lin.kv_pos0 == 7 && yoco::g_lin.norm == 1);
   CHECK(yoco::g_lin.w0 == nullptr && yoco::g_lin.y0 == nullptr && yoco::g_launches == n + 2);
+  // and so does a one-token append (the form for a few tokens)
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 16, 1, 128, 2, 64, 40, 39, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.kv_pos0 == 39 && yoco::g_lin.B == 16 && yoco::g_launches == n + 3);
 
   // ---- sliding window and cross prefill
   n = yoco::g_launches;

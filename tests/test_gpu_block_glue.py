@@ -64,6 +64,8 @@ QKV_CASES = [
     (1, 1, 128, 2, 0, 64, False, "bf16"),        # q only, one token
     (1, 300, 192, 6, 2, 64, True, "f32"),
     (3, 129, 512, 8, 0, 128, False, "bf16"),     # cross-layer query projection
+    (3, 7, 384, 3, 1, 128, True, "bf16"),        # 21 tokens: the few-token form, two token groups
+    (1, 64, 256, 2, 2, 64, False, "bf16"),       # 64 tokens, the largest few-token case
 ]
 
 
@@ -95,6 +97,8 @@ SWIGLU_CASES = [
     (2, 130, 384, 344, True, "bf16"),     # F not a multiple of the 64-feature tile
     (1, 1, 128, 64, False, "bf16"),
     (1, 257, 192, 520, True, "f32"),
+    (3, 11, 384, 344, True, "bf16"),      # 33 tokens: few-token form, F not a multiple of its 8-row groups
+    (16, 1, 256, 8192, False, "bf16"),    # one token for each of 16 sequences
 ]
 
 
@@ -122,6 +126,8 @@ RES_CASES = [
     (1, 200, 768, 256, 0, "f32"),     # W_down over row-major activations
     (3, 1, 512, 128, 0, "bf16"),
     (1, 300, 1024, 520, 0, "bf16"),   # F not a multiple of the 128-feature tile
+    (5, 8, 512, 200, 4, "bf16"),      # 40 tokens, head-major gather, few-token form
+    (1, 1, 8192, 3072, 0, "bf16"),    # one token through W_down at the 3B shape
 ]
 
 
