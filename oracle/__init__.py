@@ -60,3 +60,4 @@ from .retention import (  # noqa: F401
     gret_chunkwise,
     gret_group_norm_swish,
 )
+from .rope import rope_inv_freq, apply_rope  # noqa: F401,E402

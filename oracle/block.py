@@ -29,7 +29,8 @@ cross-decoder layers carry the same feed-forward (the pages describe only
 their attention); the feed-forward is optional here (BlockParams.swa_ffn /
 cross_ffn; absent in the smallest pins) and, when present, is SwiGLU(n) =
 W_down (silu(W_gate n) * (W_up n)) with silu(z) = z * sigmoid(z), its sizes
-chosen by the caller (the pages give none); the final norm before the output head is left out (the
+chosen by the caller (the pages give none); RoPE is optional
+(BlockParams.rope_theta, see oracle/rope.py for its readings); the final norm before the output head is left out (the
 head is not part of the path); the cross-decoder's residual stream continues
 from the self-decoder output, the same tensor the global K/V are projected
 from.
@@ -49,6 +50,7 @@ import numpy as np
 
 from .attention import attend_row, cross_prefill_attention, ring_window, swa_attention
 from .projection import global_kv_proj, rmsnorm_row
+from .rope import apply_rope
 
 __all__ = ["BlockParams", "linear_rows", "silu", "swiglu_hidden_row", "swiglu_ffn_row", "yoco_block", "yoco_block_early_exit",
            "yoco_block_generate"]
@@ -73,6 +75,9 @@ class BlockParams:
     swa_ffn: List[tuple] = field(default_factory=list)
     cross_ffn: List[tuple] = field(default_factory=list)
     eps: float = 1e-6
+    # rotary embedding base (0: none): queries and keys of every attention,
+    # and the global keys, rotated at their absolute positions
+    rope_theta: float = 0.0
 
     def ffn(self, kind, layer):
         lst = self.swa_ffn if kind == "swa" else self.cross_ffn
@@ -84,6 +89,11 @@ def silu(z):
     z = np.asarray(z, dtype=np.float64)
     e = np.exp(-np.abs(z))
     return np.where(z >= 0, z / (1.0 + e), z * e / (1.0 + e))
+
+
+def _rope(t, pos0, p):
+    """t [..., n, d] rotated for positions pos0.. when the block uses RoPE."""
+    return apply_rope(t, pos0, p.rope_theta) if p.rope_theta > 0 else t
 
 
 def swiglu_hidden_row(x_row, w_gate, w_up, gamma=None, eps=1e-6):
@@ -145,14 +155,14 @@ def _self_decoder_and_projection(x, p):
     x = np.array(x, dtype=np.float64)
     for layer, (wq, wk, wv, wo) in enumerate(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo)):
         n = _norm_rows(x, p.eps)
-        q = _heads(linear_rows(n, wq), Hq, d)
-        k = _heads(linear_rows(n, wk), Hkv, d)
+        q = _rope(_heads(linear_rows(n, wq), Hq, d), 0, p)
+        k = _rope(_heads(linear_rows(n, wk), Hkv, d), 0, p)
         v = _heads(linear_rows(n, wv), Hkv, d)
         o, _ = swa_attention(q, k, v, p.window)
         x = x + linear_rows(_merge(o), wo)
         x = _ffn_rows(x, p.ffn("swa", layer), p.eps)
     k_glob, v_glob = global_kv_proj(x, p.glob_wk, p.glob_wv, Hkv, d, eps=p.eps)
-    return x, k_glob, v_glob
+    return x, _rope(k_glob, 0, p), v_glob
 
 
 def yoco_block(x, p):
@@ -164,7 +174,7 @@ def yoco_block(x, p):
     x, k_glob, v_glob = _self_decoder_and_projection(x, p)
     for layer, (wq, wo) in enumerate(zip(p.cross_wq, p.cross_wo)):
         n = _norm_rows(x, p.eps)
-        q = _heads(linear_rows(n, wq), Hq, d)
+        q = _rope(_heads(linear_rows(n, wq), Hq, d), 0, p)
         # every cross layer reads the same k_glob / v_glob objects
         o, _ = cross_prefill_attention(q, k_glob, v_glob)
         x = x + linear_rows(_merge(o), wo)
@@ -188,7 +198,7 @@ def yoco_block_early_exit(x, p):
         new = np.empty_like(last)
         for b in range(B):
             n = rmsnorm_row(last[b], None, p.eps)
-            q = (wq @ n).reshape(Hq, d)
+            q = _rope((wq @ n).reshape(Hq, 1, d), N - 1, p)[:, 0]
             o = np.empty((Hq, d))
             for h in range(Hq):
                 o[h], _, _ = attend_row(q[h], k_glob[b, h // g, :N],
@@ -230,8 +240,8 @@ def yoco_block_generate(x, p):
             new = np.empty_like(h_t)
             for b in range(B):
                 n = rmsnorm_row(h_t[b], None, p.eps)
-                q = (wq @ n).reshape(Hq, d)
-                kr[b, :, t % W] = (wk @ n).reshape(Hkv, d)
+                q = _rope((wq @ n).reshape(Hq, 1, d), t, p)[:, 0]
+                kr[b, :, t % W] = _rope((wk @ n).reshape(Hkv, 1, d), t, p)[:, 0]
                 vr[b, :, t % W] = (wv @ n).reshape(Hkv, d)
                 o = np.empty((Hq, d))
                 for h in range(Hq):
@@ -242,14 +252,14 @@ def yoco_block_generate(x, p):
             h_t = new
         for b in range(B):
             k_row, v_row = global_kv_proj(h_t[b][None, None, :], p.glob_wk, p.glob_wv, Hkv, d, eps=p.eps)
-            k_glob[b, :, t] = k_row[0, :, 0]
+            k_glob[b, :, t] = _rope(k_row[0, :, :1], t, p)[:, 0]
             v_glob[b, :, t] = v_row[0, :, 0]
         for layer, (wq, wo) in enumerate(zip(p.cross_wq, p.cross_wo)):
             ffn = p.ffn("cross", layer)
             new = np.empty_like(h_t)
             for b in range(B):
                 n = rmsnorm_row(h_t[b], None, p.eps)
-                q = (wq @ n).reshape(Hq, d)
+                q = _rope((wq @ n).reshape(Hq, 1, d), t, p)[:, 0]
                 o = np.empty((Hq, d))
                 for h in range(Hq):
                     o[h], _, _ = attend_row(q[h], k_glob[b, h // g, :t + 1], v_glob[b, h // g, :t + 1], scale)
