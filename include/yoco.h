@@ -78,12 +78,18 @@ typedef enum { YOCO_F32 = 0, YOCO_BF16 = 1, YOCO_FP8_E4M3 = 2 } yoco_dtype;
  * Requires 1 <= N, 0 <= pos0, pos0 + N <= n_cap, D % 64 == 0, D <= 65536.
  * Numerics: float32 accumulation; with gamma given and dtype bf16, x*gamma is
  * rounded to bf16 before the product (the row scale is applied in float32).
+ * rope_theta > 0 rotates every key (not the values) at its cache position
+ * pos0 + t by the rotary embedding of base rope_theta (paperlayer.ai summary
+ * appendix E and podcast segment 20: RoPE with a per-stage base, 640K, 5M,
+ * 80M): channel pair (2i, 2i+1) turns by (pos0 + t) * rope_theta^(-2i/d), the
+ * angle reduced in double precision.  0 = no rotation; NaN, inf or < 0 is
+ * YOCO_ERR_SHAPE.
  */
 yoco_status yoco_global_kv_proj(const void* x, const void* norm_w,
                                 const void* w_k, const void* w_v,
                                 void* k_out, void* v_out,
                                 int B, int N, int D, int Hkv, int d,
-                                int n_cap, int pos0, float eps,
+                                int n_cap, int pos0, float eps, float rope_theta,
                                 yoco_dtype dtype, void* stream);
 
 /*
@@ -246,12 +252,15 @@ yoco_status yoco_gret_group_norm_swish(const void* y, const void* g, void* out, 
  *   w_q        [Hq*d, D];  q_out [B, Hq, N, d]
  *   w_k, w_v   [Hkv*d, D]; k_out, v_out [B, Hkv, N, d]; Hkv = 0 (all four
  *              NULL) projects q only, as a cross-decoder layer does
- * Requires D % 64 == 0, D <= 65536, d in {64, 128}; one dtype (F32 or BF16)
- * for every tensor.  Numerics as yoco_global_kv_proj.
+ * rope_theta > 0 rotates q and k (not v) of token t at position rope_pos0 + t
+ * exactly as yoco_global_kv_proj rotates its keys; 0 = no rotation.
+ * Requires D % 64 == 0, D <= 65536, d in {64, 128}, rope_pos0 >= 0; one dtype
+ * (F32 or BF16) for every tensor.  Numerics as yoco_global_kv_proj.
  */
 yoco_status yoco_qkv_proj(const void* x, const void* norm_w, const void* w_q, const void* w_k,
                           const void* w_v, void* q_out, void* k_out, void* v_out, int B, int N,
-                          int D, int Hq, int Hkv, int d, float eps, yoco_dtype dtype, void* stream);
+                          int D, int Hq, int Hkv, int d, float eps, float rope_theta, int rope_pos0,
+                          yoco_dtype dtype, void* stream);
 
 /*
  * Block layer glue: the SwiGLU feed-forward's gated hidden activations.

@@ -52,7 +52,7 @@ _lib = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
-    "yoco_global_kv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_global_kv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _i, _vp]),
     "yoco_swa_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "yoco_cross_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "yoco_cross_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
@@ -64,7 +64,7 @@ _SIGS = {
     "yoco_gret_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "yoco_gret_decode": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _vp, _i, _i, _i, _i, _vp]),
     "yoco_gret_group_norm_swish": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
-    "yoco_qkv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_qkv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _i, _i, _vp]),
     "yoco_swiglu": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp]),
     "yoco_linear_residual": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "yoco_kv_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
@@ -140,23 +140,26 @@ def _check(status, fn):
         raise YocoError(status, fn)
 
 
-def yoco_global_kv_proj(x, w_k, w_v, k_out, v_out, pos0=0, norm_w=None, eps=1e-6, stream=None):
+def yoco_global_kv_proj(x, w_k, w_v, k_out, v_out, pos0=0, norm_w=None, eps=1e-6, rope_theta=0.0, stream=None):
     """K/V cache rows [pos0, pos0+N) = RMSNorm(x) @ W^T, split into KV heads.
 
     x [B, N, D]; w_k, w_v [Hkv*d, D]; k_out, v_out [B, Hkv, n_cap, d]; same dtype.
+    rope_theta > 0 rotates the keys at their cache positions.
     """
     B, N, D = x.shape
     _, Hkv, n_cap, d = k_out.shape
     st = lib().yoco_global_kv_proj(_ptr(x), _ptr(norm_w), _ptr(w_k), _ptr(w_v), _ptr(k_out), _ptr(v_out),
-                                   B, N, D, Hkv, d, n_cap, pos0, eps, _dtype_code(x), _stream(stream))
+                                   B, N, D, Hkv, d, n_cap, pos0, eps, float(rope_theta), _dtype_code(x),
+                                   _stream(stream))
     _check(st, "yoco_global_kv_proj")
     return k_out, v_out
 
 
 def yoco_qkv_proj(x, w_q, head_dim, w_k=None, w_v=None, q_out=None, k_out=None, v_out=None, norm_w=None,
-                  eps=1e-6, stream=None):
+                  eps=1e-6, rope_theta=0.0, rope_pos0=0, stream=None):
     """Pre-norm Q/K/V projection: q [B, Hq, N, d] = heads(RMSNorm(x) @ W_q^T), k and v likewise
-    ([B, Hkv, N, d]); w_k = w_v = None projects q only.  Returns (q, k, v) (k, v None for q only)."""
+    ([B, Hkv, N, d]); w_k = w_v = None projects q only.  rope_theta > 0 rotates q and k of token n
+    at position rope_pos0 + n.  Returns (q, k, v) (k, v None for q only)."""
     torch = _torch()
     B, N, D = x.shape
     d = int(head_dim)
@@ -171,7 +174,7 @@ def yoco_qkv_proj(x, w_q, head_dim, w_k=None, w_v=None, q_out=None, k_out=None, 
             v_out = torch.empty(B, Hkv, N, d, dtype=x.dtype, device=x.device)
     st = lib().yoco_qkv_proj(_ptr(x), _ptr(norm_w), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(q_out),
                              _ptr(k_out if Hkv else None), _ptr(v_out if Hkv else None), B, N, D, Hq, Hkv, d,
-                             float(eps), _dtype_code(x), _stream(stream))
+                             float(eps), float(rope_theta), int(rope_pos0), _dtype_code(x), _stream(stream))
     _check(st, "yoco_qkv_proj")
     return q_out, (k_out if Hkv else None), (v_out if Hkv else None)
 

@@ -24,6 +24,14 @@ float resolve_scale(float s, int d) { return s > 0.f ? s : 1.0f / sqrtf((float)d
 
 yoco_status launched(hipError_t e) { return e == hipSuccess ? YOCO_OK : YOCO_ERR_HIP; }
 
+// log2 of a rotary base (0 = no rotation).  A base of exactly 1 would turn
+// nothing either, but is kept distinct from "off" by a tiny non-zero value.
+double rope_log2(float theta) {
+  if (!(theta > 0.f)) return 0.0;
+  const double l = log2((double)theta);
+  return l != 0.0 ? l : 1e-300;
+}
+
 struct DecodeLayout {
   int n_splits, chunk, n_hg;
   size_t o_bytes, ml_bytes, total;
@@ -68,12 +76,13 @@ int yoco_version(void) { return kVersion; }
 
 yoco_status yoco_global_kv_proj(const void* x, const void* norm_w, const void* w_k, const void* w_v,
                                 void* k_out, void* v_out, int B, int N, int D, int Hkv, int d,
-                                int n_cap, int pos0, float eps, yoco_dtype dtype, void* stream) {
+                                int n_cap, int pos0, float eps, float rope_theta, yoco_dtype dtype,
+                                void* stream) {
   if (!x || !w_k || !w_v || !k_out || !v_out) return YOCO_ERR_NULL;
   if (!is_act(dtype)) return YOCO_ERR_DTYPE;
   if (B < 1 || N < 1 || D < 1 || Hkv < 1 || n_cap < 1 || pos0 < 0 || (long long)pos0 + N > n_cap)
     return YOCO_ERR_SHAPE;
-  if (!(eps >= 0.f) || isinf(eps)) return YOCO_ERR_SHAPE;
+  if (!(eps >= 0.f) || isinf(eps) || !(rope_theta >= 0.f) || isinf(rope_theta)) return YOCO_ERR_SHAPE;
   if ((long long)B * N > kIntMax || (long long)2 * Hkv * d > kIntMax || (long long)B * Hkv * n_cap > kIntMax)
     return YOCO_ERR_SHAPE;
   if (!head_dim_ok(d) || D % 64 != 0 || D > 65536) return YOCO_ERR_UNSUPPORTED;
@@ -100,9 +109,11 @@ yoco_status yoco_global_kv_proj(const void* x, const void* norm_w, const void* w
     a.kv_rows = n_cap; a.kv_pos0 = pos0;
     a.norm = 1;
     a.eps = eps;
+    a.rope_log2_theta = rope_log2(rope_theta);
+    a.rope_pos0 = pos0;
     return launched(yoco::launch_linear(a, yoco::kLinQKV, true, as_stream(stream)));
   }
-  yoco::ProjArgs a{x, norm_w, w_k, w_v, k_out, v_out, B, N, D, Hkv, d, n_cap, pos0, eps};
+  yoco::ProjArgs a{x, norm_w, w_k, w_v, k_out, v_out, B, N, D, Hkv, d, n_cap, pos0, eps, rope_log2(rope_theta)};
   return launched(yoco::launch_kv_proj(a, dtype == YOCO_BF16, as_stream(stream)));
 }
 
@@ -115,11 +126,13 @@ static bool lin_sizes_ok(int B, int N, int K, int F, int fpt) {
 
 yoco_status yoco_qkv_proj(const void* x, const void* norm_w, const void* w_q, const void* w_k, const void* w_v,
                           void* q_out, void* k_out, void* v_out, int B, int N, int D, int Hq, int Hkv, int d,
-                          float eps, yoco_dtype dtype, void* stream) {
+                          float eps, float rope_theta, int rope_pos0, yoco_dtype dtype, void* stream) {
   if (!x || !w_q || !q_out) return YOCO_ERR_NULL;
   if (Hkv > 0 && (!w_k || !w_v || !k_out || !v_out)) return YOCO_ERR_NULL;
   if (!is_act(dtype)) return YOCO_ERR_DTYPE;
   if (Hq < 1 || Hkv < 0 || !(eps >= 0.f) || isinf(eps)) return YOCO_ERR_SHAPE;
+  if (!(rope_theta >= 0.f) || isinf(rope_theta) || rope_pos0 < 0 || (long long)rope_pos0 + N > kIntMax)
+    return YOCO_ERR_SHAPE;
   if ((long long)(Hq + 2LL * Hkv) * d > kIntMax) return YOCO_ERR_SHAPE;
   if (!head_dim_ok(d)) return YOCO_ERR_UNSUPPORTED;
   const int F = (Hq + 2 * Hkv) * d;
@@ -145,6 +158,8 @@ yoco_status yoco_qkv_proj(const void* x, const void* norm_w, const void* w_q, co
   a.kv_rows = N; a.kv_pos0 = 0;
   a.norm = 1;
   a.eps = eps;
+  a.rope_log2_theta = rope_log2(rope_theta);
+  a.rope_pos0 = rope_pos0;
   return launched(yoco::launch_linear(a, yoco::kLinQKV, dtype == YOCO_BF16, as_stream(stream)));
 }
 

@@ -112,4 +112,24 @@ __device__ __forceinline__ float xor32(float x) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// ---------------------------------------------------------------------------
+// Rotary position embedding of one channel pair (x0, x1) = channels (2i, 2i+1)
+// of a head at position p: the angle p * theta^(-2i/d) is formed and reduced
+// modulo 2 pi in double precision (positions reach 2^20 and more, where a
+// single-precision angle would be off by a sizeable fraction of a radian),
+// then rotated with single-precision sine and cosine of the reduced angle.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double rope_inv_freq(int i, int d, double log2_theta) {
+  return exp2(-(2.0 * i / d) * log2_theta);
+}
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, double angle) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const double r = angle - kTwoPi * rint(angle * (1.0 / kTwoPi));
+  float s, c;
+  sincosf((float)r, &s, &c);
+  const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
+  x0 = y0;
+  x1 = y1;
+}
+
 }  // namespace yoco

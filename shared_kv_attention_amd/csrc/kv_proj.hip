@@ -257,16 +257,21 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
         const int hh = fr / a.d, c = fr % a.d;
         T* dst = static_cast<T*>(which ? a.v_out : a.k_out) +
                  ((size_t)(bb * a.Hkv + hh) * a.n_cap + a.pos0 + n) * a.d + c;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][jj][4 * qd + e] * rs;
+        if (a.rope_log2_theta != 0.0 && !which) {   // keys only, at their cache position
+          const long long p = a.pos0 + n;
+          rope_pair(v[0], v[1], (double)p * rope_inv_freq(c >> 1, a.d, a.rope_log2_theta));
+          rope_pair(v[2], v[3], (double)p * rope_inv_freq((c >> 1) + 1, a.d, a.rope_log2_theta));
+        }
         if constexpr (sizeof(T) == 2) {
           bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[i][jj][4 * qd + e] * rs);
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)v[e];
           *reinterpret_cast<bf16x4*>(dst) = v4;
         } else {
-          f32x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = acc[i][jj][4 * qd + e] * rs;
-          *reinterpret_cast<f32x4*>(dst) = v4;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
         }
       }
     }

@@ -50,6 +50,7 @@ struct ProjArgs {
   void* v_out;
   int B, N, D, Hkv, d, n_cap, pos0;
   float eps;
+  double rope_log2_theta;  // rotary embedding of K at position pos0 + n (0: none)
 };
 
 // Position-wise block layers (linear.hip).  Weight matrices are [rows, K]
@@ -72,6 +73,8 @@ struct LinArgs {
   int kv_rows, kv_pos0;  // QKV: rows per head of the k/v buffers, first row written
   int norm;            // fused RMSNorm of the x rows (QKV, SwiGLU)
   float eps;
+  double rope_log2_theta;  // QKV: rotary embedding of q and k, log2 of its base (0: none)
+  int rope_pos0;           // QKV: position of token row n is rope_pos0 + n
 };
 
 struct RingAppendArgs {

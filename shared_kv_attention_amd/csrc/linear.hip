@@ -129,6 +129,14 @@ __device__ __forceinline__ f32x4 load4(const T* src) {
   }
 }
 
+// Rotary embedding of channels c .. c+3 (pairs (c, c+1) and (c+2, c+3)) of a
+// head at position p.
+__device__ __forceinline__ void rope4(float& v0, float& v1, float& v2, float& v3, int c, int d, long long p,
+                                      double log2_theta) {
+  rope_pair(v0, v1, (double)p * rope_inv_freq(c >> 1, d, log2_theta));
+  rope_pair(v2, v3, (double)p * rope_inv_freq((c >> 1) + 1, d, log2_theta));
+}
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
   using C = LinCfg<T>;
@@ -304,8 +312,8 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
         for (int qd = 0; qd < 4; ++qd) {
           const int f = ft * 128 + wf * 64 + i * 32 + 8 * qd + 4 * g;
           if (f >= a.F) continue;
-          const float v0 = acc[i][jj][4 * qd] * rs, v1 = acc[i][jj][4 * qd + 1] * rs;
-          const float v2 = acc[i][jj][4 * qd + 2] * rs, v3 = acc[i][jj][4 * qd + 3] * rs;
+          float v0 = acc[i][jj][4 * qd] * rs, v1 = acc[i][jj][4 * qd + 1] * rs;
+          float v2 = acc[i][jj][4 * qd + 2] * rs, v3 = acc[i][jj][4 * qd + 3] * rs;
           if constexpr (MODE == kLinQKV) {
             void* out;
             int fr, H;
@@ -314,6 +322,7 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
             else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
             else { out = a.y0; fr = f; H = a.h0; }
             const int hh = fr / a.d, c = fr % a.d;
+            if (a.rope_log2_theta != 0.0 && f < a.f2) rope4(v0, v1, v2, v3, c, a.d, a.rope_pos0 + n, a.rope_log2_theta);
             store4<T>(static_cast<T*>(out) + (((size_t)bb * H + hh) * rows + row0 + n) * a.d + c, v0, v1, v2, v3);
           } else {
             T* dst = static_cast<T*>(a.y0) + (size_t)tok * a.F + f;
@@ -619,8 +628,8 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
         for (int qd = 0; qd < 4; ++qd) {
           const int f = ft * TM + wf * 128 + i * 32 + 8 * qd + 4 * g;
           if (f >= a.F) continue;
-          const float v0 = acc[i][j][4 * qd] * rs, v1 = acc[i][j][4 * qd + 1] * rs;
-          const float v2 = acc[i][j][4 * qd + 2] * rs, v3 = acc[i][j][4 * qd + 3] * rs;
+          float v0 = acc[i][j][4 * qd] * rs, v1 = acc[i][j][4 * qd + 1] * rs;
+          float v2 = acc[i][j][4 * qd + 2] * rs, v3 = acc[i][j][4 * qd + 3] * rs;
           if constexpr (MODE == kLinQKV) {
             void* out;
             int fr, H;
@@ -629,6 +638,7 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
             else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
             else { out = a.y0; fr = f; H = a.h0; }
             const int hh = fr / a.d, c = fr % a.d;
+            if (a.rope_log2_theta != 0.0 && f < a.f2) rope4(v0, v1, v2, v3, c, a.d, a.rope_pos0 + n, a.rope_log2_theta);
             store4<bf16>(static_cast<bf16*>(out) + (((size_t)bb * H + hh) * rows + row0 + n) * a.d + c, v0, v1, v2, v3);
           } else {
             bf16* dst = static_cast<bf16*>(a.y0) + (size_t)tok * a.F + f;
@@ -797,7 +807,7 @@ __global__ __launch_bounds__(1024, 1) void linear_skinny_kernel(LinArgs a) {
   } else {
     const int f = fg * 16 + row;
     if (f >= a.F) return;
-    const float v = sum_rows(row);
+    float v = sum_rows(row);
     if constexpr (MODE == kLinQKV) {
       void* out;
       int fr, H;
@@ -806,6 +816,13 @@ __global__ __launch_bounds__(1024, 1) void linear_skinny_kernel(LinArgs a) {
       else if (f >= a.f1) { out = a.y1; fr = f - a.f1; H = a.h1; rows = a.kv_rows; row0 = a.kv_pos0; }
       else { out = a.y0; fr = f; H = a.h0; }
       const int hh = fr / a.d, c = fr % a.d;
+      if (a.rope_log2_theta != 0.0 && f < a.f2) {
+        // the pair partner (channel c ^ 1) is row ^ 1 of the same group of 16
+        float x0 = (c & 1) ? sum_rows(row ^ 1) : v, x1 = (c & 1) ? v : sum_rows(row ^ 1);
+        const double ang = (double)(a.rope_pos0 + n) * rope_inv_freq(c >> 1, a.d, a.rope_log2_theta);
+        rope_pair(x0, x1, ang);
+        v = (c & 1) ? x1 : x0;
+      }
       static_cast<bf16*>(out)[(((size_t)bb * H + hh) * rows + row0 + n) * a.d + c] = (bf16)v;
     } else {
       bf16* dst = static_cast<bf16*>(a.y0) + (size_t)tk * a.F + f;

@@ -42,22 +42,27 @@ int main() {
 
   // ---- global KV projection
   n = yoco::g_launches;
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 100, 128, 2, 64, 132, 3, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 100, 128, 2, 64, 132, 3, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
   CHECK(yoco::g_launches == n + 1);
   CHECK(yoco::g_proj.B == 2 && yoco::g_proj.N == 100 && yoco::g_proj.pos0 == 3 && yoco::g_proj.n_cap == 132);
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 12, 3, 1e-6f, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
-  CHECK(yoco_global_kv_proj(P, M, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, 1e-6f, YOCO_F32, nullptr) == YOCO_ERR_ALIGN);
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 100, 2, 64, 32, 3, 1e-6f, YOCO_F32, nullptr) == YOCO_ERR_UNSUPPORTED);
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, NAN, YOCO_F32, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 12, 3, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_global_kv_proj(P, M, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, 1e-6f, 0.f, YOCO_F32, nullptr) == YOCO_ERR_ALIGN);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 100, 2, 64, 32, 3, 1e-6f, 0.f, YOCO_F32, nullptr) == YOCO_ERR_UNSUPPORTED);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, NAN, 0.f, YOCO_F32, nullptr) == YOCO_ERR_SHAPE);
   CHECK(yoco::g_launches == n + 1);
   // bf16 with 16384 tokens or more goes to the block-layer GEMM's Q/K/V form with no query heads
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
   CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.F == 256 && yoco::g_lin.f1 == 0 && yoco::g_lin.f2 == 128);
   CHECK(yoco::g_lin.h1 == 2 && yoco::g_lin.kv_rows == 9100 && yoco::g_lin.kv_pos0 == 7 && yoco::g_lin.norm == 1);
   CHECK(yoco::g_lin.w0 == nullptr && yoco::g_lin.y0 == nullptr && yoco::g_launches == n + 2);
+  CHECK(yoco::g_lin.rope_log2_theta == 0.0);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, 1024.f, YOCO_BF16, nullptr) ==
+        YOCO_OK);
+  CHECK(yoco::g_lin.rope_log2_theta == 10.0 && yoco::g_lin.rope_pos0 == 7);
+  n = yoco::g_launches;
   // and so does a one-token append (the form for a few tokens)
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 16, 1, 128, 2, 64, 40, 39, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
-  CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.kv_pos0 == 39 && yoco::g_lin.B == 16 && yoco::g_launches == n + 3);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 16, 1, 128, 2, 64, 40, 39, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.kv_pos0 == 39 && yoco::g_lin.B == 16 && yoco::g_launches == n + 1);
 
   // ---- sliding window and cross prefill
   n = yoco::g_launches;
@@ -170,13 +175,13 @@ int main() {
 
   // ---- block layer glue: the argument block each form reaches its kernel with
   n = yoco::g_launches;
-  CHECK(yoco_qkv_proj(P, nullptr, P, P, P, P, P, P, 2, 9, 256, 4, 1, 64, 1e-6f, YOCO_F32, nullptr) == YOCO_OK);
+  CHECK(yoco_qkv_proj(P, nullptr, P, P, P, P, P, P, 2, 9, 256, 4, 1, 64, 1e-6f, 0.f, 0, YOCO_F32, nullptr) == YOCO_OK);
   CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.F == 384 && yoco::g_lin.f1 == 256 && yoco::g_lin.f2 == 320);
   CHECK(yoco::g_lin.h0 == 4 && yoco::g_lin.h1 == 1 && yoco::g_lin.norm == 1 && yoco::g_lin.K == 256);
-  CHECK(yoco_qkv_proj(P, nullptr, P, nullptr, nullptr, P, nullptr, nullptr, 1, 5, 128, 3, 0, 128, 1e-6f, YOCO_BF16,
+  CHECK(yoco_qkv_proj(P, nullptr, P, nullptr, nullptr, P, nullptr, nullptr, 1, 5, 128, 3, 0, 128, 1e-6f, 0.f, 0, YOCO_BF16,
                       nullptr) == YOCO_OK);
   CHECK(yoco::g_lin.F == 384 && yoco::g_lin.f1 == 384 && yoco::g_lin.f2 == 384 && yoco::g_lin.w1 == nullptr);
-  CHECK(yoco_qkv_proj(P, nullptr, P, nullptr, P, P, P, P, 1, 5, 128, 3, 1, 128, 1e-6f, YOCO_BF16, nullptr) ==
+  CHECK(yoco_qkv_proj(P, nullptr, P, nullptr, P, P, P, P, 1, 5, 128, 3, 1, 128, 1e-6f, 0.f, 0, YOCO_BF16, nullptr) ==
         YOCO_ERR_NULL);
   CHECK(yoco_swiglu(P, nullptr, P, P, P, 1, 7, 192, 344, 1e-6f, YOCO_BF16, nullptr) == YOCO_OK);
   CHECK(yoco::g_lin_mode == yoco::kLinSwiGLU && yoco::g_lin.F == 344 && yoco::g_lin.K == 192 && yoco::g_lin.norm == 1);

@@ -51,10 +51,10 @@ def test_version_and_status_strings(L):
 
 def proj(L, **kw):
     a = dict(x=P, g=None, wk=P, wv=P, ko=P, vo=P, B=1, N=8, D=128, Hkv=2, d=64, n_cap=16, pos0=0, eps=1e-6,
-             dt=yk.BF16)
+             rope=0.0, dt=yk.BF16)
     a.update(kw)
     return L.yoco_global_kv_proj(a["x"], a["g"], a["wk"], a["wv"], a["ko"], a["vo"], a["B"], a["N"], a["D"],
-                                 a["Hkv"], a["d"], a["n_cap"], a["pos0"], a["eps"], a["dt"], None)
+                                 a["Hkv"], a["d"], a["n_cap"], a["pos0"], a["eps"], a["rope"], a["dt"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -62,6 +62,7 @@ def proj(L, **kw):
     (dict(dt=yk.FP8_E4M3), DTYPE), (dict(dt=7), DTYPE),
     (dict(N=0), SHAPE), (dict(pos0=-1), SHAPE), (dict(pos0=9), SHAPE), (dict(n_cap=7), SHAPE),
     (dict(eps=float("nan")), SHAPE), (dict(eps=-1.0), SHAPE), (dict(Hkv=0), SHAPE),
+    (dict(rope=-1.0), SHAPE), (dict(rope=float("nan")), SHAPE), (dict(rope=float("inf")), SHAPE),
     (dict(d=96), UNSUP), (dict(D=100), UNSUP),
     (dict(x=MIS), ALIGN), (dict(g=MIS), ALIGN), (dict(ko=MIS), ALIGN),
 ])
@@ -229,17 +230,18 @@ def test_gret_norm_errors(L, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(wq=None), NULL), (dict(qo=None), NULL), (dict(wk=None), NULL), (dict(vo=None), NULL),
     (dict(dt=yk.FP8_E4M3), DTYPE), (dict(B=0), SHAPE), (dict(N=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=-1), SHAPE),
-    (dict(eps=float("inf")), SHAPE), (dict(d=32), UNSUP), (dict(D=96), UNSUP), (dict(D=65600), UNSUP),
+    (dict(eps=float("inf")), SHAPE), (dict(rope=-2.0), SHAPE), (dict(rpos=-1), SHAPE),
+    (dict(rpos=2 ** 31 - 5), SHAPE), (dict(d=32), UNSUP), (dict(D=96), UNSUP), (dict(D=65600), UNSUP),
     (dict(x=MIS), ALIGN), (dict(g=MIS), ALIGN), (dict(ko=MIS), ALIGN),
     # a q-only (cross layer) call ignores the k/v pointers
     (dict(Hkv=0, wk=None, wv=None, ko=None, vo=None, x=MIS), ALIGN),
 ])
 def test_qkv_proj_errors(L, kw, code):
     a = dict(x=P, g=None, wq=P, wk=P, wv=P, qo=P, ko=P, vo=P, B=1, N=8, D=128, Hq=4, Hkv=2, d=64, eps=1e-6,
-             dt=yk.BF16)
+             rope=0.0, rpos=0, dt=yk.BF16)
     a.update(kw)
     assert L.yoco_qkv_proj(a["x"], a["g"], a["wq"], a["wk"], a["wv"], a["qo"], a["ko"], a["vo"], a["B"], a["N"],
-                           a["D"], a["Hq"], a["Hkv"], a["d"], a["eps"], a["dt"], None) == code
+                           a["D"], a["Hq"], a["Hkv"], a["d"], a["eps"], a["rope"], a["rpos"], a["dt"], None) == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -196,44 +196,45 @@ def _gpu_ffn(x, f):
         yk.yoco_linear_residual(h, f[2], x)
 
 
-def gpu_block(x, gp, wl, early_exit=False):
+def gpu_block(x, gp, wl, early_exit=False, rope=0.0):
     """The block on the GPU, x [B, N, D] updated in place; returns (x or its
     last row after the cross layers, K, V)."""
     Hq, Hkv, d, W = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.window
     B, N, D = x.shape
     for layer, (wq, wk, wv, wo) in enumerate(gp["swa"]):
-        q, k, v = yk.yoco_qkv_proj(x, wq, d, wk, wv)
+        q, k, v = yk.yoco_qkv_proj(x, wq, d, wk, wv, rope_theta=rope)
         o = yk.yoco_swa_attn(q, k, v, W)
         yk.yoco_linear_residual(o, wo, x, a_heads=Hq)
         _gpu_ffn(x, gp["swa_ffn"][layer] if gp["swa_ffn"] else None)
     kc = torch.empty(B, Hkv, N, d, dtype=x.dtype, device=DEV)
     vc = torch.empty_like(kc)
-    yk.yoco_global_kv_proj(x, gp["glob"][0], gp["glob"][1], kc, vc)
+    yk.yoco_global_kv_proj(x, gp["glob"][0], gp["glob"][1], kc, vc, rope_theta=rope)
     if early_exit:
         last = x[:, N - 1:N].contiguous()
         for layer, (wq, wo) in enumerate(gp["cross"]):
-            q, _, _ = yk.yoco_qkv_proj(last, wq, d)
+            q, _, _ = yk.yoco_qkv_proj(last, wq, d, rope_theta=rope, rope_pos0=N - 1)
             o = yk.yoco_cross_attn_decode(q.reshape(B, Hq, d).contiguous(), kc, vc, N)
             yk.yoco_linear_residual(o.reshape(B, Hq, 1, d), wo, last, a_heads=Hq)
             _gpu_ffn(last, gp["cross_ffn"][layer] if gp["cross_ffn"] else None)
         return last[:, 0], kc, vc
     for layer, (wq, wo) in enumerate(gp["cross"]):
-        q, _, _ = yk.yoco_qkv_proj(x, wq, d)
+        q, _, _ = yk.yoco_qkv_proj(x, wq, d, rope_theta=rope)
         o = yk.yoco_cross_attn_prefill(q, kc, vc)
         yk.yoco_linear_residual(o, wo, x, a_heads=Hq)
         _gpu_ffn(x, gp["cross_ffn"][layer] if gp["cross_ffn"] else None)
     return x, kc, vc
 
 
-@pytest.mark.parametrize("with_ffn", [True, False])
-def test_tiny_block_wholly_on_gpu_matches_oracle(with_ffn):
+@pytest.mark.parametrize("with_ffn,rope", [(True, 0.0), (False, 0.0), (True, 640e3)])
+def test_tiny_block_wholly_on_gpu_matches_oracle(with_ffn, rope):
     wl = WORKLOADS["tiny_block_f32"]
-    print(f"tiny block on the GPU, ffn={with_ffn}", flush=True)
+    print(f"tiny block on the GPU, ffn={with_ffn} rope={rope}", flush=True)
     gp, p = _params(wl, with_ffn)
+    p.rope_theta = rope
     x = randn((wl.batch, wl.seq, wl.hidden), seed_for(wl.wid, 0), dtype="f32", device=DEV)
     x64 = to64(x)
-    out, kc, vc = gpu_block(x.clone(), gp, wl)
-    last, _, _ = gpu_block(x.clone(), gp, wl, early_exit=True)
+    out, kc, vc = gpu_block(x.clone(), gp, wl, rope=rope)
+    last, _, _ = gpu_block(x.clone(), gp, wl, early_exit=True, rope=rope)
     torch.cuda.synchronize()
     ref, (rk, rv) = oracle.yoco_block(x64, p)
     check(to64(kc), rk, "f32", "shared K")
@@ -279,3 +280,53 @@ def test_block_glue_at_the_3b_shape_sampled_rows():
     q_rows = to64(q)[:, :, rows].transpose(0, 2, 1, 3).reshape(B, len(rows), Hq * d)
     glue_check(to64(y1)[:, rows], x64 + oracle.linear_rows(q_rows, to64(wo)), "bf16", "x + o W_o^T (3B)")
     glue_check(to64(y2)[:, rows], x64 + oracle.linear_rows(to64(h)[:, rows], to64(wd)), "bf16", "x + h W_down^T (3B)")
+
+
+# ---------------------------------------------------------------- rotary embedding in the epilogues
+ROPE_CASES = [
+    # B, N, D, Hq, Hkv, d, theta, pos0, dtype   (token count picks the kernel form)
+    (1, 77, 256, 4, 1, 64, 10000.0, 0, "f32"),          # 128 x 128 form
+    (1, 300, 256, 4, 2, 128, 640e3, 5000, "bf16"),      # wide form
+    (3, 5, 256, 2, 1, 128, 80e6, 1 << 20, "bf16"),      # few-token form at a 1M-token position
+    (1, 64, 128, 2, 0, 64, 5e6, 123456, "bf16"),        # query only
+]
+
+
+@pytest.mark.parametrize("B,N,D,Hq,Hkv,d,theta,pos0,dt", ROPE_CASES)
+def test_qkv_proj_rope_matches_oracle(B, N, D, Hq, Hkv, d, theta, pos0, dt):
+    print(f"qkv_proj rope B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} theta={theta} pos0={pos0} {dt}", flush=True)
+    s = 1.0 / math.sqrt(D)
+    x = randn((B, N, D), 3500 + N, dtype=dt, device=DEV)
+    wq = randn((Hq * d, D), 3501, std=s, dtype=dt, device=DEV)
+    wk = randn((Hkv * d, D), 3502, std=s, dtype=dt, device=DEV) if Hkv else None
+    wv = randn((Hkv * d, D), 3503, std=s, dtype=dt, device=DEV) if Hkv else None
+    q, k, v = yk.yoco_qkv_proj(x, wq, d, wk, wv, rope_theta=theta, rope_pos0=pos0)
+    torch.cuda.synchronize()
+    rq, _ = oracle.global_kv_proj(to64(x), to64(wq), to64(wq), Hq, d)
+    glue_check(to64(q), oracle.apply_rope(rq, pos0, theta), dt, "rotated q")
+    if Hkv:
+        rk, rv = oracle.global_kv_proj(to64(x), to64(wk), to64(wv), Hkv, d)
+        glue_check(to64(k), oracle.apply_rope(rk, pos0, theta), dt, "rotated k")
+        glue_check(to64(v), rv, dt, "v (never rotated)")
+
+
+@pytest.mark.parametrize("B,N,dt", [(2, 300, "bf16"), (1, 77, "f32"), (16, 1, "bf16"), (2, 8200, "bf16")])
+def test_global_kv_proj_rope_matches_oracle(B, N, dt):
+    """Keys rotated at their cache positions pos0 + t (every kernel form),
+    values untouched."""
+    D, Hkv, d, theta, pos0 = 256, 2, 128, 80e6, 1000
+    n_cap = pos0 + N + 3
+    print(f"kv_proj rope B={B} N={N} {dt}", flush=True)
+    x = randn((B, N, D), 3600 + N, dtype=dt, device=DEV)
+    wk = randn((Hkv * d, D), 3601, std=0.06, dtype=dt, device=DEV)
+    wv = randn((Hkv * d, D), 3602, std=0.06, dtype=dt, device=DEV)
+    ko = torch.zeros(B, Hkv, n_cap, d, dtype=_tdt(dt), device=DEV)
+    vo = torch.zeros_like(ko)
+    yk.yoco_global_kv_proj(x, wk, wv, ko, vo, pos0=pos0, rope_theta=theta)
+    torch.cuda.synchronize()
+    rows = list(range(N)) if N <= 300 else [0, 1, 4095, 4096, N - 1]
+    rk, rv = oracle.global_kv_proj(to64(x)[:, rows], to64(wk), to64(wv), Hkv, d)
+    rk = np.stack([oracle.apply_rope(rk[:, :, i:i + 1], pos0 + r, theta)[:, :, 0] for i, r in enumerate(rows)], axis=2)
+    idx = [pos0 + r for r in rows]
+    glue_check(to64(ko)[:, :, idx], rk, dt, "rotated keys")
+    glue_check(to64(vo)[:, :, idx], rv, dt, "values")
