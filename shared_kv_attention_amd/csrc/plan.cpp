@@ -9,7 +9,7 @@ static long long split_target(int B, int Hq, int Hkv, int ctx) {
   const long long units = (long long)B * Hkv * ((Hq / Hkv + 3) / 4);
   const long long target = 4096;                       // workgroups (one wave each)
   long long s = (target + units - 1) / units;
-  const long long max_s = (ctx + 255) / 256;           // at least 256 keys per split
+  const long long max_s = (ctx + 63) / 64;             // at least 64 keys per split
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   return s;
@@ -18,7 +18,7 @@ static long long split_target(int B, int Hq, int Hkv, int ctx) {
 int decode_split_bound(int B, int Hq, int Hkv, int ctx) { return (int)split_target(B, Hq, Hkv, ctx); }
 
 // Split-K plan of the decode kernel: enough one-wave workgroups to keep all
-// 256 CUs streaming (about 4096), at least 256 keys per split, the chunk a
+// 256 CUs streaming (about 4096), at least 64 keys per split, the chunk a
 // multiple of 64 keys, and never more than kDecodeMaxSplits splits.
 void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int* n_hg) {
   *n_hg = (Hq / Hkv + 3) / 4;
