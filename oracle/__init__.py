@@ -42,6 +42,7 @@ from .attention import (  # noqa: F401
     causal_allowed,
     ring_window,
     swa_ring_decode_attention,
+    merge_partial_attention,
 )
 from .projection import rmsnorm_row, rmsnorm, global_kv_proj  # noqa: F401
 from .fp8 import (  # noqa: F401

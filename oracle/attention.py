@@ -179,6 +179,26 @@ def decode_attention(q, k_cache, v_cache, ctx_lens, scale=None, bh=None):
     return o, lse
 
 
+def merge_partial_attention(o_parts, lse_parts):
+    """Attention over a union of disjoint key sets, from the results over each
+    set: with L = log sum_s exp(lse_s),  o = sum_s exp(lse_s - L) o_s.
+
+    This is the combine step of a decode whose cache is split across shards
+    (each shard attends over its rows and reports o_s with its log-sum-exp);
+    the pages split long sequences across devices ([S App. A]; [P seg. 14]),
+    the merge itself is the softmax definition regrouped.
+    o_parts [S, ..., d]; lse_parts [S, ...] (natural log).  Returns (o, L).
+    """
+    o_parts, lse_parts = _as64(o_parts), _as64(lse_parts)
+    if o_parts.shape[:-1] != lse_parts.shape:
+        raise ValueError("o_parts [S, ..., d] and lse_parts [S, ...]")
+    m = lse_parts.max(axis=0)
+    w = np.exp(lse_parts - m)
+    tot = w.sum(axis=0)
+    o = (w[..., None] * o_parts).sum(axis=0) / tot[..., None]
+    return o, m + np.log(tot)
+
+
 def ring_window(pos, window):
     """(position, slot) pairs a decode query at position pos reads from a ring
     of W slots, in position order: positions max(0, pos-W+1) .. pos, position
