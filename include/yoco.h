@@ -108,6 +108,35 @@ yoco_status yoco_swa_attn(const void* q, const void* k, const void* v,
                           float softmax_scale, yoco_dtype dtype, void* stream);
 
 /*
+ * One sequence shard's sliding-window attention (a long sequence split across
+ * devices; the pages' chunk parallelism: paperlayer.ai summary appendix A,
+ * podcast segment 14 -- the self-decoder exchanges only with its neighbour).
+ * k, v hold the shard's Nkv rows preceded by a halo of the previous shard's
+ * last rows: [B, Hkv, Nkv, d]; q, o are the shard's own Nq rows, the last Nq
+ * rows of that buffer: [B, Hq, Nq, d]; lse [B, Hq, Nq] or NULL.  Row i sits
+ * at buffer position Nkv - Nq + i and sees the window of W keys ending there,
+ * so a halo of at least W - 1 rows gives exactly those rows of the full
+ * sequence's sliding-window attention (bitwise when the halo starts at a
+ * multiple of 64 sequence positions: the key tiles then coincide).
+ * Requires 1 <= Nq <= Nkv; otherwise as yoco_swa_attn.
+ */
+yoco_status yoco_swa_attn_halo(const void* q, const void* k, const void* v,
+                               void* o, float* lse,
+                               int B, int Hq, int Hkv, int Nq, int Nkv, int d, int window,
+                               float softmax_scale, yoco_dtype dtype, void* stream);
+
+/*
+ * Merge of attention results over disjoint key sets (the shards of a cache
+ * split across devices, each decoded with yoco_cross_attn_decode and its
+ * log-sum-exp): o = sum_s exp(lse_s - L) o_s, L = log sum_s exp(lse_s).
+ *   o_parts [S, rows, d] (F32 or BF16), lse_parts [S, rows] float32,
+ *   o [rows, d], lse [rows] float32 or NULL; rows = B * Hq of the decode.
+ * Requires S >= 1, d in {64, 128}.  Float32 arithmetic.
+ */
+yoco_status yoco_attn_merge(const void* o_parts, const float* lse_parts, void* o, float* lse,
+                            int S, int rows, int d, yoco_dtype dtype, void* stream);
+
+/*
  * Cross-decoder causal attention over the shared cache, many queries
  * (full prefill of one cross-decoder layer, or a chunk of it).
  * Source: podcast segment 12 (each cross layer has its own queries and

@@ -23,6 +23,8 @@ __all__ = [
     "library_path",
     "yoco_global_kv_proj",
     "yoco_swa_attn",
+    "yoco_swa_attn_halo",
+    "yoco_attn_merge",
     "yoco_cross_attn_prefill",
     "yoco_cross_attn_decode",
     "yoco_cross_attn_decode_workspace_bytes",
@@ -54,6 +56,8 @@ _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_
 _SIGS = {
     "yoco_global_kv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _i, _vp]),
     "yoco_swa_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_swa_attn_halo": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
+    "yoco_attn_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "yoco_cross_attn_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "yoco_cross_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
                                     _vp, _sz, _vp]),
@@ -212,6 +216,33 @@ def yoco_swa_attn(q, k, v, window, o=None, lse=None, softmax_scale=0.0, stream=N
     st = lib().yoco_swa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, int(window),
                              float(softmax_scale), _dtype_code(q), _stream(stream))
     _check(st, "yoco_swa_attn")
+    return o
+
+
+def yoco_swa_attn_halo(q, k, v, window, o=None, lse=None, softmax_scale=0.0, stream=None):
+    """One shard's sliding-window attention: k/v [B, Hkv, Nkv, d] are a halo of earlier rows followed by the
+    shard's rows, q [B, Hq, Nq, d] the shard's own (last Nq) rows.  Returns o."""
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib().yoco_swa_attn_halo(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nkv, d, int(window),
+                                  float(softmax_scale), _dtype_code(q), _stream(stream))
+    _check(st, "yoco_swa_attn_halo")
+    return o
+
+
+def yoco_attn_merge(o_parts, lse_parts, o=None, lse=None, stream=None):
+    """Merge per-shard attention results: o_parts [S, ..., d], lse_parts [S, ...] float32.  Returns o [..., d]."""
+    torch = _torch()
+    S, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = o_parts[0].numel() // d
+    if o is None:
+        o = torch.empty(o_parts.shape[1:], dtype=o_parts.dtype, device=o_parts.device)
+    st = lib().yoco_attn_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse), S, rows, d, _dtype_code(o_parts),
+                               _stream(stream))
+    _check(st, "yoco_attn_merge")
     return o
 
 

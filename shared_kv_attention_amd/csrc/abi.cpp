@@ -227,6 +227,26 @@ yoco_status yoco_swa_attn(const void* q, const void* k, const void* v, void* o, 
   return attn_common(q, k, v, o, lse, B, Hq, Hkv, N, N, N, 0, d, window, true, softmax_scale, dtype, stream);
 }
 
+yoco_status yoco_swa_attn_halo(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                               int Hkv, int Nq, int Nkv, int d, int window, float softmax_scale, yoco_dtype dtype,
+                               void* stream) {
+  if (Nq > Nkv) return YOCO_ERR_SHAPE;
+  return attn_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, Nkv, Nkv - Nq, d, window, true, softmax_scale, dtype,
+                     stream);
+}
+
+yoco_status yoco_attn_merge(const void* o_parts, const float* lse_parts, void* o, float* lse, int S, int rows, int d,
+                            yoco_dtype dtype, void* stream) {
+  if (!o_parts || !lse_parts || !o) return YOCO_ERR_NULL;
+  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (S < 1 || rows < 1 || (long long)S * rows > kIntMax) return YOCO_ERR_SHAPE;
+  if (!head_dim_ok(d)) return YOCO_ERR_UNSUPPORTED;
+  if (!aligned(o_parts, 16) || !aligned(o, 16) || !aligned(lse_parts, 4) || (lse && !aligned(lse, 4)))
+    return YOCO_ERR_ALIGN;
+  yoco::MergeArgs a{o_parts, lse_parts, o, lse, S, rows, d};
+  return launched(yoco::launch_attn_merge(a, dtype == YOCO_BF16, as_stream(stream)));
+}
+
 yoco_status yoco_cross_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                     int Hq, int Hkv, int Nq, int n_kv, int n_cap, int q_offset, int d,
                                     float softmax_scale, yoco_dtype dtype, void* stream) {

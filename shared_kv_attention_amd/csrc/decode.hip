@@ -434,6 +434,33 @@ __global__ __launch_bounds__(64) void ring_append_kernel(RingAppendArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of per-shard attention results (a cache split across devices, each
+// shard decoded with its log-sum-exp): o = sum_s exp(lse_s - L) o_s with
+// L = log sum_s exp(lse_s).  One workgroup per row, one thread per channel.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void attn_merge_kernel(MergeArgs a) {
+  const int row = blockIdx.x, c = threadIdx.x;
+  const size_t stride = (size_t)a.rows;   // between shards, in rows
+  float m = -INFINITY;
+  for (int s = 0; s < a.S; ++s) m = fmaxf(m, a.lse_parts[s * stride + row]);
+  float tot = 0.f, acc = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const float w = __expf(a.lse_parts[s * stride + row] - m);
+    tot += w;
+    acc = fmaf(w, to_f32(static_cast<const T*>(a.o_parts)[(s * stride + row) * a.d + c]), acc);
+  }
+  static_cast<T*>(a.o)[(size_t)row * a.d + c] = from_f32<T>(acc / tot);
+  if (a.lse != nullptr && c == 0) a.lse[row] = m + __logf(tot);
+}
+
+hipError_t launch_attn_merge(const MergeArgs& a, bool is_bf16, hipStream_t stream) {
+  if (is_bf16) hipLaunchKernelGGL(attn_merge_kernel<bf16>, dim3((unsigned)a.rows), dim3(a.d), 0, stream, a);
+  else hipLaunchKernelGGL(attn_merge_kernel<float>, dim3((unsigned)a.rows), dim3(a.d), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(64), 0, stream, a);
   return hipGetLastError();

@@ -77,6 +77,14 @@ struct LinArgs {
   int rope_pos0;           // QKV: position of token row n is rope_pos0 + n
 };
 
+struct MergeArgs {
+  const void* o_parts;     // [S, rows, d] activation dtype
+  const float* lse_parts;  // [S, rows]
+  void* o;                 // [rows, d]
+  float* lse;              // [rows] or null
+  int S, rows, d;
+};
+
 struct RingAppendArgs {
   const void* k_new;   // [B, Hkv, d]
   const void* v_new;
@@ -136,6 +144,7 @@ hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t stream);
 hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
+hipError_t launch_attn_merge(const MergeArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t stream);
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_gret_norm(const GretNormArgs& a, bool is_bf16, hipStream_t stream);

@@ -20,6 +20,7 @@ extern QuantArgs g_quant;
 extern RingAppendArgs g_ring;
 extern GretArgs g_gret;
 extern LinArgs g_lin;
+extern MergeArgs g_merge;
 extern int g_lin_mode;
 extern int g_decode_kinds[3];
 }  // namespace yoco
@@ -190,6 +191,18 @@ int main() {
   CHECK(yoco_linear_residual(P, 3, P, P, 2, 3, 512, 256, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
   CHECK(yoco_linear_residual(P, 0, P, M, 2, 3, 512, 256, YOCO_BF16, nullptr) == YOCO_ERR_ALIGN);
   CHECK(yoco::g_launches == n + 4);
+
+  // ---- one shard of a split sequence: window attention with a halo, merge of decode shards
+  n = yoco::g_launches;
+  CHECK(yoco_swa_attn_halo(P, P, P, P, nullptr, 1, 8, 2, 300, 1323, 128, 1024, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_attn.q_offset == 1023 && yoco::g_attn.n_kv == 1323 && yoco::g_attn.kv_rows == 1323 &&
+        yoco::g_attn.Nq == 300 && yoco::g_attn.window == 1024);
+  CHECK(yoco_swa_attn_halo(P, P, P, P, nullptr, 1, 8, 2, 301, 300, 128, 1024, 0.f, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_attn_merge(P, (const float*)P, P, (float*)P, 8, 512, 128, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco::g_merge.S == 8 && yoco::g_merge.rows == 512 && yoco::g_merge.d == 128);
+  CHECK(yoco_attn_merge(P, (const float*)P, P, nullptr, 0, 512, 128, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_attn_merge(M, (const float*)P, P, nullptr, 2, 512, 128, YOCO_BF16, nullptr) == YOCO_ERR_ALIGN);
+  CHECK(yoco::g_launches == n + 2);
 
   // ---- fp8 quantiser
   n = yoco::g_launches;

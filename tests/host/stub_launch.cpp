@@ -15,6 +15,7 @@ GretArgs g_gret;
 GretDecodeArgs g_gret_dec;
 GretNormArgs g_gret_norm;
 LinArgs g_lin;
+MergeArgs g_merge;
 int g_lin_mode = -1;
 int g_decode_kinds[3];
 
@@ -28,6 +29,7 @@ hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t) { ++g_launch
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t) { ++g_launches; g_gret = a; return hipSuccess; }
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool, hipStream_t) { ++g_launches; g_gret_dec = a; return hipSuccess; }
 hipError_t launch_gret_norm(const GretNormArgs& a, bool, hipStream_t) { ++g_launches; g_gret_norm = a; return hipSuccess; }
+hipError_t launch_attn_merge(const MergeArgs& a, bool, hipStream_t) { ++g_launches; g_merge = a; return hipSuccess; }
 hipError_t launch_linear(const LinArgs& a, int mode, bool, hipStream_t) {
   ++g_launches; g_lin = a; g_lin_mode = mode; return hipSuccess;
 }

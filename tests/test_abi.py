@@ -268,6 +268,27 @@ def test_linear_residual_errors(L, kw, code):
                                   None) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(dt=yk.FP8_E4M3), DTYPE), (dict(Nq=0), SHAPE), (dict(Nq=301), SHAPE),
+    (dict(W=0), SHAPE), (dict(d=32), UNSUP), (dict(k=MIS), ALIGN),
+])
+def test_swa_attn_halo_errors(L, kw, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=8, Hkv=2, Nq=200, Nkv=300, d=128, W=64, dt=yk.BF16)
+    a.update(kw)
+    assert L.yoco_swa_attn_halo(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                a["Nkv"], a["d"], a["W"], 0.0, a["dt"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), NULL), (dict(lp=None), NULL), (dict(o=None), NULL), (dict(dt=yk.FP8_E4M3), DTYPE),
+    (dict(S=0), SHAPE), (dict(rows=0), SHAPE), (dict(d=96), UNSUP), (dict(o=MIS), ALIGN), (dict(lse=4096 + 2), ALIGN),
+])
+def test_attn_merge_errors(L, kw, code):
+    a = dict(op=P, lp=P, o=P, lse=None, S=4, rows=64, d=128, dt=yk.BF16)
+    a.update(kw)
+    assert L.yoco_attn_merge(a["op"], a["lp"], a["o"], a["lse"], a["S"], a["rows"], a["d"], a["dt"], None) == code
+
+
 def quant(L, **kw):
     a = dict(kv=P, dt=yk.F32, codes=P, scale=P, B=2, Hkv=4, n=10, d=64, ws=P, wsb=64)
     a.update(kw)
