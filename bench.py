@@ -544,6 +544,68 @@ def run_block(wl, dev, steps):
     return out
 
 
+# ---------------------------------------------------------------- one device's share
+def run_shard(wl, dev, parts=8, reps=3):
+    """One device's share of the 1M-token early-exit flow split over `parts`
+    devices by sequence chunks: each self-decoder layer over the device's
+    2^20 / parts rows plus a 1024-row halo of the previous chunk, the global
+    projection of its rows, and per cross-decoder layer the last token's
+    decode over its cache shard plus the merge of the `parts` shard results
+    (the halo and the partials would arrive over xGMI; that exchange is not
+    timed here)."""
+    B, N, D, Hq, Hkv, d, W = wl.batch, wl.seq, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    C = N // parts
+    wid = wl.wid
+    q = randn((B, Hq, C, d), seed_for(wid, 500), device=dev)
+    k = randn((B, Hkv, C + W, d), seed_for(wid, 501), device=dev)
+    v = randn((B, Hkv, C + W, d), seed_for(wid, 502), device=dev)
+    o = torch.empty_like(q)
+    x = randn((B, C, D), seed_for(wid, 503), device=dev)
+    wk = randn((Hkv * d, D), seed_for(wid, 504), std=wl.weight_std, device=dev)
+    wv = randn((Hkv * d, D), seed_for(wid, 505), std=wl.weight_std, device=dev)
+    kc = torch.empty(B, Hkv, C, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    qd = randn((B, Hq, d), seed_for(wid, 506), device=dev)
+    od = torch.empty_like(qd)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    ws = torch.empty(yk.yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, C, d), dtype=torch.uint8, device=dev)
+    o_parts = randn((parts, B, Hq, d), seed_for(wid, 507), device=dev)
+    lse_parts = randn((parts, B, Hq), seed_for(wid, 508), dtype="f32", device=dev)
+    om = torch.empty_like(qd)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return events_ms([(a, b)])[0] / reps
+
+    swa_ms = timed(lambda: yk.yoco_swa_attn_halo(q, k, v, W, o=o))
+    proj_ms = timed(lambda: yk.yoco_global_kv_proj(x, wk, wv, kc, vc))
+    dec_ms = timed(lambda: yk.yoco_cross_attn_decode(qd, kc, vc, C, o=od, lse=lse, workspace=ws))
+    merge_ms = timed(lambda: yk.yoco_attn_merge(o_parts, lse_parts, o=om))
+    f_swa = attn_flops(C * W, Hq, d, B)                 # every shard row sees a full window
+    f_proj = proj_flops(B, C, D, Hkv * d)
+    dbytes = decode_bytes(B, Hkv, C, d, Hq, 2, 2)
+    step = wl.n_self_layers * swa_ms + proj_ms + wl.n_cross_layers * (dec_ms + merge_ms)
+    return {
+        "workload": wl.name, "devices": parts, "rows_per_device": C, "halo_rows": W,
+        "swa_layer": {"ms": swa_ms, "TFLOP/s": f_swa / (swa_ms * 1e-3) / 1e12,
+                      "frac_mfma_peak": f_swa / (swa_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "kv_proj": {"ms": proj_ms, "TFLOP/s": f_proj / (proj_ms * 1e-3) / 1e12},
+        "decode_shard": {"ms": dec_ms, "GB/s": dbytes / (dec_ms * 1e-3) / 1e9,
+                         "frac_hbm_peak": dbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "merge_ms": merge_ms,
+        "device_ms_per_step": step,
+        "timing": "HIP events around back-to-back calls of each part; the exchanges between devices are not timed",
+    }
+
+
 # ---------------------------------------------------------------- early exit
 def run_early_exit(wl, dev, steps):
     """1M-token early-exit prefill: L_s SWA layers over all tokens, the global
@@ -737,6 +799,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_early_exit:
         out["early_exit_1m"] = run_early_exit(WORKLOADS["early_exit_1m_bf16"], dev, args.extra_steps)
+        torch.cuda.empty_cache()
+        out["early_exit_1m_one_of_8_devices"] = run_shard(WORKLOADS["early_exit_1m_bf16"], dev)
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
