@@ -679,6 +679,35 @@ def run_early_exit(wl, dev, steps):
     }
 
 
+# ---------------------------------------------------------------- achievable peaks
+def run_peaks(dev, reps=5):
+    """What this chip reaches at its clock under load: a streaming read of a
+    4 GiB buffer and a register-resident bf16 matrix-core loop."""
+    buf = torch.zeros(1 << 30, dtype=torch.int32, device=dev)
+    part = torch.empty(2048, dtype=torch.int32, device=dev)
+    mout = torch.empty(4 * 1024, dtype=torch.float32, device=dev)
+    iters = 20000
+    res = {}
+    for name, fn in (("read", lambda: yk.yoco_peak_hbm_read(buf, blocks=2048, partial=part)),
+                     ("mfma", lambda: yk.yoco_peak_mfma_bf16(iters, blocks=1024, out=mout))):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = events_ms([(a, b)])[0] / reps
+    read_gbs = buf.numel() * 4 / (res["read"] * 1e-3) / 1e9
+    mfma_tf = 1024 * 4 * iters * 8 * 32768 / (res["mfma"] * 1e-3) / 1e12
+    del buf
+    return {"hbm_read_GB/s": read_gbs, "frac_of_spec_hbm": read_gbs / HBM_PEAK_GBS,
+            "mfma_bf16_TFLOP/s": mfma_tf, "frac_of_spec_mfma": mfma_tf / BF16_PEAK_TFLOPS,
+            "what": "libyoco peak microbenchmarks: one streaming read of 4 GiB; 1024 workgroups x 4 waves x "
+                    "20000 rounds of 8 independent 32x32x16 bf16 MFMAs from registers"}
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -755,6 +784,10 @@ def main():
         "ms_per_launch": attn_ms,
     }
 
+    peaks = run_peaks(dev)
+    roofline["measured_peak"] = peaks["mfma_bf16_TFLOP/s"]
+    roofline["frac_of_measured_peak"] = attn_tflops / peaks["mfma_bf16_TFLOP/s"]
+
     out = {
         "metric": METRIC,
         "value": tflops,
@@ -777,12 +810,15 @@ def main():
         },
         "frac_mfma_peak": tflops / BF16_PEAK_TFLOPS,
         "roofline": roofline,
+        "measured_peaks": peaks,
     }
     del step
     torch.cuda.empty_cache()
 
     if not args.no_decode:
         out["decode"] = run_decode(WORKLOADS["decode_32k_bf16"], dev, args.decode_steps)
+        out["decode"]["roofline"]["measured_peak"] = peaks["hbm_read_GB/s"]
+        out["decode"]["roofline"]["frac_of_measured_peak"] = out["decode"]["GB/s"] / peaks["hbm_read_GB/s"]
         torch.cuda.empty_cache()
     if not args.no_fp8_decode:
         out["decode_fp8"] = run_decode(WORKLOADS["decode_512k_fp8"], dev, WORKLOADS["decode_512k_fp8"].decode_steps)

@@ -24,6 +24,8 @@ __all__ = [
     "yoco_global_kv_proj",
     "yoco_swa_attn",
     "yoco_swa_attn_halo",
+    "yoco_peak_hbm_read",
+    "yoco_peak_mfma_bf16",
     "yoco_attn_merge",
     "yoco_cross_attn_prefill",
     "yoco_cross_attn_decode",
@@ -73,6 +75,8 @@ _SIGS = {
     "yoco_linear_residual": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp]),
     "yoco_kv_quantize_fp8": (_i, [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "yoco_kv_quantize_fp8_workspace_bytes": (_sz, [_i]),
+    "yoco_peak_hbm_read": (_i, [_vp, _sz, _vp, _i, _vp]),
+    "yoco_peak_mfma_bf16": (_i, [_i, _vp, _i, _vp]),
     "yoco_status_string": (ctypes.c_char_p, [_i]),
     "yoco_version": (_i, []),
 }
@@ -217,6 +221,28 @@ def yoco_swa_attn(q, k, v, window, o=None, lse=None, softmax_scale=0.0, stream=N
                              float(softmax_scale), _dtype_code(q), _stream(stream))
     _check(st, "yoco_swa_attn")
     return o
+
+
+def yoco_peak_hbm_read(buf, blocks=2048, partial=None, stream=None):
+    """Stream `buf` (a device tensor, size a multiple of 16 bytes) once; returns the per-workgroup uint32 sums
+    (as int32)."""
+    torch = _torch()
+    if partial is None:
+        partial = torch.empty(blocks, dtype=torch.int32, device=buf.device)
+    st = lib().yoco_peak_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(partial), int(blocks),
+                                  _stream(stream))
+    _check(st, "yoco_peak_hbm_read")
+    return partial
+
+
+def yoco_peak_mfma_bf16(iters, blocks=1024, out=None, device=None, stream=None):
+    """Matrix-core loop: blocks x 4 waves x iters x 8 MFMAs of 32x32x16 bf16; returns out [4 * blocks]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(4 * blocks, dtype=torch.float32, device=device or "cuda")
+    st = lib().yoco_peak_mfma_bf16(int(iters), _ptr(out), int(blocks), _stream(stream))
+    _check(st, "yoco_peak_mfma_bf16")
+    return out
 
 
 def yoco_swa_attn_halo(q, k, v, window, o=None, lse=None, softmax_scale=0.0, stream=None):

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libyoco.so")
 
-SOURCES = ["attn_fwd.hip", "decode.hip", "kv_proj.hip", "linear.hip", "fp8_quant.hip", "gret.hip", "plan.cpp", "abi.cpp"]
+SOURCES = ["attn_fwd.hip", "decode.hip", "kv_proj.hip", "linear.hip", "fp8_quant.hip", "gret.hip", "peak.hip", "plan.cpp", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

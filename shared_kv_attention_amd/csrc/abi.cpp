@@ -247,6 +247,20 @@ yoco_status yoco_attn_merge(const void* o_parts, const float* lse_parts, void* o
   return launched(yoco::launch_attn_merge(a, dtype == YOCO_BF16, as_stream(stream)));
 }
 
+yoco_status yoco_peak_hbm_read(const void* buf, size_t bytes, uint32_t* partial, int blocks, void* stream) {
+  if (!buf || !partial) return YOCO_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > 65536) return YOCO_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(partial, 4)) return YOCO_ERR_ALIGN;
+  return launched(yoco::launch_peak_read(buf, (long long)bytes, partial, blocks, as_stream(stream)));
+}
+
+yoco_status yoco_peak_mfma_bf16(int iters, float* out, int blocks, void* stream) {
+  if (!out) return YOCO_ERR_NULL;
+  if (iters < 1 || iters > (1 << 20) || blocks < 1 || blocks > 65536) return YOCO_ERR_SHAPE;
+  if (!aligned(out, 4)) return YOCO_ERR_ALIGN;
+  return launched(yoco::launch_peak_mfma(iters, out, blocks, as_stream(stream)));
+}
+
 yoco_status yoco_cross_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                     int Hq, int Hkv, int Nq, int n_kv, int n_cap, int q_offset, int d,
                                     float softmax_scale, yoco_dtype dtype, void* stream) {

@@ -1,0 +1,76 @@
+// Achievable-peak microbenchmarks of the chip the library runs on: a
+// streaming HBM read and a register-resident bf16 matrix-core loop.  They
+// report what this MI355X reaches at its clock under load, beside the spec
+// figures (8 TB/s, 2.5 PFLOP/s dense bf16) the kernels are also measured
+// against.  Both compute a checkable result so that nothing can be
+// optimised away: the read sums the 32-bit words it loads, the matrix loop
+// accumulates products of exactly representable operands.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace yoco {
+
+// Every thread sums 16-byte chunks in a grid-stride loop (8 chunks in flight
+// per iteration); one partial sum per workgroup (wrapping 32-bit integer sum).
+__global__ __launch_bounds__(256) void peak_read_kernel(const u32x4* __restrict__ src, long long n_chunks,
+                                                        uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[256];
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t s = 0;
+  for (; i + 7 * stride < n_chunks; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u][0] + v[u][1] + v[u][2] + v[u][3];
+  }
+  for (; i < n_chunks; i += stride) {
+    const u32x4 v = src[i];
+    s += v[0] + v[1] + v[2] + v[3];
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+// Each wave runs `iters` rounds of 8 independent 32x32x16 bf16 MFMAs on
+// operands of ones: every accumulator element gains 16 per MFMA, so after
+// the loop each equals 16 * iters exactly (iters <= 2^20).  Lane 0 of each
+// wave writes the sum of its 8 accumulators' first elements.
+__global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, float* __restrict__ out) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (bf16)1.0f;
+    b[j] = (bf16)1.0f;
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = mma32(a, b, acc[i]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0];
+  if ((threadIdx.x & 63) == 0) out[(size_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = s;
+}
+
+hipError_t launch_peak_read(const void* src, long long bytes, uint32_t* partial, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(peak_read_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
+                     bytes / 16, partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_peak_mfma(int iters, float* out, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(peak_mfma_kernel, dim3(blocks), dim3(256), 0, stream, iters, out);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

@@ -30,6 +30,8 @@ hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t) { ++g_launches; g
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool, hipStream_t) { ++g_launches; g_gret_dec = a; return hipSuccess; }
 hipError_t launch_gret_norm(const GretNormArgs& a, bool, hipStream_t) { ++g_launches; g_gret_norm = a; return hipSuccess; }
 hipError_t launch_attn_merge(const MergeArgs& a, bool, hipStream_t) { ++g_launches; g_merge = a; return hipSuccess; }
+hipError_t launch_peak_read(const void*, long long, uint32_t*, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_peak_mfma(int, float*, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_linear(const LinArgs& a, int mode, bool, hipStream_t) {
   ++g_launches; g_lin = a; g_lin_mode = mode; return hipSuccess;
 }

@@ -289,6 +289,17 @@ def test_attn_merge_errors(L, kw, code):
     assert L.yoco_attn_merge(a["op"], a["lp"], a["o"], a["lse"], a["S"], a["rows"], a["d"], a["dt"], None) == code
 
 
+def test_peak_microbenchmark_errors(L):
+    assert L.yoco_peak_hbm_read(None, 1024, P, 8, None) == NULL
+    assert L.yoco_peak_hbm_read(P, 1000, P, 8, None) == SHAPE
+    assert L.yoco_peak_hbm_read(P, 1024, P, 0, None) == SHAPE
+    assert L.yoco_peak_hbm_read(MIS, 1024, P, 8, None) == ALIGN
+    assert L.yoco_peak_mfma_bf16(10, None, 8, None) == NULL
+    assert L.yoco_peak_mfma_bf16(0, P, 8, None) == SHAPE
+    assert L.yoco_peak_mfma_bf16((1 << 20) + 1, P, 8, None) == SHAPE
+    assert L.yoco_peak_mfma_bf16(10, P, 70000, None) == SHAPE
+
+
 def quant(L, **kw):
     a = dict(kv=P, dt=yk.F32, codes=P, scale=P, B=2, Hkv=4, n=10, d=64, ws=P, wsb=64)
     a.update(kw)
