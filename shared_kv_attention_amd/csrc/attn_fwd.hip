@@ -30,6 +30,8 @@
 //    sliding window, whose tiles all cost the same), and within each round
 //    the heads of one KV head are placed on one XCD (workgroups go to the 8
 //    XCDs round-robin), so each XCD's L2 holds one KV head's K/V.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_lds.hpp"
@@ -80,11 +82,290 @@ __device__ __forceinline__ void pipe_sched_steps() {
   }
 }
 
+// Key tiles [lo, hi] that query tile qt (bq rows) needs.
+__device__ __forceinline__ void key_span(const AttnArgs& a, bool swa, int bq, int bk, int qt, int& lo, int& hi) {
+  const int q_first = qt * bq, q_last = min(q_first + bq, a.Nq) - 1;
+  const int P0 = a.q_offset + q_first, P1 = a.q_offset + q_last;
+  lo = swa ? max(0, P0 - a.window + 1) / bk : 0;
+  hi = min(P1, a.n_kv - 1) / bk;
+}
+
+// One wave's 32 query rows of one (batch, head): Q operands, running
+// softmax state and unnormalised O, and the per-tile step.
+template <typename T, int D, bool SWA>
+struct AttnWave {
+  using C = AttnCfg<T, D>;
+  using frag = typename Elem<T>::frag;
+  frag qf[C::NC];
+  f32x16 acc[C::NDB];
+  float m_run, l_run;        // running max (log2 domain) and this lane's partial denominator
+  int qi, lo_key, hi_key;    // this lane's query row and its allowed keys
+  int pw0, pw1;              // first and last query position of the wave
+  bool live;                 // the wave holds at least one valid row
+
+  // rows wq0 .. wq0 + 31 (lane l -> row wq0 + l % 32) of the head at qbase
+  __device__ __forceinline__ void init(const AttnArgs& a, const T* qbase, int wq0, int l) {
+    const int g = l >> 5;
+    qi = wq0 + (l & 31);
+    const int pos = a.q_offset + qi;
+    lo_key = SWA ? max(0, pos - a.window + 1) : 0;
+    hi_key = min(pos, a.n_kv - 1);
+    if (qi < a.Nq) {
+      const T* qrow = qbase + (size_t)qi * D;
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) qf[c] = load_frag_global<T>(qrow + 16 * c + 8 * g);
+    } else {
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) qf[c] = frag{};
+    }
+    // wave-uniform: kept in scalar registers so that tile decisions are scalar branches
+    live = __builtin_amdgcn_readfirstlane(wq0 < a.Nq) != 0;
+    pw0 = __builtin_amdgcn_readfirstlane(a.q_offset + wq0);
+    pw1 = __builtin_amdgcn_readfirstlane(a.q_offset + min(wq0 + 31, a.Nq - 1));
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  }
+
+  // key tile t from (ktile, vtile) in LDS
+  __device__ __forceinline__ void tile(const AttnArgs& a, int t, const char* ktile, const char* vtile, int l) {
+    const int g = l >> 5, r32 = l & 31;
+    const int k0 = t * C::BK, k1 = k0 + C::BK - 1;
+    const bool skip = !live || k0 > pw1 || (SWA && k1 <= pw0 - a.window);
+    if (skip) return;
+    const bool need_mask = k1 > pw0 || k1 >= a.n_kv || (SWA && k0 <= pw1 - a.window);
+
+    // S^T = K Q^T
+    f32x16 s[C::NKB];
+    if constexpr (sizeof(T) == 2) {
+      // slot n = (k step c = n / NKB, key block kb = n % NKB): the two key
+      // blocks alternate, so consecutive MFMAs are independent; fragments
+      // are read FRAG_AHEAD slots ahead through a small ring
+      constexpr int NS = C::NC * C::NKB, PD = C::FRAG_AHEAD;
+      const int krow = sigma(r32);
+      frag ring[PD + 1];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int n = 0; n < PD; ++n) ring[n] = lds_frag_k<T, C::CH>(ktile, (n % C::NKB) * 32 + krow, n / C::NKB, g);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        if (n + PD < NS) {
+          const int m = n + PD;
+          ring[m % (PD + 1)] = lds_frag_k<T, C::CH>(ktile, (m % C::NKB) * 32 + krow, m / C::NKB, g);
+        }
+        s[n % C::NKB] = mma32(ring[n % (PD + 1)], qf[n / C::NKB], s[n % C::NKB]);
+      }
+      pipe_sched_prologue<1, PD, 0>();
+      pipe_sched_steps<1, NS, PD, 0>();
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+        s[kb] = f32x16{};
+        const int krow = kb * 32 + sigma(r32);
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) s[kb] = mma32(lds_frag_k<T, C::CH>(ktile, krow, c, g), qf[c], s[kb]);
+      }
+    }
+
+    // element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8*g + i%8.
+    // Masked scores become -inf (a select, never an additive mask).
+    float mraw = -INFINITY;
+    if (need_mask) {
+      // allowed keys of this lane's row: [lo_key, hi_key], i.e. element
+      // offsets off (key = k0 + 8g + off) in [lim_lo, lim_hi].  The lower
+      // bound can only bite on a tile that reaches below some row's window.
+      const int lim_hi = hi_key - (k0 + 8 * g), lim_lo = lo_key - (k0 + 8 * g);
+      auto mask_tile = [&](auto both) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int off = kb * 32 + 16 * (i >> 3) + (i & 7);
+            // both bounds: one unsigned range test; upper bound only: one signed test
+            const bool ok = decltype(both)::value ? (unsigned)(off - lim_lo) <= (unsigned)(lim_hi - lim_lo)
+                                                  : off <= lim_hi;
+            const float x = ok ? s[kb][i] : -INFINITY;
+            s[kb][i] = x;
+            mraw = fmaxf(mraw, x);
+          }
+        }
+      };
+      if (SWA && k0 <= pw1 - a.window) mask_tile(std::true_type{});
+      else mask_tile(std::false_type{});
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[kb][i]);
+      }
+    }
+    mraw = pair32_max(mraw);
+    const float mloc = mraw * a.scale_log2;   // scale > 0: max commutes with it
+    // Each row decides from its own scores only (rows never influence each
+    // other, so results are bitwise causal).
+    const bool up = mloc > m_run + 8.0f;
+    if (__any(up)) {
+      const float alpha = !up ? 1.f : (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mloc));
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) acc[db] *= alpha;
+      m_run = up ? mloc : m_run;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, neg_m));
+    }
+    // P^T fragments: step c covers keys 16c .. 16c+15 of the tile
+    frag pf[C::NPC];
+#pragma unroll
+    for (int c = 0; c < C::NPC; ++c) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pf[c][jj] = from_f32<T>(s[c >> 1][8 * (c & 1) + jj]);
+    }
+    // float32 row sum (4 independent partial sums for instruction-level parallelism)
+    float ls[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int i = (kb == 0 ? 4 : 0); i < 16; ++i) ls[i & 3] += s[kb][i];
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+
+    // O^T += V^T P^T
+    if constexpr (sizeof(T) == 2) {
+      // slot n = (key step c = n / NDB, dim block db = n % NDB): the dim
+      // blocks alternate; each fragment is two transposed reads, issued
+      // FRAG_AHEAD slots ahead
+      constexpr int NS = C::NPC * C::NDB, PD = C::FRAG_AHEAD;
+      frag ring[PD + 1];
+#pragma unroll
+      for (int n = 0; n < PD; ++n) ring[n] = lds_frag_vt<T, C::CH>(vtile, n / C::NDB, n % C::NDB, l);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        if (n + PD < NS) {
+          const int m = n + PD;
+          ring[m % (PD + 1)] = lds_frag_vt<T, C::CH>(vtile, m / C::NDB, m % C::NDB, l);
+        }
+        acc[n % C::NDB] = mma32(ring[n % (PD + 1)], pf[n / C::NDB], acc[n % C::NDB]);
+      }
+      pipe_sched_prologue<2, PD, 0>();
+      pipe_sched_steps<2, NS, PD, 0>();
+    } else {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+        for (int c = 0; c < C::NPC; ++c) acc[db] = mma32(lds_frag_vt<T, C::CH>(vtile, c, db, l), pf[c], acc[db]);
+      }
+    }
+  }
+
+  // normalise and write this lane's row of O (and its log-sum-exp)
+  __device__ __forceinline__ void write(const AttnArgs& a, size_t bh, int l) const {
+    const int g = l >> 5;
+    const float l_tot = pair32_sum(l_run);
+    if (qi >= a.Nq) return;
+    const float inv = 1.f / l_tot;
+    T* orow = static_cast<T*>(a.o) + (bh * a.Nq + qi) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int dim = db * 32 + 8 * qd + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc[db][4 * qd + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + dim) = v4;
+        } else {
+          f32x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * qd + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + dim) = v4;
+        }
+      }
+    }
+    if (a.lse != nullptr && g == 0) {
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      a.lse[bh * a.Nq + qi] = (mref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+  }
+};
+
+// Cooperative staging of K/V tiles (global -> LDS directly, no registers) by
+// the 4 waves (256 threads) that share the tiles.  Each wave instruction
+// fills 64 consecutive 16-byte LDS slots (lane i -> slot base + i).  Slot P of
+// a tile holds row P / CH at physical chunk P % CH, i.e. logical chunk
+// (P % CH) ^ swizzle(row); so each lane fetches the global chunk that belongs
+// in its slot.  The loads are buffer loads through a per-tile resource whose
+// base is the tile and whose size ends at row n_kv: the lane offsets are
+// loop-invariant registers (no per-load address arithmetic), and rows at or
+// past n_kv are never read -- they load as zeros (always masked out).
+template <typename T, int D>
+struct TileStager {
+  using C = AttnCfg<T, D>;
+  static constexpr int ROWB = D * C::E;   // bytes per K/V row
+  unsigned koff[C::PER_T], voff[C::PER_T];
+  const char* kbase;
+  const char* vbase;
+  int n_kv, wslot;
+
+  __device__ __forceinline__ void init(const char* kb, const char* vb, int n_kv_, int wi, int l) {
+    // the bases are uniform: keep them scalar so the buffer resources are built in SGPRs
+    kbase = uniform_ptr(kb);
+    vbase = uniform_ptr(vb);
+    n_kv = __builtin_amdgcn_readfirstlane(n_kv_);
+    wslot = __builtin_amdgcn_readfirstlane(64 * wi);
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      const int slot = C::NT * r + wslot + l;
+      const int row = slot / C::CH, pch = slot % C::CH;
+      koff[r] = (unsigned)(row * ROWB + ((pch ^ swz_k<C::CH>(row)) << 4));
+      voff[r] = (unsigned)(row * ROWB + ((pch ^ swz_v<C::CH>(row)) << 4));
+    }
+  }
+  // Every buffer starts zeroed, so a slot that an out-of-range load leaves
+  // untouched still holds finite data; this lane's zeros land before its loads.
+  __device__ __forceinline__ void zero(char* k0, char* v0, char* k1, char* v1, int l) const {
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      const int o = (C::NT * r + wslot + l) * 16;
+      *reinterpret_cast<u32x4*>(k0 + o) = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(v0 + o) = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(k1 + o) = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(v1 + o) = u32x4{0, 0, 0, 0};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  __device__ __forceinline__ void load(int t, char* kdst_tile, char* vdst_tile) const {
+    const size_t tb = (size_t)t * C::BK * ROWB;   // uniform tile base
+    // bytes of rows < n_kv (uniform; read back as a scalar so the resource stays in SGPRs)
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(C::TILE_BYTES, (n_kv - t * C::BK) * ROWB)));
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tb), (short)0, valid, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tb), (short)0, valid, kBufferFlags);
+#pragma unroll
+    for (int r = 0; r < C::PER_T; ++r) {
+      char* kdst = kdst_tile + (C::NT * r + wslot) * 16;
+      char* vdst = vdst_tile + (C::NT * r + wslot) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)kdst, 16, (int)koff[r], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)vdst, 16, (int)voff[r], 0, 0, 0);
+    }
+  }
+};
+
+// the tile loads' LDS writes land asynchronously: wait for this wave's before
+// the barrier that hands the buffer to the other waves
+__device__ __forceinline__ void tile_landed() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// One 4-wave workgroup per query tile.
+// ---------------------------------------------------------------------------
 template <typename T, int D, bool SWA>
 __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_EU)) void attn_fwd_kernel(AttnArgs a) {
   using C = AttnCfg<T, D>;
-  using frag = typename Elem<T>::frag;
-  constexpr int RB = C::RB;
   // Two buffer sets as distinct LDS objects, used in a statically alternating
   // order (the tile loop is unrolled by two): the compiler can then see that
   // the asynchronous loads into one set never alias reads of the other, and
@@ -95,7 +376,7 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
   const int tid = threadIdx.x;
   // wave index as a scalar: every wave-level decision below is a scalar branch
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, g = l >> 5, r32 = l & 31;
+  const int l = tid & 63;
 
   // ---- workgroup -> (batch, head, query tile) ----
   const int BH = a.B * a.Hq;
@@ -113,280 +394,41 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
   const char* kbase = static_cast<const char*>(a.k) + ((size_t)(b * a.Hkv + kvh) * a.kv_rows) * D * C::E;
   const char* vbase = static_cast<const char*>(a.v) + ((size_t)(b * a.Hkv + kvh) * a.kv_rows) * D * C::E;
 
-  // ---- this lane's query rows (one per 32-row block) ----
-  const int q_first = qt * C::BQ;
-  const int wq0 = q_first + w * 32 * RB;
-  int qi[RB], lo_key[RB], hi_key[RB];
-  frag qf[RB][C::NC];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    qi[rb] = wq0 + rb * 32 + r32;
-    const int pos = a.q_offset + qi[rb];
-    lo_key[rb] = SWA ? max(0, pos - a.window + 1) : 0;   // allowed keys of this row
-    hi_key[rb] = min(pos, a.n_kv - 1);
-    if (qi[rb] < a.Nq) {
-      const T* qrow = qbase + (size_t)qi[rb] * D;
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) qf[rb][c] = load_frag_global<T>(qrow + 16 * c + 8 * g);
-    } else {
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) qf[rb][c] = frag{};
-    }
-  }
+  AttnWave<T, D, SWA> wv;
+  wv.init(a, qbase, qt * C::BQ + w * 32, l);
+  int t_lo, t_hi;
+  key_span(a, SWA, C::BQ, C::BK, qt, t_lo, t_hi);
 
-  // ---- key-tile range of the workgroup and of this wave ----
-  const int q_last = min(q_first + C::BQ, a.Nq) - 1;
-  const int P0 = a.q_offset + q_first, P1 = a.q_offset + q_last;
-  const int t_lo = SWA ? max(0, P0 - a.window + 1) / C::BK : 0;
-  const int t_hi = min(P1, a.n_kv - 1) / C::BK;
-  const bool wave_live = wq0 < a.Nq;
-  const int pw0 = a.q_offset + wq0;
-  const int pw1 = a.q_offset + min(wq0 + 32 * RB - 1, a.Nq - 1);
-
-  // ---- cooperative tile staging: global -> LDS directly (no registers) ----
-  // Each wave instruction fills 64 consecutive 16-byte LDS slots (lane i ->
-  // slot base + i).  Slot P of a tile holds row P / CH at physical chunk
-  // P % CH, i.e. logical chunk (P % CH) ^ swizzle(row); so each lane fetches
-  // the global chunk that belongs in its slot.  Rows at or past n_kv are
-  // clamped to the last valid row (finite data, always masked out).
-  constexpr int ROWB = D * C::E;   // bytes per K/V row
-  unsigned koff[C::PER_T], voff[C::PER_T];   // loop-invariant byte offsets of this lane's slots
-  int srow[C::PER_T];
-#pragma unroll
-  for (int r = 0; r < C::PER_T; ++r) {
-    const int slot = C::NT * r + 64 * w + l;
-    const int row = slot / C::CH, pch = slot % C::CH;
-    srow[r] = row;
-    koff[r] = (unsigned)(row * ROWB + ((pch ^ swz_k<C::CH>(row)) << 4));
-    voff[r] = (unsigned)(row * ROWB + ((pch ^ swz_v<C::CH>(row)) << 4));
-  }
-  auto load_tile = [&](int t, char* kdst_tile, char* vdst_tile) {
-    const char* kt = kbase + (size_t)t * C::BK * ROWB;   // uniform tile base
-    const char* vt = vbase + (size_t)t * C::BK * ROWB;
-    const bool tail = (t + 1) * C::BK > a.n_kv;         // tile crosses the last valid row
-#pragma unroll
-    for (int r = 0; r < C::PER_T; ++r) {
-      unsigned ko = koff[r], vo = voff[r];
-      if (tail) {
-        const int over = t * C::BK + srow[r] - (a.n_kv - 1);   // rows past n_kv-1 re-read row n_kv-1
-        if (over > 0) {
-          ko -= (unsigned)(over * ROWB);
-          vo -= (unsigned)(over * ROWB);
-        }
-      }
-      char* kdst = kdst_tile + (C::NT * r + 64 * w) * 16;
-      char* vdst = vdst_tile + (C::NT * r + 64 * w) * 16;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(kt + ko),
-                                       (__attribute__((address_space(3))) void*)kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vt + vo),
-                                       (__attribute__((address_space(3))) void*)vdst, 16, 0, 0);
-    }
-  };
-  // the tile's LDS writes land asynchronously: wait for them before the
-  // barrier that hands the buffer to the other waves
-  auto tile_landed = []() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-  f32x16 acc_o[RB][C::NDB];
-  float m_run[RB], l_run[RB];   // running max (log2 domain) and this lane's partial denominator
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) acc_o[rb][db] = f32x16{};
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
-  }
+  TileStager<T, D> st;
+  st.init(kbase, vbase, a.n_kv, w, l);
+  st.zero(kbuf0, vbuf0, kbuf1, vbuf1, l);
 
   // one tile: compute from (ktile, vtile) while tile t+1 streams into (knext, vnext)
   auto tile_step = [&](int t, const char* ktile, const char* vtile, char* knext, char* vnext)
       __attribute__((always_inline)) {
     const bool has_next = t < t_hi;
-    if (has_next) load_tile(t + 1, knext, vnext);   // this set was released by the last barrier
-    const int k0 = t * C::BK, k1 = k0 + C::BK - 1;
-    const bool skip = !wave_live || k0 > pw1 || (SWA && k1 <= pw0 - a.window);
-    if (!skip) {
-      const bool need_mask = k1 > pw0 || k1 >= a.n_kv || (SWA && k0 <= pw1 - a.window);
-
-      // S^T = K Q^T: each K fragment serves every row block of the wave
-      f32x16 s[RB][C::NKB];
-      if constexpr (sizeof(T) == 2 && RB == 1) {
-        // slot n = (k step c = n / NKB, key block kb = n % NKB): the two key
-        // blocks alternate, so consecutive MFMAs are independent; fragments
-        // are read FRAG_AHEAD slots ahead through a small ring
-        constexpr int NS = C::NC * C::NKB, PD = C::FRAG_AHEAD;
-        const int krow = sigma(r32);
-        frag ring[PD + 1];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) s[0][kb] = f32x16{};
-#pragma unroll
-        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_k<T, C::CH>(ktile, (n % C::NKB) * 32 + krow, n / C::NKB, g);
-#pragma unroll
-        for (int n = 0; n < NS; ++n) {
-          if (n + PD < NS) {
-            const int m = n + PD;
-            ring[m % (PD + 1)] = lds_frag_k<T, C::CH>(ktile, (m % C::NKB) * 32 + krow, m / C::NKB, g);
-          }
-          s[0][n % C::NKB] = mma32(ring[n % (PD + 1)], qf[0][n / C::NKB], s[0][n % C::NKB]);
-        }
-        pipe_sched_prologue<1, PD, 0>();
-        pipe_sched_steps<1, NS, PD, 0>();
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[rb][kb] = f32x16{};
-          const int krow = kb * 32 + sigma(r32);
-#pragma unroll
-          for (int c = 0; c < C::NC; ++c) {
-            const frag kf = lds_frag_k<T, C::CH>(ktile, krow, c, g);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mma32(kf, qf[rb][c], s[rb][kb]);
-          }
-        }
-      }
-
-      frag pf[RB][C::NPC];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        // element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8*g + i%8.
-        // Masked scores become -inf (a select, never an additive mask).
-        float mraw = -INFINITY;
-        if (need_mask) {
-          // allowed keys of this lane's row: [lo_key, hi_key]; one unsigned range test per score
-          const unsigned span = (unsigned)(hi_key[rb] - lo_key[rb]);
-          const int base = k0 + 8 * g - lo_key[rb];
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int off = kb * 32 + 16 * (i >> 3) + (i & 7);
-              const float x = ((unsigned)(base + off) <= span) ? s[rb][kb][i] : -INFINITY;
-              s[rb][kb][i] = x;
-              mraw = fmaxf(mraw, x);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[rb][kb][i]);
-          }
-        }
-        mraw = fmaxf(mraw, xor32(mraw));
-        const float mloc = mraw * a.scale_log2;   // scale > 0: max commutes with it
-        // Each row decides from its own scores only (rows never influence
-        // each other, so results are bitwise causal).
-        const bool up = mloc > m_run[rb] + 8.0f;
-        if (__any(up)) {
-          const float alpha = !up ? 1.f : (m_run[rb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - mloc));
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < C::NDB; ++db) acc_o[rb][db] *= alpha;
-          m_run[rb] = up ? mloc : m_run[rb];
-        }
-        const float neg_m = (m_run[rb] == -INFINITY) ? 0.f : -m_run[rb];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[rb][kb][i] = __builtin_amdgcn_exp2f(fmaf(s[rb][kb][i], a.scale_log2, neg_m));
-        }
-        // P^T fragments: step c covers keys 16c .. 16c+15 of the tile
-#pragma unroll
-        for (int c = 0; c < C::NPC; ++c) {
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) pf[rb][c][jj] = from_f32<T>(s[rb][c >> 1][8 * (c & 1) + jj]);
-        }
-        // float32 row sum (4 independent partial sums for instruction-level parallelism)
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ls[i & 3] += s[rb][kb][i];
-        }
-        const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
-        l_run[rb] += lsum;
-      }
-      // O^T += V^T P^T: each V^T fragment serves every row block of the wave
-      if constexpr (sizeof(T) == 2 && RB == 1) {
-        // slot n = (key step c = n / NDB, dim block db = n % NDB): the dim
-        // blocks alternate; each fragment is two transposed reads, issued
-        // FRAG_AHEAD slots ahead
-        constexpr int NS = C::NPC * C::NDB, PD = C::FRAG_AHEAD;
-        frag ring[PD + 1];
-#pragma unroll
-        for (int n = 0; n < PD; ++n) ring[n] = lds_frag_vt<T, C::CH>(vtile, n / C::NDB, n % C::NDB, l);
-#pragma unroll
-        for (int n = 0; n < NS; ++n) {
-          if (n + PD < NS) {
-            const int m = n + PD;
-            ring[m % (PD + 1)] = lds_frag_vt<T, C::CH>(vtile, m / C::NDB, m % C::NDB, l);
-          }
-          acc_o[0][n % C::NDB] = mma32(ring[n % (PD + 1)], pf[0][n / C::NDB], acc_o[0][n % C::NDB]);
-        }
-        pipe_sched_prologue<2, PD, 0>();
-        pipe_sched_steps<2, NS, PD, 0>();
-      } else {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-          for (int c = 0; c < C::NPC; ++c) {
-            const frag vf = lds_frag_vt<T, C::CH>(vtile, c, db, l);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = mma32(vf, pf[rb][c], acc_o[rb][db]);
-          }
-        }
-      }
-    }
-
+    if (has_next) st.load(t + 1, knext, vnext);   // this set was released by the last barrier
+    wv.tile(a, t, ktile, vtile, l);
     if (has_next) tile_landed();
     __syncthreads();
   };
 
-  load_tile(t_lo, kbuf0, vbuf0);
+  st.load(t_lo, kbuf0, vbuf0);
   tile_landed();
   __syncthreads();
   for (int t = t_lo; t <= t_hi; t += 2) {
     tile_step(t, kbuf0, vbuf0, kbuf1, vbuf1);
     if (t + 1 <= t_hi) tile_step(t + 1, kbuf1, vbuf1, kbuf0, vbuf0);
   }
-
-  // ---- normalise and write ----
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = l_run[rb] + xor32(l_run[rb]);
-    if (qi[rb] < a.Nq) {
-      const float inv = 1.f / l_tot;
-      T* orow = static_cast<T*>(a.o) + ((size_t)(b * a.Hq + h) * a.Nq + qi[rb]) * D;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          const int dim = db * 32 + 8 * qd + 4 * g;
-          if constexpr (sizeof(T) == 2) {
-            bf16x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = (bf16)(acc_o[rb][db][4 * qd + e] * inv);
-            *reinterpret_cast<bf16x4*>(orow + dim) = v4;
-          } else {
-            f32x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = acc_o[rb][db][4 * qd + e] * inv;
-            *reinterpret_cast<f32x4*>(orow + dim) = v4;
-          }
-        }
-      }
-      if (a.lse != nullptr && g == 0) {
-        const float mref = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
-        a.lse[(size_t)(b * a.Hq + h) * a.Nq + qi[rb]] = (mref + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      }
-    }
-  }
+  wv.write(a, (size_t)(b * a.Hq + h), l);
 }
 
 template <typename T, int D, bool SWA>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
-  const int nqt = (a.Nq + AttnCfg<T, D>::BQ - 1) / AttnCfg<T, D>::BQ;
+  using C = AttnCfg<T, D>;
+  const int nqt = (a.Nq + C::BQ - 1) / C::BQ;
   const long long nblocks = (long long)nqt * a.B * a.Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, SWA>), dim3((unsigned)nblocks), dim3(AttnCfg<T, D>::NT), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, SWA>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream, a);
   return hipGetLastError();
 }
 

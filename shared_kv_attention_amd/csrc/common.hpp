@@ -20,6 +20,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Fourth word of a raw buffer resource on gfx9-family chips: data format
+// 32 bits (field [18:15] = 4), no index stride, no swizzle, no thread-id
+// addressing.  Untyped buffer loads read bytes at base + offset and return
+// zeros for offsets at or past the resource's size.
+constexpr int kBufferFlags = 0x00020000;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -110,7 +116,27 @@ __device__ __forceinline__ float xor32(float x) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) << 2), __float_as_int(x)));
 }
 
+// Maximum / sum of the values held by lanes l and l ^ 32, on both lanes
+// (v_permlane32_swap exchanges the two halves of the wave in the VALU; the
+// sum is formed in the same order, low half first, on both lanes).
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// A pointer that is the same on every lane, as a scalar value.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
 
 // ---------------------------------------------------------------------------
 // Rotary position embedding of one channel pair (x0, x1) = channels (2i, 2i+1)
