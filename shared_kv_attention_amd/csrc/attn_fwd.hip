@@ -38,16 +38,22 @@
 
 namespace yoco {
 
-template <typename T, int D>
+template <typename T, int D, bool SWA>
 struct AttnCfg {
   static constexpr int E = Elem<T>::bytes;
   // 4 waves x 32 query rows.  (Two 32-row blocks per wave halve the LDS
   // traffic per MFMA but need one wave per SIMD; measured slower.)
-  static constexpr int RB = 1;                  // 32-row blocks per wave
   static constexpr int NW = 4;                  // waves per workgroup
   static constexpr int NT = NW * 64;            // threads per workgroup
-  static constexpr int BQ = NW * 32 * RB;       // query rows per workgroup (128)
-  static constexpr int BK = (E == 2) ? 64 : 32;
+  static constexpr int BQ = NW * 32;            // query rows per workgroup (128)
+  // bf16 sliding window: 32-key tiles (32 KB of LDS per workgroup) and at most
+  // 168 VGPRs, so that three workgroups share a CU.  Its query tiles all cost
+  // about the same, and at the 3B shape (4096 rows x 24 heads = 768 tiles)
+  // two per CU is one and a half rounds; three per CU is one.  The causal
+  // kernel keeps 64-key tiles and two workgroups per CU: its tiles range from
+  // 1 to 64 key tiles and run heaviest first.
+  static constexpr bool THREE = SWA && E == 2;
+  static constexpr int BK = (E == 2 && !THREE) ? 64 : 32;
   static constexpr int CH = D * E / 16;         // 16-byte chunks per K/V row
   static constexpr int PER_T = BK * CH / NT;    // chunks per thread per tensor
   static constexpr int NKB = BK / 32;           // 32-key score blocks per tile
@@ -56,9 +62,9 @@ struct AttnCfg {
   static constexpr int NPC = BK / 16;           // 16-key steps of P V
   static constexpr int TILE_BYTES = BK * D * E;
   // bf16 matrix steps read their LDS fragments this many MFMA slots ahead
-  static constexpr int FRAG_AHEAD = 3;
+  static constexpr int FRAG_AHEAD = THREE ? 2 : 3;
   static_assert(PER_T >= 1 && BK * CH % NT == 0, "tile must split over the workgroup");
-  static constexpr int MIN_WAVES_PER_EU = (RB == 2) ? 1 : 2;
+  static constexpr int MIN_WAVES_PER_EU = THREE ? 3 : 2;
 };
 
 // Scheduler hints for a run of NS matrix-core slots whose LDS operand (R
@@ -94,7 +100,7 @@ __device__ __forceinline__ void key_span(const AttnArgs& a, bool swa, int bq, in
 // softmax state and unnormalised O, and the per-tile step.
 template <typename T, int D, bool SWA>
 struct AttnWave {
-  using C = AttnCfg<T, D>;
+  using C = AttnCfg<T, D, SWA>;
   using frag = typename Elem<T>::frag;
   frag qf[C::NC];
   f32x16 acc[C::NDB];
@@ -304,9 +310,9 @@ struct AttnWave {
 // base is the tile and whose size ends at row n_kv: the lane offsets are
 // loop-invariant registers (no per-load address arithmetic), and rows at or
 // past n_kv are never read -- they load as zeros (always masked out).
-template <typename T, int D>
+template <typename T, int D, bool SWA>
 struct TileStager {
-  using C = AttnCfg<T, D>;
+  using C = AttnCfg<T, D, SWA>;
   static constexpr int ROWB = D * C::E;   // bytes per K/V row
   unsigned koff[C::PER_T], voff[C::PER_T];
   const char* kbase;
@@ -364,8 +370,8 @@ __device__ __forceinline__ void tile_landed() { asm volatile("s_waitcnt vmcnt(0)
 // One 4-wave workgroup per query tile.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool SWA>
-__global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_EU)) void attn_fwd_kernel(AttnArgs a) {
-  using C = AttnCfg<T, D>;
+__global__ __launch_bounds__((AttnCfg<T, D, SWA>::NT), (AttnCfg<T, D, SWA>::MIN_WAVES_PER_EU)) void attn_fwd_kernel(AttnArgs a) {
+  using C = AttnCfg<T, D, SWA>;
   // Two buffer sets as distinct LDS objects, used in a statically alternating
   // order (the tile loop is unrolled by two): the compiler can then see that
   // the asynchronous loads into one set never alias reads of the other, and
@@ -399,7 +405,7 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
   int t_lo, t_hi;
   key_span(a, SWA, C::BQ, C::BK, qt, t_lo, t_hi);
 
-  TileStager<T, D> st;
+  TileStager<T, D, SWA> st;
   st.init(kbase, vbase, a.n_kv, w, l);
   st.zero(kbuf0, vbuf0, kbuf1, vbuf1, l);
 
@@ -425,7 +431,7 @@ __global__ __launch_bounds__((AttnCfg<T, D>::NT), (AttnCfg<T, D>::MIN_WAVES_PER_
 
 template <typename T, int D, bool SWA>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t stream) {
-  using C = AttnCfg<T, D>;
+  using C = AttnCfg<T, D, SWA>;
   const int nqt = (a.Nq + C::BQ - 1) / C::BQ;
   const long long nblocks = (long long)nqt * a.B * a.Hq;
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, SWA>), dim3((unsigned)nblocks), dim3(C::NT), 0, stream, a);
