@@ -336,26 +336,30 @@ __global__ __launch_bounds__(256, 2) void linear_kernel(LinArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 form with a wide tile: 256 weight rows x 256 tokens per workgroup, 4
-// waves of 128 x 128 (a 4 x 4 block of 32x32 MFMA tiles, the accumulators in
-// the matrix-core register file), k in stages of 32 through a 4-stage LDS
-// ring filled by direct global -> LDS loads three stages ahead.  Per k step a
-// wave reads 8 fragments for 16 MFMAs (0.5 KB of LDS per MFMA, half the 64 x 64
-// tile's), and the loads in flight cover the HBM latency.  The RMSNorm sums of
+// bf16 form with a wide tile: TM = 64 NI weight rows (192 or 256) x TN
+// tokens (256 or 128) per workgroup, 4 waves of TM/2 x TN/2 (an NI x TN/64
+// block of 32x32 MFMA tiles, the accumulators in the matrix-core register
+// file), k in stages of 32 through a 4-stage LDS ring filled by direct global
+// -> LDS loads three stages ahead.  At 256 x 256 a wave reads 8 fragments per
+// k step for 16 MFMAs (0.5 KB of LDS per MFMA, half the 64 x 64 tile's), and
+// the loads in flight cover the HBM latency.  The row count per tile is
+// chosen per shape so that the tiles fill whole rounds of the chip: the 3B
+// block's 3072-wide products make 16 x 16 tiles of 192 x 256 (one round
+// instead of three quarters of one with 256 x 256), its Q/K/V product (5120
+// rows) 27 x 16 (1.7 rounds instead of 1.25).  (320-row tiles would make one
+// round of the latter but need more than 512 registers per lane.)  The RMSNorm sums of
 // squares are taken from the staged token rows in LDS; a norm gain is staged
 // with each k slice and applied to the token fragments in registers (x * gamma
 // rounded to bf16, as in the 128 x 128 form).
 // ---------------------------------------------------------------------------
 namespace wide {
-constexpr int TM = 256;                 // weight rows per tile
 constexpr int BK = 32;                  // k per stage: 64 bytes per row
 constexpr int NST = 4;                  // ring stages
-constexpr int OPW = 256 * 64;           // the weight operand of one stage (bytes)
 constexpr int GB = 256;                 // per-wave gain slice of one stage (64 bytes used)
-template <int TN>
-constexpr int stage_bytes() { return OPW + TN * 64 + 4 * GB; }
-template <int TN>
-constexpr int lds_bytes() { return NST * stage_bytes<TN>() + 512 * 4; }   // ring, then rs[256], ssp[256]
+template <int TM, int TN>
+constexpr int stage_bytes() { return TM * 64 + TN * 64 + 4 * GB; }   // weight rows, token rows, gain
+template <int TM, int TN>
+constexpr int lds_bytes() { return NST * stage_bytes<TM, TN>() + 512 * 4; }   // ring, then rs[256], ssp[256]
 }  // namespace wide
 
 // 16-byte chunk swizzle for 64-byte rows: rows r, r+4, r+8, r+12 (which share
@@ -396,12 +400,16 @@ template <int N>
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// TN tokens per tile (256, or 128 when that keeps more of the chip busy):
-// 4 waves as 2 (weight-row halves of 128) x 2 (token halves of TN / 2).
-template <int MODE, bool GAIN, int TN>
+// TN tokens per tile (256, or 128 when that keeps more of the chip busy),
+// NI 32-row blocks per wave: 4 waves as 2 (weight-row halves of TM / 2) x 2
+// (token halves of TN / 2).
+template <int MODE, bool GAIN, int TN, int NI>
 __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   using namespace wide;
-  constexpr int STB = stage_bytes<TN>();
+  constexpr int TM = 64 * NI;             // weight rows per tile
+  constexpr int OPW = TM * 64;            // the weight operand of one stage (bytes)
+  static_assert(MODE != kLinSwiGLU || NI == 4, "the SwiGLU row interleave is laid out for 256 rows");
+  constexpr int STB = stage_bytes<TM, TN>();
   constexpr int NJ = TN / 64;             // 32-token blocks per wave
   constexpr int XR = TN / 64;             // token-operand loads per thread per stage
   constexpr int TPT = 256 / TN;           // threads per token for the norm sums
@@ -409,13 +417,14 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   float* rs_lds = reinterpret_cast<float*>(ring + NST * STB);
   float* ssp_lds = rs_lds + 256;
   constexpr bool NORM = MODE != kLinResidual;
-  constexpr int PER = 4 + XR + (GAIN ? 1 : 0);   // loads per thread per stage
+  constexpr int PER = NI + XR + (GAIN ? 1 : 0);   // loads per thread per stage
+  constexpr int NR = NI > XR ? NI : XR;            // staging slots per thread
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, r32 = l & 31;
   const int wf = w >> 1, wt = w & 1;
   const int M = a.B * a.N;
-  constexpr int FPT = MODE == kLinSwiGLU ? 128 : 256;   // output features per tile
+  constexpr int FPT = MODE == kLinSwiGLU ? 128 : TM;   // output features per tile
   const int nft = (a.F + FPT - 1) / FPT;
   const int id = blockIdx.x;
   int tt, ft;
@@ -432,26 +441,28 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   // staging addresses: slot P = 256 r + tid of an operand holds row P / 4 at
   // physical chunk P % 4 (logical chunk (P % 4) ^ wswz(row)); rows past the
   // end are clamped (finite data, never stored)
-  const char* wsrc[4];
+  const char* wsrc[NI];
   const char* xsrc[XR];
   const int dh = a.x_heads > 0 ? a.K / a.x_heads : a.K;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < NR; ++r) {
     const int slot = 256 * r + tid;
     const int row = slot >> 2, lch = (slot & 3) ^ wswz(row);
-    const void* wm;
-    int fr;
-    if constexpr (MODE == kLinSwiGLU) {
-      const int blk = (row >> 5) & 3;
-      fr = min(ft * 128 + (row >> 7) * 64 + (blk >> 1) * 32 + (row & 31), a.F - 1);
-      wm = (blk & 1) ? a.w1 : a.w0;
-    } else {
-      const int f = min(ft * TM + row, a.F - 1);
-      if (MODE == kLinQKV && f >= a.f2) { wm = a.w2; fr = f - a.f2; }
-      else if (MODE == kLinQKV && f >= a.f1) { wm = a.w1; fr = f - a.f1; }
-      else { wm = a.w0; fr = f; }
+    if (r < NI) {
+      const void* wm;
+      int fr;
+      if constexpr (MODE == kLinSwiGLU) {
+        const int blk = (row >> 5) & 3;
+        fr = min(ft * 128 + (row >> 7) * 64 + (blk >> 1) * 32 + (row & 31), a.F - 1);
+        wm = (blk & 1) ? a.w1 : a.w0;
+      } else {
+        const int f = min(ft * TM + row, a.F - 1);
+        if (MODE == kLinQKV && f >= a.f2) { wm = a.w2; fr = f - a.f2; }
+        else if (MODE == kLinQKV && f >= a.f1) { wm = a.w1; fr = f - a.f1; }
+        else { wm = a.w0; fr = f; }
+      }
+      wsrc[r] = static_cast<const char*>(wm) + (size_t)fr * a.K * 2 + lch * 16;
     }
-    wsrc[r] = static_cast<const char*>(wm) + (size_t)fr * a.K * 2 + lch * 16;
     if (r < XR) {
       const int trow = min(t0 + row, M - 1);
       if (a.x_heads > 0) {
@@ -473,9 +484,9 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
       xo = ((size_t)h * a.N * dh + c0) * 2;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < NR; ++r) {
       const unsigned m0 = __builtin_amdgcn_readfirstlane(sb + (unsigned)((256 * r + 64 * w) * 16));
-      dma16(wsrc[r] + wo, m0);
+      if (r < NI) dma16(wsrc[r] + wo, m0);
       if (r < XR) dma16(xsrc[r] + xo, m0 + OPW);
     }
     if constexpr (GAIN) {
@@ -484,21 +495,21 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
     }
   };
 
-  f32x16 acc[4][NJ];
+  f32x16 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
   float ss = 0.f;
 
-  // Fragments of one k step (16 deep) of a stage: 4 weight-row blocks, NJ token blocks.
+  // Fragments of one k step (16 deep) of a stage: NI weight-row blocks, NJ token blocks.
   struct Frags {
-    bf16x8 a[4], b[NJ];
+    bf16x8 a[NI], b[NJ];
   };
   auto read_frags = [&](int ks, int kc, Frags& f) __attribute__((always_inline)) {
     const char* S = ring + (ks & (NST - 1)) * STB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = wide_frag(S, wf * 128 + i * 32 + r32, kc, g);
+    for (int i = 0; i < NI; ++i) f.a[i] = wide_frag(S, wf * (TM / 2) + i * 32 + r32, kc, g);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) f.b[j] = wide_frag(S + OPW, wt * (TN / 2) + j * 32 + r32, kc, g);
     if constexpr (GAIN) {
@@ -511,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   };
   auto mma_frags = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = mma32(f.a[i], f.b[j], acc[i][j]);
   };
@@ -557,9 +568,9 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
   landed(0);
   Frags f0, f1;
   read_frags(0, 0, f0);
-  constexpr int NM = 4 * NJ;                                 // MFMAs per k step
-  constexpr int NR0 = 4 + NJ + (NORM ? 4 / TPT : 0);         // LDS reads in the first half
-  constexpr int NR1 = 4 + NJ;
+  constexpr int NM = NI * NJ;                                // MFMAs per k step
+  constexpr int NR0 = NI + NJ + (NORM ? 4 / TPT : 0);        // LDS reads in the first half
+  constexpr int NR1 = NI + NJ;
   static_assert(NR0 <= NM && NR1 <= NM, "one read per MFMA");
   for (int ks = 0; ks + 1 < nks; ++ks) {
     read_frags(ks, 1, f1);
@@ -599,7 +610,7 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
     lds_barrier();
   }
 
-  // acc[i][j][e] = C^T[tile row wf*128 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*TN/2 + j*32 + r32]
+  // acc[i][j][e] = C^T[tile row wf*TM/2 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*TN/2 + j*32 + r32]
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int tl = wt * (TN / 2) + j * 32 + r32;
@@ -623,10 +634,10 @@ __global__ __launch_bounds__(256, 1) void linear_wide_kernel(LinArgs a) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-          const int f = ft * TM + wf * 128 + i * 32 + 8 * qd + 4 * g;
+          const int f = ft * TM + wf * (TM / 2) + i * 32 + 8 * qd + 4 * g;
           if (f >= a.F) continue;
           float v0 = acc[i][j][4 * qd] * rs, v1 = acc[i][j][4 * qd + 1] * rs;
           float v2 = acc[i][j][4 * qd + 2] * rs, v3 = acc[i][j][4 * qd + 3] * rs;
@@ -666,30 +677,48 @@ static int cu_count() {
   return n;
 }
 
-template <int MODE, bool GAIN, int TN>
+template <int MODE, bool GAIN, int TN, int NI>
 static void launch_wide(const LinArgs& a, long long tiles, hipStream_t stream) {
-  constexpr int lds = wide::lds_bytes<TN>();
+  constexpr int lds = wide::lds_bytes<64 * NI, TN>();
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_wide_kernel<MODE, GAIN, TN>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&linear_wide_kernel<MODE, GAIN, TN, NI>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((linear_wide_kernel<MODE, GAIN, TN>), dim3((unsigned)tiles), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((linear_wide_kernel<MODE, GAIN, TN, NI>), dim3((unsigned)tiles), dim3(256), lds, stream, a);
 }
 
+// Tile shape per problem: the one with the best expected rate -- a per-CU
+// rate for the shape (from its LDS bytes per MFMA: 256 x 256 1.0, 192 x 256
+// 0.95, 256 x 128 0.9) times the useful fraction of its padded tiles times
+// the fraction of the last round's CUs that are busy (one workgroup per CU).
 template <int MODE, bool GAIN>
 static void launch_wide_tn(const LinArgs& a, hipStream_t stream) {
-  // tokens per tile: the one that leaves fewer compute units idle in the last
-  // round of workgroups (one workgroup per CU), the narrower tile counted at
-  // 0.9 of the wide one's rate (it reads 1.5x the LDS bytes per MFMA)
-  const int M = a.B * a.N, cus = cu_count();
-  constexpr int FPT = MODE == kLinSwiGLU ? 128 : 256;
-  const long long nft = (a.F + FPT - 1) / FPT;
-  const long long t256 = (long long)((M + 255) / 256) * nft, t128 = (long long)((M + 127) / 128) * nft;
-  auto eff = [&](long long t, double rate) { return rate * (double)t / (double)(((t + cus - 1) / cus) * cus); };
-  if (eff(t256, 1.0) >= eff(t128, 0.9)) launch_wide<MODE, GAIN, 256>(a, t256, stream);
-  else launch_wide<MODE, GAIN, 128>(a, t128, stream);
+  const long long M = (long long)a.B * a.N, cus = cu_count();
+  struct Shape { int tm, tn; double rate; };
+  const Shape shapes[] = {{256, 256, 1.0}, {256, 128, 0.9}, {192, 256, 0.95}};
+  int best = 0;
+  double best_eff = -1.0;
+  long long best_tiles = 0;
+  for (int i = 0; i < 3; ++i) {
+    const Shape& sh = shapes[i];
+    if (MODE == kLinSwiGLU && sh.tm != 256) continue;
+    const int fpt = MODE == kLinSwiGLU ? 128 : sh.tm;
+    const long long nft = (a.F + fpt - 1) / fpt, ntt = (M + sh.tn - 1) / sh.tn, tiles = nft * ntt;
+    const double useful = (double)a.F / (double)(nft * fpt) * (double)M / (double)(ntt * sh.tn);
+    const double eff = sh.rate * useful * (double)tiles / (double)(((tiles + cus - 1) / cus) * cus);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = i;
+      best_tiles = tiles;
+    }
+  }
+  switch (best) {
+    case 0: launch_wide<MODE, GAIN, 256, 4>(a, best_tiles, stream); break;
+    case 1: launch_wide<MODE, GAIN, 128, 4>(a, best_tiles, stream); break;
+    default: if constexpr (MODE != kLinSwiGLU) launch_wide<MODE, GAIN, 256, 3>(a, best_tiles, stream); break;
+  }
 }
 
 // ---------------------------------------------------------------------------
