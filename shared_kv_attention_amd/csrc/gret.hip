@@ -25,9 +25,10 @@
 //             (R^T staged in LDS), then an attention-like tile loop with
 //             decay weights e^{L_n - L_m} (formed per pair from the
 //             difference, so a strong gate can never overflow) instead of a
-//             softmax, with direct global -> LDS double-buffered K/V tiles,
-//             on the same accumulator.  The heavier second halves of the
-//             chunks (four key tiles instead of two) are dispatched first.
+//             softmax, with direct global -> LDS double-buffered 32-key K/V
+//             tiles (three workgroups per CU), on the same accumulator.  The
+//             heavier second halves of the chunks (twice the key tiles) are
+//             dispatched first.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_lds.hpp"
@@ -214,15 +215,22 @@ __global__ __launch_bounds__(256) void gret_scan_kernel(GretArgs a) {
 //    decays) are staged global -> LDS directly and double-buffered
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
+__global__ __launch_bounds__(256, 3) void gret_out_kernel(GretArgs a) {
   using C = GretCfg<D>;
-  constexpr int PER_T = C::BK * C::CH / 256;    // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) char tiles[4 * C::TILE];
-  char* const kt0 = tiles;
-  char* const vt0 = tiles + C::TILE;
-  char* const kt1 = tiles + 2 * C::TILE;
-  char* const vt1 = tiles + 3 * C::TILE;
-  __shared__ __attribute__((aligned(16))) float lg0[C::BK], lg1[C::BK];
+  // 32-key tiles: with at most 168 VGPRs and 48 KB of LDS, three workgroups
+  // share a CU (the 3B shape's 768 workgroups are then one round, not 1.5)
+  constexpr int BK = 32;                         // key rows per LDS tile
+  constexpr int TB = BK * D * 2;                 // bytes of one K or V tile
+  constexpr int PER_T = BK * C::CH / 256;        // 16-byte chunks per thread per tile
+  static_assert(2 * TB <= D * D * 2, "the second tile set fits in the R^T region");
+  // set 0 as its own LDS objects; the chunk's R^T (D rows, K-tile layout)
+  // first, and once it has been used, set 1, in a region of its own -- so the
+  // loads into one set are never taken for writes to the other
+  __shared__ __attribute__((aligned(16))) char kt0[TB], vt0[TB];
+  __shared__ __attribute__((aligned(16))) char rset[D * D * 2];
+  char* const kt1 = rset;
+  char* const vt1 = rset + TB;
+  __shared__ __attribute__((aligned(16))) float lg0[64], lg1[64];   // one log-decay per lane of wave 0
   const int nrb = a.chunk / 128;
   // linear block index -> (row block, descending: the later rows see more keys; head; chunk)
   const int nblk_bh = a.nc * a.B * a.H;
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
   const size_t hrow = (size_t)bh * a.N;
   const int k_end = min(q0 + 127, a.N - 1);     // last key any row here can see
   const int pw1 = min(wq0 + 31, a.N - 1);       // last row of this wave
-  const int ntiles = (k_end - c0) / C::BK + 1;
+  const int ntiles = (k_end - c0) / BK + 1;
 
   // ---- tile staging by DMA: slot P = 256 r + tid of a tile holds row P / CH
   // at physical chunk P % CH; rows past k_end re-read row k_end (finite data,
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
     voff[r] = (unsigned)(row * D * 2 + ((pch ^ swz_v<C::CH>(row)) << 4));
   }
   auto load_tile = [&](int t, char* kd, char* vd, float* lgd) {
-    const int k0 = c0 + t * C::BK;
+    const int k0 = c0 + t * BK;
 #pragma unroll
     for (int r = 0; r < PER_T; ++r) {
       const int over = k0 + srow[r] - k_end;
@@ -276,15 +284,15 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
     }
   };
   load_tile(0, kt0, vt0, lg0);
-  // R^T of the chunk (D rows) into the second buffer set, K-tile layout
+  // R^T of the chunk (D rows) into its region, K-tile layout, BK rows per tile
   {
     const char* rbase = static_cast<const char*>(a.rin) + ((size_t)bh * a.nc + c) * D * D * 2;
 #pragma unroll
-    for (int h = 0; h < D / C::BK; ++h)
+    for (int h = 0; h < D / BK; ++h)
 #pragma unroll
       for (int r = 0; r < PER_T; ++r)
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(rbase + h * C::TILE + koff[r]),
-                                         (__attribute__((address_space(3))) void*)(kt1 + h * C::TILE + (256 * r + 64 * w) * 16),
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(rbase + h * TB + koff[r]),
+                                         (__attribute__((address_space(3))) void*)(rset + h * TB + (256 * r + 64 * w) * 16),
                                          16, 0, 0);
   }
 
@@ -305,10 +313,10 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
   {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const char* rt = kt1 + (db >> 1) * C::TILE;
+      const char* rt = rset + db * TB;   // R^T rows db*32 .. db*32 + 31
       bf16x8 rf[C::NC];
 #pragma unroll
-      for (int cc = 0; cc < C::NC; ++cc) rf[cc] = lds_frag_k<bf16, C::CH>(rt, (db & 1) * 32 + r32, cc, g);
+      for (int cc = 0; cc < C::NC; ++cc) rf[cc] = lds_frag_k<bf16, C::CH>(rt, r32, cc, g);
       acc[db] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < C::NC; ++cc) acc[db] = mma32(rf[cc], qf[cc], acc[db]);
@@ -323,34 +331,27 @@ __global__ __launch_bounds__(256, 2) void gret_out_kernel(GretArgs a) {
       __attribute__((always_inline)) {
     const bool has_next = t + 1 < ntiles;
     if (has_next) load_tile(t + 1, kn, vn, lgn);
-    const int k0 = c0 + t * C::BK;
+    const int k0 = c0 + t * BK;
     if (wave_live && k0 <= pw1) {
-      // S^T = K Q^T; element i of block kb <-> key k0 + kb*32 + 16*(i/8) + 8g + i%8
-      f32x16 s[2];
+      // S^T = K Q^T; element i <-> key k0 + 16*(i/8) + 8g + i%8
+      f32x16 s = f32x16{};
+      const int krow = sigma(r32);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int krow = kb * 32 + sigma(r32);
-#pragma unroll
-        for (int cc = 0; cc < C::NC; ++cc) s[kb] = mma32(lds_frag_k<bf16, C::CH>(kt, krow, cc, g), qf[cc], s[kb]);
-      }
+      for (int cc = 0; cc < C::NC; ++cc) s = mma32(lds_frag_k<bf16, C::CH>(kt, krow, cc, g), qf[cc], s);
       // decay weights, masked by m <= n (a select: 2^{L_n - L_m} may
       // overflow above the diagonal)
-      bf16x8 pf[4];
+      bf16x8 pf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int off = kb * 32 + 16 * (i >> 3) + 8 * g + (i & 7);
-          const float wgt = s[kb][i] * __builtin_amdgcn_exp2f(l_n - lgt[off]);
-          pf[2 * kb + (i >> 3)][i & 7] = (bf16)((k0 + off <= n) ? wgt : 0.f);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int off = 16 * (i >> 3) + 8 * g + (i & 7);
+        const float wgt = s[i] * __builtin_amdgcn_exp2f(l_n - lgt[off]);
+        pf[i >> 3][i & 7] = (bf16)((k0 + off <= n) ? wgt : 0.f);
       }
       // O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) acc[db] = mma32(lds_frag_vt<bf16, C::CH>(vt, cc, db, l), pf[cc], acc[db]);
+        for (int cc = 0; cc < 2; ++cc) acc[db] = mma32(lds_frag_vt<bf16, C::CH>(vt, cc, db, l), pf[cc], acc[db]);
       }
     }
     if (has_next) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
