@@ -345,9 +345,10 @@ size_t yoco_kv_quantize_fp8_workspace_bytes(int Hkv);
  * Achievable-peak microbenchmarks (diagnostics, not part of the method): what
  * this chip reaches at its clock under load, beside the spec peaks.
  * yoco_peak_hbm_read streams `bytes` (a multiple of 16) of `buf` once with
- * `blocks` workgroups of 256 threads and writes one wrapping 32-bit sum of
- * the words each workgroup read to partial[blocks] (their sum, modulo 2^32,
- * is the sum of every 32-bit word of the buffer).
+ * `blocks` workgroups of 256 threads, each reading one contiguous 1/blocks of
+ * the buffer, and writes one wrapping 32-bit sum of the words each workgroup
+ * read to partial[blocks] (their sum, modulo 2^32, is the sum of every 32-bit
+ * word of the buffer).
  * yoco_peak_mfma_bf16 runs `blocks` workgroups of 4 waves, each wave `iters`
  * rounds of 8 independent 32x32x16 bf16 MFMAs (2^18 flops per round) on
  * operands of ones, and writes out[4 * blocks] = 128 * iters per wave
