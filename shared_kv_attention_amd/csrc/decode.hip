@@ -207,7 +207,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int vkey = min(key0 + j, key_end - 1);
-      vr[j] = *reinterpret_cast<const vword*>(vb + (size_t)vkey * D);
+      // V rows are consumed whole by this one load (K rows are split over two
+      // loads per 128-byte line): stream them non-temporally (+8 % on the 32K
+      // decode; K the same way loses a quarter, its line's second load misses)
+      vr[j] = __builtin_nontemporal_load(reinterpret_cast<const vword*>(vb + (size_t)vkey * D));
     }
   };
 
