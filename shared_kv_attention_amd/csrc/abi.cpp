@@ -33,14 +33,22 @@ double rope_log2(float theta) {
 }
 
 struct DecodeLayout {
-  int n_splits, chunk, n_hg;
+  int n_splits, chunk, n_hg, full_lines;
   size_t o_bytes, ml_bytes, total;
 };
 
-DecodeLayout decode_layout(int B, int Hq, int Hkv, int ctx, int d) {
+// The workspace holds the partials of the plan for kDecodeMaxWorkgroups
+// (what the size queries return, whatever the dtype).  A bf16 d = 128 cache
+// whose splits are long enough is read by the whole-line K form, planned for
+// that form's own workgroup target (never more splits).
+DecodeLayout decode_layout(int B, int Hq, int Hkv, int ctx, int d, int kv_kind = 1) {
   DecodeLayout L{};
-  yoco::decode_plan(B, Hq, Hkv, ctx, &L.n_splits, &L.chunk, &L.n_hg);
-  const size_t rows = (size_t)B * Hq * L.n_splits;
+  yoco::decode_plan(B, Hq, Hkv, ctx, yoco::kDecodeMaxWorkgroups, &L.n_splits, &L.chunk, &L.n_hg);
+  const int cap_splits = L.n_splits;
+  L.full_lines = kv_kind == 1 && d == 128 && L.chunk >= yoco::kDecodeFullLineMinChunk;
+  if (L.full_lines)
+    yoco::decode_plan(B, Hq, Hkv, ctx, yoco::decode_workgroup_target(kv_kind, d), &L.n_splits, &L.chunk, &L.n_hg);
+  const size_t rows = (size_t)B * Hq * cap_splits;
   L.o_bytes = align16(rows * d * sizeof(float));
   L.ml_bytes = align16(rows * sizeof(float));
   L.total = L.o_bytes + 2 * L.ml_bytes;
@@ -294,7 +302,8 @@ yoco_status yoco_cross_attn_decode(const void* q, const void* k_cache, const voi
       (lse && !aligned(lse, 4)) || (ctx_lens && !aligned(ctx_lens, 4)) || (k_scale && !aligned(k_scale, 4)) ||
       (v_scale && !aligned(v_scale, 4)))
     return YOCO_ERR_ALIGN;
-  const DecodeLayout L = decode_layout(B, Hq, Hkv, ctx, d);
+  const int kk = kv_dtype == YOCO_F32 ? 0 : (kv_dtype == YOCO_BF16 ? 1 : 2);
+  const DecodeLayout L = decode_layout(B, Hq, Hkv, ctx, d, kk);
   if (!workspace || workspace_bytes < L.total) return YOCO_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
@@ -318,9 +327,9 @@ yoco_status yoco_cross_attn_decode(const void* q, const void* k_cache, const voi
   a.n_splits = L.n_splits;
   a.chunk = L.chunk;
   a.n_hg = L.n_hg;
+  a.full_lines = L.full_lines;
   a.scale_log2 = resolve_scale(softmax_scale, d) * 1.4426950408889634f;
   const int qk = q_dtype == YOCO_F32 ? 0 : 1;
-  const int kk = kv_dtype == YOCO_F32 ? 0 : (kv_dtype == YOCO_BF16 ? 1 : 2);
   return launched(yoco::launch_decode(a, qk, kk, d, as_stream(stream)));
 }
 
@@ -348,7 +357,7 @@ yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new,
       (k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)) || (lse && !aligned(lse, 4)))
     return YOCO_ERR_ALIGN;
   const int ctx = pos + 1 < W ? pos + 1 : W;   // slots 0 .. ctx-1 hold the window
-  const DecodeLayout L = decode_layout(B, Hq, Hkv, ctx, d);
+  const DecodeLayout L = decode_layout(B, Hq, Hkv, ctx, d, dtype == YOCO_F32 ? 0 : 1);
   if (!workspace || workspace_bytes < L.total) return YOCO_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
   const int esz = dtype == YOCO_F32 ? 4 : 2;
@@ -376,6 +385,7 @@ yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new,
   a.n_splits = L.n_splits;
   a.chunk = L.chunk;
   a.n_hg = L.n_hg;
+  a.full_lines = L.full_lines;
   a.scale_log2 = resolve_scale(softmax_scale, d) * 1.4426950408889634f;
   const int kind = dtype == YOCO_F32 ? 0 : 1;
   return launched(yoco::launch_decode(a, kind, kind, d, as_stream(stream)));

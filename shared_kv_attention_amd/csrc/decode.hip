@@ -13,11 +13,16 @@
 //    4) query heads of its KV head.  Splits give thousands of workgroups even
 //    for one sequence, so all 256 CUs stream concurrently.
 //  * Keys are processed 16 at a time.  For q . k, lane l holds key l%16 and
-//    dims {32c + 8*(l/16) + j}: 16-byte row loads (8-byte for fp8 codes) in
-//    the natural operand layout of the 16x16x32 matrix core, so K needs no
-//    LDS staging.  The A operand is the query block replicated 4 times
-//    (row r -> head r%4), so every lane receives all 4 heads' scores of its
-//    own key.
+//    dims {32c + 8*(l/16) + j}, the operand layout of the 16x16x32 matrix
+//    core, so K needs no LDS staging.  fp8 and float32 caches load that
+//    layout directly (one 8- or 32-byte row piece per lane and step), and so
+//    do bf16 caches with short splits.  With long splits bf16 caches load
+//    whole 128-byte lines instead -- each instruction 8 keys x one line,
+//    non-temporal -- and a row rotate by 8 within 16-lane rows
+//    (DPP, written into half of the lanes) rearranges two such loads into
+//    the fragments of two matrix steps.  The A operand is the query block
+//    replicated 4 times (row r -> head r%4), so every lane receives all 4
+//    heads' scores of its own key.
 //  * For P V each lane owns D/64 output dims across all keys: one V row is
 //    read by one load instruction (fully contiguous), and the per-lane
 //    accumulator is only 4 heads x D/64 floats -- no cross-lane reduction of
@@ -28,9 +33,11 @@
 //    float32 FMAs.
 //  * Online softmax in the exp2 domain; the running max per head is raised
 //    only when a block exceeds it by 2^8 (wave-uniform branch).
-//  * The next block's loads are issued before the current block is used; for
-//    bf16 caches the K loads that first touch each 128-byte line go two
-//    blocks ahead.
+//  * Loads run ahead of use: V one block; K one block (fp8, float32), two
+//    for the bf16 instruction that first touches a line, three in the
+//    whole-line form.  The whole-line form takes 3 waves per SIMD instead of
+//    4 and pays only on long splits (>= 1024 keys: the 32K x B16 and 1M
+//    decodes, +3 %); shorter splits keep the operand-layout form.
 //  * fp8-e4m3 caches: codes are decoded in registers (exactly, to bf16 for
 //    the matrix core and to f32 for P V); the per-head scales factor out of
 //    both products: the K scale is folded into the softmax scale and the V
@@ -136,7 +143,7 @@ __device__ __forceinline__ int decode_ctx(const DecodeArgs& a, int b) {
   return min(max((int)a.ctx_lens[b], 1), a.ctx);
 }
 
-template <typename QT, typename KVT, int D>
+template <typename QT, typename KVT, int D, bool KF>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using MT = typename KvTraits<KVT>::mma_t;
   static_assert(sizeof(MT) == sizeof(QT), "query dtype must match the matrix-core dtype");
@@ -188,43 +195,87 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     for (int e = 0; e < DPL; ++e) acc[i][e] = 0.f;
   }
 
-  // One K load instruction covers 16 rows x 32 dims, i.e. half of a 128-byte
-  // line of each bf16 row.  For bf16 caches the instruction that touches a
-  // line first ("lead") is issued two blocks ahead and the other one block
-  // ahead, so the line's fill is already under way when it arrives (+3% on
-  // the 32K decode; K and V are still read once).  fp8 and f32 caches issue
-  // all K loads one block ahead (the staggering measured slower for fp8).
-  auto is_lead = [](int c) { return sizeof(KVT) == 2 && (c & 1) == 0; };
+  // Operand-layout K loads (fp8, float32, and bf16 with short splits): lane
+  // (G, r16) loads key r16's elements 32c + 8G .. +7 for each step c.  One
+  // instruction covers 16 rows x 32 dims, half of a 128-byte line of each
+  // bf16 row; for bf16 the instruction that touches a line first ("lead") is
+  // issued two blocks ahead and the other one block ahead, so the line's fill
+  // is under way when the second arrives (+3 % on the 32K decode; fp8 measured
+  // slower with it and keeps one block).
+  constexpr bool KFULL = KF && sizeof(KVT) == 2;
+  auto is_lead = [](int c) { return !KFULL && sizeof(KVT) == 2 && (c & 1) == 0; };
   Raw8<KVT> kc[NC], kn[NC], k2[NC];
-  vword vc[16], vn[16];
   auto load_k = [&](int key0, Raw8<KVT>* kr, bool lead) {
     const int kkey = min(key0 + r16, key_end - 1);   // never read rows >= ctx_b
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       if (is_lead(c) == lead) kr[c] = load_raw8<KVT>(kb + (size_t)kkey * D + 32 * c);
   };
+  // Whole-line K loads (bf16, long splits): instruction (line L, half h)
+  // gives lane (G, k) the 16 bytes of key 8h + (k & 7) at element
+  // 64L + 32(k >> 3) + 8G: 8 keys x one full line per instruction, so it
+  // streams non-temporally (the operand-layout loads above touch each line
+  // with two instructions and must stay cached).  A row rotate by 8 within
+  // each 16-lane row, written into half of the lanes (bank mask), turns the
+  // two halves of line L into the fragments of steps 2L and 2L + 1 (lane
+  // (G, k): key k, elements 32c + 8G .. +7).  Three blocks in flight.
+  constexpr int NL = D / 64;
+  const KVT* kb0 = static_cast<const KVT*>(a.k) + head_off * D;
+  auto load_kf = [&](int key0, u32x4 (&raw)[NL][2]) {
+#pragma unroll
+    for (int L = 0; L < NL; ++L)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = min(key0 + 8 * h + (r16 & 7), key_end - 1);
+        raw[L][h] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(kb0 + (size_t)key * D + 64 * L + 32 * (r16 >> 3) + 8 * G));
+      }
+  };
+  auto kf_frags = [&](const u32x4 (&raw)[NL][2], Raw8<KVT>* kr) {
+    if constexpr (KFULL) {
+#pragma unroll
+      for (int L = 0; L < NL; ++L)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // row_ror:8 (0x128); banks 2-3 (lanes k >= 8) take the other half's keys
+          kr[2 * L].w[w] = (uint32_t)__builtin_amdgcn_update_dpp((int)raw[L][0][w], (int)raw[L][1][w], 0x128, 0xF, 0xC, false);
+          kr[2 * L + 1].w[w] = (uint32_t)__builtin_amdgcn_update_dpp((int)raw[L][1][w], (int)raw[L][0][w], 0x128, 0xF, 0x3, false);
+        }
+    }
+  };
+  u32x4 kf0[NL][2], kf1[NL][2], kf2[NL][2], kf3[NL][2];
+  vword vc[16], vn[16];
   auto load_v = [&](int key0, vword* vr) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int vkey = min(key0 + j, key_end - 1);
-      // V rows are consumed whole by this one load (K rows are split over two
-      // loads per 128-byte line): stream them non-temporally (+8 % on the 32K
-      // decode; K the same way loses a quarter, its line's second load misses)
+      // each V row is consumed whole by this one load: stream it non-temporally
+      // (+8 % on the 32K decode over cached loads)
       vr[j] = __builtin_nontemporal_load(reinterpret_cast<const vword*>(vb + (size_t)vkey * D));
     }
   };
 
-  load_k(key_begin, kc, true);
-  load_k(key_begin, kc, false);
+  if constexpr (KFULL) {
+    load_kf(key_begin, kf0);
+    if (key_begin + 16 < key_end) load_kf(key_begin + 16, kf1);
+    if (key_begin + 32 < key_end) load_kf(key_begin + 32, kf2);
+  } else {
+    load_k(key_begin, kc, true);
+    load_k(key_begin, kc, false);
+  }
   load_v(key_begin, vc);
-  if (key_begin + 16 < key_end) load_k(key_begin + 16, kn, true);
+  if (!KFULL && key_begin + 16 < key_end) load_k(key_begin + 16, kn, true);
   for (int key0 = key_begin; key0 < key_end; key0 += 16) {
     const bool has_next = key0 + 16 < key_end;
     if (has_next) {
-      load_k(key0 + 16, kn, false);
+      if constexpr (!KFULL) load_k(key0 + 16, kn, false);
       load_v(key0 + 16, vn);
     }
-    if (key0 + 32 < key_end) load_k(key0 + 32, k2, true);
+    if (!KFULL && key0 + 32 < key_end) load_k(key0 + 32, k2, true);
+    if constexpr (KFULL) {
+      if (key0 + 48 < key_end) load_kf(key0 + 48, kf3);
+      kf_frags(kf0, kc);
+    }
 
     // scores: lane (G, r16) receives head i's score of key key0 + r16 in s[i]
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -316,10 +367,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
       }
     }
     if (has_next) {
+      if constexpr (KFULL) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kc[c] = kn[c];
-        if (is_lead(c)) kn[c] = k2[c];
+        for (int L = 0; L < NL; ++L)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            kf0[L][h] = kf1[L][h];
+            kf1[L][h] = kf2[L][h];
+            kf2[L][h] = kf3[L][h];
+          }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          kc[c] = kn[c];
+          if (is_lead(c)) kn[c] = k2[c];
+        }
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) vc[j] = vn[j];
@@ -415,7 +477,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 template <typename QT, typename KVT, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.n_splits, a.Hkv * a.n_hg, a.B);
-  hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D>), grid, dim3(64), 0, stream, a);
+  bool launched = false;
+  if constexpr (sizeof(KVT) == 2 && D == 128) {
+    if (a.full_lines) {
+      hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D, true>), grid, dim3(64), 0, stream, a);
+      launched = true;
+    }
+  }
+  if (!launched) hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D, false>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<QT, D>), dim3(a.Hq, a.B, D / 32), dim3(256), 0, stream, a);

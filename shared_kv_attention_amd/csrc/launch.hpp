@@ -39,6 +39,7 @@ struct DecodeArgs {
   int B, Hq, Hkv, n_cap;
   int n_splits, chunk, n_hg;
   float scale_log2;
+  int full_lines;          // bf16 K read in whole lines, three blocks ahead (long splits)
 };
 
 struct ProjArgs {
@@ -155,8 +156,17 @@ hipError_t launch_gret_norm(const GretNormArgs& a, bool is_bf16, hipStream_t str
 // follows from it.  At most kDecodeMaxSplits splits (the combine pass keeps one
 // weight per split in LDS).
 constexpr int kDecodeMaxSplits = 4096;
-void decode_plan(int B, int Hq, int Hkv, int ctx, int* n_splits, int* chunk, int* n_hg);
-// An upper bound on decode_plan's n_splits for every context length <= ctx.
+// Workgroup targets: at most kDecodeMaxWorkgroups (the workspace is sized for
+// it); decode_workgroup_target gives the one for a kernel form (kv_kind:
+// 0 float32, 1 bf16, 2 fp8).
+constexpr int kDecodeMaxWorkgroups = 4096;
+// bf16 d = 128 splits of at least this many keys use the whole-line K form
+// (three blocks in flight, 3 waves per SIMD) and its own workgroup target.
+constexpr int kDecodeFullLineMinChunk = 1024;
+int decode_workgroup_target(int kv_kind, int d);
+void decode_plan(int B, int Hq, int Hkv, int ctx, int target, int* n_splits, int* chunk, int* n_hg);
+// An upper bound on decode_plan's n_splits for every context length <= ctx
+// and every target <= kDecodeMaxWorkgroups.
 int decode_split_bound(int B, int Hq, int Hkv, int ctx);
 
 }  // namespace yoco

@@ -103,8 +103,41 @@ int main() {
       CHECK((unsigned char*)(a.part_l + rows) <= ws + need);
       CHECK(yoco_cross_attn_decode(P, P, P, nullptr, nullptr, nullptr, ctx, P, nullptr, B, Hq, Hkv, ctx, d, 0.f, YOCO_BF16,
                                    YOCO_BF16, ws, need - 1, nullptr) == YOCO_ERR_WORKSPACE);
+      // every kernel form plans within the same (dtype-independent) workspace;
+      // the bf16 form's smaller workgroup target never gives more splits
+      const int bf16_splits = a.n_splits;
+      const yoco_dtype forms[][2] = {{YOCO_F32, YOCO_F32}, {YOCO_BF16, YOCO_FP8_E4M3}};
+      for (const auto& f : forms) {
+        CHECK(yoco_cross_attn_decode(P, P, P, (float*)P, (float*)P, nullptr, ctx, P, nullptr, B, Hq, Hkv, ctx, d, 0.f,
+                                     f[0], f[1], ws, need, nullptr) == YOCO_OK);
+        const yoco::DecodeArgs& b = yoco::g_decode;
+        CHECK(b.n_splits >= bf16_splits && b.n_splits <= yoco::kDecodeMaxSplits);
+        CHECK((long long)b.n_splits * b.chunk >= ctx && b.chunk % 64 == 0);
+        CHECK((unsigned char*)(b.part_l + (size_t)B * Hq * b.n_splits) <= ws + need);
+      }
     }
     std::free(ws);
+  }
+  {
+    // long bf16 d = 128 splits take the whole-line K form (12-wave-per-CU plan);
+    // short splits, fp8 and float32 caches do not
+    struct Case { int B, Hq, Hkv, ctx, d; yoco_dtype kv; int full; };
+    const Case cases[] = {{16, 32, 8, 32768, 128, YOCO_BF16, 1}, {1, 24, 8, 1 << 20, 128, YOCO_BF16, 1},
+                          {32, 32, 8, 16384, 128, YOCO_BF16, 1}, {1, 24, 8, 131072, 128, YOCO_BF16, 0},
+                          {16, 32, 8, 32768, 64, YOCO_BF16, 0}, {16, 32, 8, 32768, 128, YOCO_FP8_E4M3, 0},
+                          {16, 32, 8, 32768, 128, YOCO_F32, 0}};
+    for (const Case& c : cases) {
+      const size_t need = yoco_cross_attn_decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.ctx, c.d);
+      unsigned char* ws = (unsigned char*)std::malloc(need);
+      const yoco_dtype qd = c.kv == YOCO_F32 ? YOCO_F32 : YOCO_BF16;
+      CHECK(yoco_cross_attn_decode(P, P, P, (float*)P, (float*)P, nullptr, c.ctx, P, nullptr, c.B, c.Hq, c.Hkv, c.ctx,
+                                   c.d, 0.f, qd, c.kv, ws, need, nullptr) == YOCO_OK);
+      const yoco::DecodeArgs& a = yoco::g_decode;
+      CHECK(a.full_lines == c.full);
+      if (c.full) CHECK(a.chunk >= yoco::kDecodeFullLineMinChunk && (long long)a.n_splits * c.B * c.Hkv <= 256 * 12);
+      CHECK((unsigned char*)(a.part_l + (size_t)c.B * c.Hq * a.n_splits) <= ws + need);
+      std::free(ws);
+    }
   }
   {
     const size_t need = yoco_cross_attn_decode_workspace_bytes(2, 8, 2, 100, 128);

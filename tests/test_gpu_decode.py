@@ -21,6 +21,9 @@ DECODE_CASES = [
     (2, 6, 2, 700, 650, [650, 333], 64, "bf16"),
     (2, 12, 2, 300, 300, None, 128, "bf16"),      # 6 query heads per KV head: two head groups
     (1, 4, 4, 5000, 4999, None, 128, "f32"),
+    # splits of 1024 keys: the whole-line K form, with ragged lengths (rows past
+    # each length hold NaN and must never be read)
+    (32, 32, 8, 16384, 16384, [16384, 1, 16383, 1024, 1025, 2047, 5000, 16000] * 4, 128, "bf16"),
 ]
 
 
