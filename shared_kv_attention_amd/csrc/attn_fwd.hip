@@ -8,7 +8,8 @@
 //
 // Design (MI355X-first):
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head); keys are
-//    streamed in tiles of BK rows (64 for bf16) staged through LDS with
+//    streamed in tiles of BK rows (64 for the causal bf16 form, 32 for the
+//    sliding window and for float32) staged through LDS with
 //    double buffering: the next tile's global loads are in flight while the
 //    current tile is multiplied.
 //  * Scores are formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA so
