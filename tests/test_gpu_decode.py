@@ -88,22 +88,28 @@ def test_quantize_fp8_bit_exact(src):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
-def test_decode_fp8_parity():
-    B, Hq, Hkv, n, d = 2, 8, 2, 3000, 128
+@pytest.mark.parametrize("B,Hq,Hkv,n,lens", [
+    (2, 8, 2, 3000, [3000, 1234]),
+    # 32 sequences of ragged length over a 16384-row cache (splits of 1024 keys)
+    (32, 32, 8, 16384, [16384, 1, 16383, 1024, 1025, 2047, 5000, 16000] * 4),
+])
+def test_decode_fp8_parity(B, Hq, Hkv, n, lens):
+    d = 128
+    print(f"fp8 decode parity B={B} Hq={Hq} Hkv={Hkv} n={n}", flush=True)
     q = randn((B, Hq, d), 940, device=DEV)
     kf = randn((B, Hkv, n, d), 941, dtype="f32", device=DEV)
     vf = randn((B, Hkv, n, d), 942, dtype="f32", device=DEV)
     kc, ks = yk.yoco_kv_quantize_fp8(kf)
     vc, vs = yk.yoco_kv_quantize_fp8(vf)
-    cl = torch.tensor([3000, 1234], dtype=torch.int32, device=DEV)
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
     o = yk.yoco_cross_attn_decode(q, kc, vc, n, ctx_lens=cl, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     kd = oracle.dequantize_kv_fp8(kc.cpu().numpy(), ks.cpu().numpy())
     vd = oracle.dequantize_kv_fp8(vc.cpu().numpy(), vs.cpu().numpy())
-    ro, _ = oracle.decode_attention(to64(q), kd, vd, [3000, 1234])
+    ro, _ = oracle.decode_attention(to64(q), kd, vd, lens)
     check(to64(o), ro, "bf16", "fp8 decode", rel_axes=(2,))
     # quantisation error against the unquantised cache is reported, not gated
-    ru, _ = oracle.decode_attention(to64(q), to64(kf), to64(vf), [3000, 1234])
+    ru, _ = oracle.decode_attention(to64(q), to64(kf), to64(vf), lens)
     print("fp8 cache: max |O - O_unquantised| =", np.abs(to64(o) - ru).max())
 
 
