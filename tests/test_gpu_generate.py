@@ -141,3 +141,48 @@ def test_tiny_block_generation_matches_oracle():
             h = h + o.double().cpu().numpy().reshape(B, Hq * d) @ wo.T
         out[:, t] = h
     check(out, ref, "f32", "tiny block generated token by token")
+
+
+def test_generation_step_graph_replays_match_eager():
+    """One generation step (ring decode with its append, the projection append,
+    cross decode) captured as a HIP graph: every replay, with eager work and
+    synchronisations between the replays, reproduces the eager step bitwise.
+    The cross cache is long enough for the whole-line K form of the decode."""
+    B, Hq, Hkv, d, W, D, ctx = 32, 32, 8, 128, 256, 256, 16384
+    pos = ctx - 1
+    kr = randn((B, Hkv, W, d), 970, device=DEV)
+    vr = randn((B, Hkv, W, d), 971, device=DEV)
+    kc = randn((B, Hkv, ctx, d), 972, device=DEV)
+    vc = randn((B, Hkv, ctx, d), 973, device=DEV)
+    wk = randn((Hkv * d, D), 974, std=0.05, device=DEV)
+    wv = randn((Hkv * d, D), 975, std=0.05, device=DEV)
+    qs, qc = randn((B, Hq, d), 976, device=DEV), randn((B, Hq, d), 977, device=DEV)
+    kn, vn = randn((B, Hkv, d), 978, device=DEV), randn((B, Hkv, d), 979, device=DEV)
+    hid = randn((B, 1, D), 980, device=DEV)
+    o_self = torch.empty(B, Hq, d, dtype=torch.bfloat16, device=DEV)
+    o_cross = torch.empty_like(o_self)
+    ws_s = torch.empty(yk.yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d), dtype=torch.uint8, device=DEV)
+    ws_c = torch.empty(yk.yoco_cross_attn_decode_workspace_bytes(B, Hq, Hkv, ctx, d), dtype=torch.uint8, device=DEV)
+
+    def step():
+        yk.yoco_swa_decode(qs, kr, vr, pos, k_new=kn, v_new=vn, o=o_self, workspace=ws_s)
+        yk.yoco_global_kv_proj(hid, wk, wv, kc, vc, pos0=pos)
+        yk.yoco_cross_attn_decode(qc, kc, vc, ctx, o=o_cross, workspace=ws_c)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (o_self.clone(), o_cross.clone(), kr.clone(), kc[:, :, pos].clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        o_self.fill_(0)
+        o_cross.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (o_self, o_cross, kr, kc[:, :, pos])
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
