@@ -138,3 +138,44 @@ def test_gret_prefill_full_size_sampled_heads():
                                               to64(z[:, h:h + 1]), 16.0, 256)
         rel_check(to64(o[:, h:h + 1]), ref_o, f"full-size head {h}")
         rel_check(to64(st[:, h:h + 1]), ref_st, f"full-size state head {h}")
+
+
+def test_gret_graph_replays_match_eager():
+    """Gated-retention prefill (three kernels, workspace) and decode (state
+    updated in place) captured as one HIP graph: every replay, with eager work
+    between the replays, reproduces the eager calls bitwise."""
+    B, H, N, d = 1, 4, 700, 128
+    s = d ** -0.25
+    q = randn((B, H, N, d), 990, std=s, device=DEV)
+    k = randn((B, H, N, d), 991, std=s, device=DEV)
+    v = randn((B, H, N, d), 992, device=DEV)
+    z = randn((B, H, N), 993, dtype="f32", device=DEV) + 3.0
+    o = torch.empty_like(q)
+    st = torch.empty(B, H, d, d, dtype=torch.float32, device=DEV)
+    ws = torch.empty(yk.yoco_gret_prefill_workspace_bytes(B, H, N, d, 256), dtype=torch.uint8, device=DEV)
+    qd, kd, vd = (randn((B, H, d), 994 + i, std=s, device=DEV) for i in range(3))
+    zd = randn((B, H), 997, dtype="f32", device=DEV) + 3.0
+    od = torch.empty(B, H, d, dtype=torch.bfloat16, device=DEV)
+    st_dec = torch.empty_like(st)
+
+    def calls():
+        yk.yoco_gret_prefill(q, k, v, z, 16.0, o=o, state_out=st, workspace=ws)
+        st_dec.copy_(st)
+        yk.yoco_gret_decode(qd, kd, vd, zd, 16.0, st_dec, o=od)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = (o.clone(), st.clone(), od.clone(), st_dec.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(4):
+        for t in (o, st, od, st_dec):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((o, st, od, st_dec), ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager calls"
+        calls()
+        torch.cuda.synchronize()
