@@ -349,8 +349,10 @@ struct TileStager {
   }
   __device__ __forceinline__ void load(int t, char* kdst_tile, char* vdst_tile) const {
     const size_t tb = (size_t)t * C::BK * ROWB;   // uniform tile base
-    // bytes of rows < n_kv (uniform; read back as a scalar so the resource stays in SGPRs)
-    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(C::TILE_BYTES, (n_kv - t * C::BK) * ROWB)));
+    // bytes of rows < n_kv (uniform; read back as a scalar so the resource
+    // stays in SGPRs).  The row count is clamped to one tile before it is
+    // scaled to bytes, so the product stays small for any cache length.
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(C::BK, n_kv - t * C::BK)) * ROWB);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tb), (short)0, valid, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tb), (short)0, valid, kBufferFlags);
 #pragma unroll

@@ -142,3 +142,27 @@ def test_planted_key_dominates_across_tiles():
     torch.cuda.synchronize()
     ro, _ = oracle.cross_prefill_attention(to64(q), to64(k), to64(v), rows=list(range(300, 512)))
     check(to64(o)[:, :, 300:], ro[:, :, 300:], "bf16", "planted", rel_axes=(2, 3))
+
+
+def test_cache_past_2_pow_31_bytes_reads_its_first_keys():
+    """A cache of 2^24 rows of bf16 d = 128 (4 GiB per tensor): the first key
+    tile's byte count is past 2^31.  One query at the last position, key 0
+    planted to dominate every other (all zero) key: the output must be v[0]
+    -- a tile that loaded as zeros would give the mean of V instead."""
+    n, d = 1 << 24, 128
+    print(f"prefill over {n} cache rows", flush=True)
+    q = randn((1, 1, 1, d), 810, device=DEV)
+    k = torch.zeros(1, 1, n, d, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros(1, 1, n, d, dtype=torch.bfloat16, device=DEV)
+    k[0, 0, 0] = (q[0, 0, 0].float() * 5).to(torch.bfloat16)    # score ~ 5 |q|^2 / sqrt(d) ~ 56 >> ln(2^24)
+    v[0, 0, 0] = randn((d,), 811, device=DEV)
+    v[0, 0, 1:4096] = randn((4095, d), 812, device=DEV)
+    o = yk.yoco_cross_attn_prefill(q, k, v, q_offset=n - 1)
+    torch.cuda.synchronize()
+    ro, _ = oracle.decode_attention(to64(q)[:, :, 0], to64(k[:, :, :4096]), to64(v[:, :, :4096]), [4096])
+    # the other 2^24 - 4096 keys have score 0 and value 0: they only add to the
+    # denominator, which the planted key's weight e^56 makes negligible
+    check(to64(o)[:, :, 0], ro, "bf16", "2^24-row cache", rel_axes=(2,))
+    assert (o[0, 0, 0].float() - v[0, 0, 0].float()).abs().max().item() <= 2e-2
+    del k, v
+    torch.cuda.empty_cache()
