@@ -32,7 +32,9 @@
  *               stream).  Every call is stream-ordered and asynchronous:
  *               it enqueues kernels and returns; it never synchronises,
  *               never allocates and keeps no mutable global state, so calls
- *               on different streams may run concurrently.
+ *               on different streams may run concurrently (the one
+ *               exception, yoco_cross_attn_decode_noalloc, uses a fixed
+ *               device array of the library and says so below).
  *   Errors      argument errors are detected before any HIP call and leave
  *               every output untouched; YOCO_ERR_HIP reports a failed launch
  *               (hipGetLastError).  Faults inside a kernel surface
@@ -190,6 +192,38 @@ yoco_status yoco_cross_attn_decode(const void* q, const void* k_cache,
 
 /* Workspace of yoco_cross_attn_decode for these sizes (0 on invalid sizes). */
 size_t yoco_cross_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int ctx, int d);
+
+/*
+ * yoco_cross_attn_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP stream capture, tight serving
+ * loops, harnesses that forbid allocation.  The split partials live in a
+ * fixed device array of the library (one copy per GPU, held until the process
+ * ends); the call allocates nothing and runs the same kernels, so its output
+ * equals yoco_cross_attn_decode's bit for bit.
+ *   Arguments, layouts and checks as yoco_cross_attn_decode.
+ *   Limit: the workspace yoco_cross_attn_decode_workspace_bytes would return
+ *   for these sizes must not exceed yoco_cross_attn_decode_noalloc_max_bytes()
+ *   (16 MiB: 32768 partial rows of d = 128 floats, which covers every call
+ *   with up to 512 sequences of 32 query heads at d = 128, whatever the
+ *   context length); larger sizes return YOCO_ERR_WORKSPACE before any
+ *   launch.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (different streams, or different host threads) race and must
+ *   be serialised by the caller.  Nothing in the array needs clearing between
+ *   calls.  The first call on each device looks up that device's copy (one
+ *   hipGetSymbolAddress, no allocation); a failure there is YOCO_ERR_HIP.
+ */
+yoco_status yoco_cross_attn_decode_noalloc(const void* q, const void* k_cache,
+                                           const void* v_cache, const float* k_scale,
+                                           const float* v_scale, const int32_t* ctx_lens,
+                                           int ctx, void* o, float* lse,
+                                           int B, int Hq, int Hkv, int n_cap, int d,
+                                           float softmax_scale, yoco_dtype q_dtype,
+                                           yoco_dtype kv_dtype, void* stream);
+
+/* Bytes of the fixed device array behind yoco_cross_attn_decode_noalloc. */
+size_t yoco_cross_attn_decode_noalloc_max_bytes(void);
+
 
 /*
  * Self-decoder sliding-window attention for one new token per sequence (a

@@ -30,6 +30,8 @@ __all__ = [
     "yoco_cross_attn_prefill",
     "yoco_cross_attn_decode",
     "yoco_cross_attn_decode_workspace_bytes",
+    "yoco_cross_attn_decode_noalloc",
+    "yoco_cross_attn_decode_noalloc_max_bytes",
     "yoco_swa_decode",
     "yoco_swa_decode_workspace_bytes",
     "yoco_gret_prefill",
@@ -64,6 +66,9 @@ _SIGS = {
     "yoco_cross_attn_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i,
                                     _vp, _sz, _vp]),
     "yoco_cross_attn_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "yoco_cross_attn_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                            _i, _vp]),
+    "yoco_cross_attn_decode_noalloc_max_bytes": (_sz, []),
     "yoco_swa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]),
     "yoco_swa_decode_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "yoco_gret_prefill": (_i, [_vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
@@ -307,6 +312,24 @@ def yoco_cross_attn_decode(q, k_cache, v_cache, ctx, ctx_lens=None, k_scale=None
         _ptr(lse), B, Hq, Hkv, n_cap, d, float(softmax_scale), _dtype_code(q), _dtype_code(k_cache),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "yoco_cross_attn_decode")
+    return o
+
+
+def yoco_cross_attn_decode_noalloc_max_bytes():
+    return lib().yoco_cross_attn_decode_noalloc_max_bytes()
+
+
+def yoco_cross_attn_decode_noalloc(q, k_cache, v_cache, ctx, o, ctx_lens=None, k_scale=None, v_scale=None, lse=None,
+                                   softmax_scale=0.0, stream=None):
+    """yoco_cross_attn_decode with the library's fixed device array as its workspace (nothing is allocated;
+    the caller passes the output o).  Calls that overlap on one GPU race."""
+    B, Hq, d = q.shape
+    Hkv, n_cap = k_cache.shape[1], k_cache.shape[2]
+    st = lib().yoco_cross_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(ctx_lens), int(ctx), _ptr(o),
+        _ptr(lse), B, Hq, Hkv, n_cap, d, float(softmax_scale), _dtype_code(q), _dtype_code(k_cache),
+        _stream(stream))
+    _check(st, "yoco_cross_attn_decode_noalloc")
     return o
 
 
