@@ -23,8 +23,10 @@
  *                          denominator, scale included
  *   Heads       query head h reads KV head h / (Hq / Hkv) (contiguous groups)
  *   dtypes      YOCO_F32 and YOCO_BF16 for activations, caches and outputs;
- *               YOCO_FP8_E4M3 (OCP e4m3fn codes, uint8) only for a decode
- *               cache.  All arithmetic accumulates in float32.
+ *               YOCO_FP8_E4M3 (OCP e4m3fn codes, uint8) only for the global
+ *               cache (written by yoco_global_kv_proj or
+ *               yoco_kv_quantize_fp8, read by yoco_cross_attn_decode).  All
+ *               arithmetic accumulates in float32.
  *   head_dim    d must be 64 or 128.
  *   Pointers    device pointers (HIP), 16-byte aligned, owned by the caller.
  *               Outputs must not overlap inputs.
@@ -72,27 +74,53 @@ typedef enum { YOCO_F32 = 0, YOCO_BF16 = 1, YOCO_FP8_E4M3 = 2 } yoco_dtype;
  * cross-decoder layer).  Normalisation read as RMSNorm:
  *   n_t = x_t / sqrt(mean_j x_tj^2 + eps) * gamma,
  *   K[b,h,pos0+t,c] = sum_j n_bt,j W_K[h*d+c, j]   (V likewise with W_V).
- *   x       [B, N, D] act dtype
- *   norm_w  [D] act dtype (gamma), or NULL for gamma = 1
- *   w_k,w_v [Hkv*d, D] act dtype
- *   k_out,v_out [B, Hkv, n_cap, d] act dtype; rows [pos0, pos0+N) written,
+ *   x       [B, N, D] act_dtype (F32 or BF16)
+ *   norm_w  [D] act_dtype (gamma), or NULL for gamma = 1
+ *   w_k,w_v [Hkv*d, D] act_dtype
+ *   k_out,v_out [B, Hkv, n_cap, d] kv_dtype; rows [pos0, pos0+N) written,
  *           other rows untouched (so prompt chunks can be appended)
  * Requires 1 <= N, 0 <= pos0, pos0 + N <= n_cap, D % 64 == 0, D <= 65536.
- * Numerics: float32 accumulation; with gamma given and dtype bf16, x*gamma is
- * rounded to bf16 before the product (the row scale is applied in float32).
+ * Numerics: float32 accumulation; with gamma given and act_dtype bf16, x*gamma
+ * is rounded to bf16 before the product (the row scale is applied in float32).
  * rope_theta > 0 rotates every key (not the values) at its cache position
  * pos0 + t by the rotary embedding of base rope_theta (paperlayer.ai summary
  * appendix E and podcast segment 20: RoPE with a per-stage base, 640K, 5M,
  * 80M): channel pair (2i, 2i+1) turns by (pos0 + t) * rope_theta^(-2i/d), the
  * angle reduced in double precision.  0 = no rotation; NaN, inf or < 0 is
  * YOCO_ERR_SHAPE.
+ *
+ * kv_dtype is act_dtype (k_scale, v_scale and the workspace are then unused
+ * and may be NULL), or YOCO_FP8_E4M3: the cache is written as 8-bit codes
+ * (podcast segments 1 and 24: an 8-bit KV cache is the deployed form; the
+ * shared cache is written once, segment 12), in the format of
+ * yoco_kv_quantize_fp8.  Each value is first rounded to act_dtype, exactly as
+ * the act_dtype cache would hold it, and then encoded:
+ *   pos0 == 0  the call sets the scales from its own rows: k_scale[h] =
+ *              max |K[:, h, 0:N, :]| / 448 (1 if that is 0), v_scale likewise,
+ *              both written ([Hkv] float32 each).  The codes equal
+ *              yoco_kv_quantize_fp8 applied to the act_dtype projection of the
+ *              same rows, bit for bit.
+ *   pos0 > 0   rows appended to a cache whose scales are set: k_scale and
+ *              v_scale are read, not written, and each value is encoded with
+ *              them as yoco_kv_quantize_fp8 encodes (saturating at +-448).
+ *   The rows are staged in act_dtype in the workspace: >=
+ *   yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, act_dtype, kv_dtype)
+ *   bytes, 16-byte aligned, not shared by concurrent calls.
  */
 yoco_status yoco_global_kv_proj(const void* x, const void* norm_w,
                                 const void* w_k, const void* w_v,
                                 void* k_out, void* v_out,
+                                float* k_scale, float* v_scale,
                                 int B, int N, int D, int Hkv, int d,
                                 int n_cap, int pos0, float eps, float rope_theta,
-                                yoco_dtype dtype, void* stream);
+                                yoco_dtype act_dtype, yoco_dtype kv_dtype,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Workspace of yoco_global_kv_proj for these sizes: 0 unless kv_dtype is
+ * YOCO_FP8_E4M3 (and 0 on invalid sizes). */
+size_t yoco_global_kv_proj_workspace_bytes(int B, int N, int Hkv, int d,
+                                           yoco_dtype act_dtype, yoco_dtype kv_dtype);
 
 /*
  * Self-decoder sliding-window attention.
@@ -223,7 +251,6 @@ yoco_status yoco_cross_attn_decode_noalloc(const void* q, const void* k_cache,
 
 /* Bytes of the fixed device array behind yoco_cross_attn_decode_noalloc. */
 size_t yoco_cross_attn_decode_noalloc_max_bytes(void);
-
 
 /*
  * Self-decoder sliding-window attention for one new token per sequence (a

@@ -49,7 +49,9 @@ from .fp8 import (  # noqa: F401
     E4M3_MAX,
     e4m3_decode,
     e4m3_encode,
+    kv_fp8_scales,
     quantize_kv_fp8,
+    encode_kv_fp8,
     dequantize_kv_fp8,
 )
 from .block import BlockParams, linear_rows, silu, swiglu_hidden_row, swiglu_ffn_row, yoco_block, yoco_block_early_exit, yoco_block_generate  # noqa: F401

@@ -29,7 +29,9 @@ __all__ = [
     "E4M3_MAX",
     "e4m3_decode",
     "e4m3_encode",
+    "kv_fp8_scales",
     "quantize_kv_fp8",
+    "encode_kv_fp8",
     "dequantize_kv_fp8",
 ]
 
@@ -86,24 +88,43 @@ def e4m3_encode(x):
     return out.reshape(arr.shape)
 
 
+def kv_fp8_scales(kv):
+    """Per-KV-head scales of a KV tensor [B, Hkv, n, d]: s_h = amax_h / 448
+    over all (b, n, d) of head h, one float32 division (1 for an all-zero
+    head).  kv holds the exact float32 or bfloat16 values."""
+    x32 = np.asarray(kv, dtype=np.float32)
+    hkv = x32.shape[1]
+    scales = np.empty(hkv, dtype=np.float32)
+    for h in range(hkv):
+        amax = np.float32(np.max(np.abs(x32[:, h]))) if x32[:, h].size else np.float32(0)
+        scales[h] = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(E4M3_MAX))
+    return scales
+
+
 def quantize_kv_fp8(kv):
     """Quantise a KV tensor [B, Hkv, n, d] to e4m3fn codes with per-head scales.
 
     kv holds the exact values the quantiser receives (float32 or bfloat16
     values, here as any float array).  Returns (codes uint8 [B, Hkv, n, d],
-    scales float32 [Hkv]).
+    scales float32 [Hkv]): the scales of kv_fp8_scales, and each value x of
+    head h encoded as e4m3fn(x / s_h), the division in float32 (IEEE,
+    correctly rounded).
     """
+    scales = kv_fp8_scales(kv)
+    return encode_kv_fp8(kv, scales), scales
+
+
+def encode_kv_fp8(kv, scales):
+    """Codes of a KV tensor [B, Hkv, n, d] under per-head scales that are
+    already set (rows appended to an 8-bit cache after its scales were fixed):
+    code = e4m3fn(x / s_h), the division in float32, saturating like
+    e4m3_encode.  kv holds the exact float32 or bfloat16 values."""
     x32 = np.asarray(kv, dtype=np.float32)
-    hkv = x32.shape[1]
+    s32 = np.asarray(scales, dtype=np.float32)
     codes = np.empty(x32.shape, dtype=np.uint8)
-    scales = np.empty(hkv, dtype=np.float32)
-    for h in range(hkv):
-        amax = np.float32(np.max(np.abs(x32[:, h]))) if x32[:, h].size else np.float32(0)
-        s = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(E4M3_MAX))
-        scales[h] = s
-        y = x32[:, h] / s           # float32 / float32: IEEE, correctly rounded
-        codes[:, h] = e4m3_encode(y)
-    return codes, scales
+    for h in range(x32.shape[1]):
+        codes[:, h] = e4m3_encode(x32[:, h] / s32[h])
+    return codes
 
 
 def dequantize_kv_fp8(codes, scales):

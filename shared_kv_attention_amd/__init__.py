@@ -22,6 +22,7 @@ __all__ = [
     "lib",
     "library_path",
     "yoco_global_kv_proj",
+    "yoco_global_kv_proj_workspace_bytes",
     "yoco_swa_attn",
     "yoco_swa_attn_halo",
     "yoco_peak_hbm_read",
@@ -58,7 +59,9 @@ _lib = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
-    "yoco_global_kv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _i, _vp]),
+    "yoco_global_kv_proj": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _i, _i,
+                                 _vp, _sz, _vp]),
+    "yoco_global_kv_proj_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "yoco_swa_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "yoco_swa_attn_halo": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]),
     "yoco_attn_merge": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
@@ -153,18 +156,39 @@ def _check(status, fn):
         raise YocoError(status, fn)
 
 
-def yoco_global_kv_proj(x, w_k, w_v, k_out, v_out, pos0=0, norm_w=None, eps=1e-6, rope_theta=0.0, stream=None):
+def yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, act_dtype, kv_dtype):
+    return lib().yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, act_dtype, kv_dtype)
+
+
+def yoco_global_kv_proj(x, w_k, w_v, k_out, v_out, pos0=0, norm_w=None, eps=1e-6, rope_theta=0.0, k_scale=None,
+                        v_scale=None, workspace=None, stream=None):
     """K/V cache rows [pos0, pos0+N) = RMSNorm(x) @ W^T, split into KV heads.
 
-    x [B, N, D]; w_k, w_v [Hkv*d, D]; k_out, v_out [B, Hkv, n_cap, d]; same dtype.
-    rope_theta > 0 rotates the keys at their cache positions.
+    x [B, N, D]; w_k, w_v [Hkv*d, D]; k_out, v_out [B, Hkv, n_cap, d] in x's dtype, or uint8 for an 8-bit
+    (e4m3fn) cache: then k_scale, v_scale [Hkv] float32 are written (pos0 == 0; allocated if not given) or read
+    (pos0 > 0).  rope_theta > 0 rotates the keys at their cache positions.
+    Returns (k_out, v_out), or (k_out, v_out, k_scale, v_scale) for an 8-bit cache.
     """
+    torch = _torch()
     B, N, D = x.shape
     _, Hkv, n_cap, d = k_out.shape
+    act, kvd = _dtype_code(x), _dtype_code(k_out)
+    fp8 = kvd == FP8_E4M3
+    if fp8 and k_scale is None:
+        k_scale = torch.empty(Hkv, dtype=torch.float32, device=x.device)
+    if fp8 and v_scale is None:
+        v_scale = torch.empty(Hkv, dtype=torch.float32, device=x.device)
+    if fp8 and workspace is None:
+        need = yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, act, kvd)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().yoco_global_kv_proj(_ptr(x), _ptr(norm_w), _ptr(w_k), _ptr(w_v), _ptr(k_out), _ptr(v_out),
-                                   B, N, D, Hkv, d, n_cap, pos0, eps, float(rope_theta), _dtype_code(x),
-                                   _stream(stream))
+                                   _ptr(k_scale if fp8 else None), _ptr(v_scale if fp8 else None),
+                                   B, N, D, Hkv, d, n_cap, pos0, eps, float(rope_theta), act, kvd,
+                                   _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "yoco_global_kv_proj")
+    if fp8:
+        return k_out, v_out, k_scale, v_scale
     return k_out, v_out
 
 

@@ -55,6 +55,60 @@ DecodeLayout decode_layout(int B, int Hq, int Hkv, int ctx, int d, int kv_kind =
   return L;
 }
 
+// Workspace of an 8-bit global projection that sets the scales: the
+// per-head maxima of K and V (2 Hkv words), then K and V staged in the
+// activation dtype as [B, Hkv, N, d].
+struct ProjFp8Layout {
+  size_t amax, k_stage, v_stage, total;
+};
+ProjFp8Layout proj_fp8_layout(int B, int N, int Hkv, int d, yoco_dtype act) {
+  ProjFp8Layout L{};
+  const size_t stage = align16((size_t)B * Hkv * N * d * (act == YOCO_F32 ? 4 : 2));
+  L.amax = 0;
+  L.k_stage = align16((size_t)2 * Hkv * sizeof(uint32_t));
+  L.v_stage = L.k_stage + stage;
+  L.total = L.v_stage + stage;
+  return L;
+}
+
+// The projection GEMM into a [B, Hkv, n_cap, d] activation-dtype cache,
+// token t at position pos0 + t written to row row0 + t.  amax (non-null) asks
+// for the per-head maxima of the written values; *fused_amax tells whether
+// the chosen kernel form collected them.
+hipError_t proj_gemm(const void* x, const void* norm_w, const void* w_k, const void* w_v, void* k_out, void* v_out,
+                     int B, int N, int D, int Hkv, int d, int n_cap, int pos0, int row0, float eps,
+                     float rope_theta, bool is_bf16, uint32_t* amax, hipStream_t st, bool* fused_amax = nullptr) {
+  if (fused_amax) *fused_amax = false;
+  if (is_bf16 && ((long long)B * N >= 16384 || (long long)B * N <= 64)) {
+    // the block-layer GEMM in its Q/K/V form with no query heads: for long
+    // prompts its wide bf16 tiles (measured 18.7 vs 22.9 ms at 2^20 tokens),
+    // for a few tokens (the one-token append of generation) its form that
+    // spreads K over many waves.  In between, the 128 x 128 kernel below, two
+    // workgroups per CU, hides latency better (72 vs 80 us at 4096 tokens); it
+    // also serves float32.
+    yoco::LinArgs la{};
+    la.x = x;
+    la.norm_w = norm_w;
+    la.w1 = w_k;
+    la.w2 = w_v;
+    la.y1 = k_out;
+    la.y2 = v_out;
+    la.B = B; la.N = N; la.K = D; la.F = 2 * Hkv * d;
+    la.f1 = 0; la.f2 = Hkv * d;
+    la.h0 = 0; la.h1 = Hkv; la.d = d;
+    la.kv_rows = n_cap; la.kv_pos0 = row0;
+    la.norm = 1;
+    la.eps = eps;
+    la.rope_log2_theta = rope_log2(rope_theta);
+    la.rope_pos0 = pos0;
+    return yoco::launch_linear(la, yoco::kLinQKV, true, st);
+  }
+  yoco::ProjArgs a{x, norm_w, w_k, w_v, k_out, v_out, B, N, D, Hkv, d, n_cap, pos0, row0, eps, rope_log2(rope_theta),
+                   amax};
+  if (fused_amax) *fused_amax = amax != nullptr;
+  return yoco::launch_kv_proj(a, is_bf16, st);
+}
+
 bool decode_sizes_ok(int B, int Hq, int Hkv, int ctx, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || ctx < 1 || Hq % Hkv != 0) return false;
   if (!head_dim_ok(d)) return false;
@@ -82,12 +136,22 @@ const char* yoco_status_string(yoco_status s) {
 
 int yoco_version(void) { return kVersion; }
 
+size_t yoco_global_kv_proj_workspace_bytes(int B, int N, int Hkv, int d, yoco_dtype act_dtype, yoco_dtype kv_dtype) {
+  if (B < 1 || N < 1 || Hkv < 1 || !head_dim_ok(d) || !is_act(act_dtype)) return 0;
+  if (kv_dtype != YOCO_FP8_E4M3) return 0;   // no workspace (or an invalid dtype)
+  if ((long long)B * N > kIntMax || (long long)B * Hkv * N > kIntMax) return 0;
+  return proj_fp8_layout(B, N, Hkv, d, act_dtype).total;
+}
+
 yoco_status yoco_global_kv_proj(const void* x, const void* norm_w, const void* w_k, const void* w_v,
-                                void* k_out, void* v_out, int B, int N, int D, int Hkv, int d,
-                                int n_cap, int pos0, float eps, float rope_theta, yoco_dtype dtype,
+                                void* k_out, void* v_out, float* k_scale, float* v_scale, int B, int N, int D,
+                                int Hkv, int d, int n_cap, int pos0, float eps, float rope_theta,
+                                yoco_dtype act_dtype, yoco_dtype kv_dtype, void* workspace, size_t workspace_bytes,
                                 void* stream) {
+  const bool fp8 = kv_dtype == YOCO_FP8_E4M3;
   if (!x || !w_k || !w_v || !k_out || !v_out) return YOCO_ERR_NULL;
-  if (!is_act(dtype)) return YOCO_ERR_DTYPE;
+  if (fp8 && (!k_scale || !v_scale)) return YOCO_ERR_NULL;
+  if (!is_act(act_dtype) || (kv_dtype != act_dtype && !fp8)) return YOCO_ERR_DTYPE;
   if (B < 1 || N < 1 || D < 1 || Hkv < 1 || n_cap < 1 || pos0 < 0 || (long long)pos0 + N > n_cap)
     return YOCO_ERR_SHAPE;
   if (!(eps >= 0.f) || isinf(eps) || !(rope_theta >= 0.f) || isinf(rope_theta)) return YOCO_ERR_SHAPE;
@@ -95,34 +159,43 @@ yoco_status yoco_global_kv_proj(const void* x, const void* norm_w, const void* w
     return YOCO_ERR_SHAPE;
   if (!head_dim_ok(d) || D % 64 != 0 || D > 65536) return YOCO_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 16) || !aligned(v_out, 16) ||
-      (norm_w && !aligned(norm_w, 16)))
+      (norm_w && !aligned(norm_w, 16)) || (k_scale && fp8 && !aligned(k_scale, 4)) ||
+      (v_scale && fp8 && !aligned(v_scale, 4)))
     return YOCO_ERR_ALIGN;
-  if (dtype == YOCO_BF16 && ((long long)B * N >= 16384 || (long long)B * N <= 64)) {
-    // the block-layer GEMM in its Q/K/V form with no query heads: for long
-    // prompts its wide bf16 tiles (measured 18.7 vs 22.9 ms at 2^20 tokens),
-    // for a few tokens (the one-token append of generation) its form that
-    // spreads K over many waves.  In between, the 128 x 128 kernel below, two
-    // workgroups per CU, hides latency better (72 vs 80 us at 4096 tokens); it
-    // also serves float32.
-    yoco::LinArgs a{};
-    a.x = x;
-    a.norm_w = norm_w;
-    a.w1 = w_k;
-    a.w2 = w_v;
-    a.y1 = k_out;
-    a.y2 = v_out;
-    a.B = B; a.N = N; a.K = D; a.F = 2 * Hkv * d;
-    a.f1 = 0; a.f2 = Hkv * d;
-    a.h0 = 0; a.h1 = Hkv; a.d = d;
-    a.kv_rows = n_cap; a.kv_pos0 = pos0;
-    a.norm = 1;
-    a.eps = eps;
-    a.rope_log2_theta = rope_log2(rope_theta);
-    a.rope_pos0 = pos0;
-    return launched(yoco::launch_linear(a, yoco::kLinQKV, true, as_stream(stream)));
+  const bool is_bf16 = act_dtype == YOCO_BF16;
+  hipStream_t st = as_stream(stream);
+  if (!fp8) return launched(proj_gemm(x, norm_w, w_k, w_v, k_out, v_out, B, N, D, Hkv, d, n_cap, pos0, pos0, eps,
+                                      rope_theta, is_bf16, nullptr, st));
+  // 8-bit cache: the rows are projected exactly as into an act_dtype cache, but
+  // into a staging buffer in the workspace; then each tensor is encoded into
+  // the cache rows [pos0, pos0 + N) -- with scales set from the staged rows'
+  // per-head maxima (pos0 == 0), or with the given scales (pos0 > 0).
+  const ProjFp8Layout L = proj_fp8_layout(B, N, Hkv, d, act_dtype);
+  if (!workspace || workspace_bytes < L.total) return YOCO_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(ws + L.amax);
+  const bool set_scales = pos0 == 0;
+  yoco_status s = YOCO_OK;
+  if (set_scales && (s = launched(yoco::launch_quant_clear(amax, 2 * Hkv, st))) != YOCO_OK) return s;
+  // the 128 x 128 projection kernel collects the maxima in its epilogue; the
+  // block-layer GEMM forms (long prompts, a few tokens) are followed by a pass
+  // over the staged rows
+  bool fused_amax = false;
+  s = launched(proj_gemm(x, norm_w, w_k, w_v, ws + L.k_stage, ws + L.v_stage, B, N, D, Hkv, d, N, pos0, 0, eps,
+                         rope_theta, is_bf16, set_scales ? amax : nullptr, st, &fused_amax));
+  if (s != YOCO_OK) return s;
+  const long long slab = (long long)N * d;
+  yoco::QuantArgs qk{ws + L.k_stage, static_cast<uint8_t*>(k_out), k_scale, amax, B, Hkv, slab,
+                     (long long)n_cap * d, (long long)pos0 * d, set_scales ? 0 : 1};
+  yoco::QuantArgs qv{ws + L.v_stage, static_cast<uint8_t*>(v_out), v_scale, amax + Hkv, B, Hkv, slab,
+                     (long long)n_cap * d, (long long)pos0 * d, set_scales ? 0 : 1};
+  if (set_scales && !fused_amax) {
+    if ((s = launched(yoco::launch_quant_amax(qk, is_bf16, st))) != YOCO_OK) return s;
+    if ((s = launched(yoco::launch_quant_amax(qv, is_bf16, st))) != YOCO_OK) return s;
   }
-  yoco::ProjArgs a{x, norm_w, w_k, w_v, k_out, v_out, B, N, D, Hkv, d, n_cap, pos0, eps, rope_log2(rope_theta)};
-  return launched(yoco::launch_kv_proj(a, dtype == YOCO_BF16, as_stream(stream)));
+  if ((s = launched(yoco::launch_quant_encode(qk, is_bf16, st))) != YOCO_OK) return s;
+  return launched(yoco::launch_quant_encode(qv, is_bf16, st));
 }
 
 static bool lin_sizes_ok(int B, int N, int K, int F, int fpt) {
@@ -503,7 +576,7 @@ yoco_status yoco_kv_quantize_fp8(const void* kv, yoco_dtype in_dtype, void* code
   if (!workspace || workspace_bytes < yoco_kv_quantize_fp8_workspace_bytes(Hkv)) return YOCO_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
   yoco::QuantArgs a{kv, static_cast<uint8_t*>(codes), scale, static_cast<uint32_t*>(workspace), B, Hkv,
-                    (long long)n * d};
+                    (long long)n * d, (long long)n * d, 0};
   return launched(yoco::launch_quant_fp8(a, in_dtype == YOCO_BF16, as_stream(stream)));
 }
 

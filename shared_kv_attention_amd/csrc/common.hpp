@@ -83,6 +83,19 @@ __device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w, bool hi) {
             : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
 }
 
+// Four values -> four OCP e4m3fn codes (byte i = code of x[i]) with the
+// per-head scale s: x / s as one correctly rounded float32 division, clamped
+// to +-448 (saturation), then the hardware's round-to-nearest-even conversion.
+__device__ __forceinline__ uint32_t encode_e4m3_x4(float x0, float x1, float x2, float x3, float s) {
+  const float y0 = fminf(fmaxf(__fdiv_rn(x0, s), -448.f), 448.f);
+  const float y1 = fminf(fmaxf(__fdiv_rn(x1, s), -448.f), 448.f);
+  const float y2 = fminf(fmaxf(__fdiv_rn(x2, s), -448.f), 448.f);
+  const float y3 = fminf(fmaxf(__fdiv_rn(x3, s), -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+  return (uint32_t)w;
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane helpers
 // ---------------------------------------------------------------------------

@@ -65,53 +65,69 @@ __global__ __launch_bounds__(256) void quant_amax_kernel(QuantArgs a) {
   }
 }
 
+// Codes of slab (b, h) go to codes + (b * Hkv + h) * dst_slab + dst_off: a
+// tensor quantised whole (dst_slab = slab, dst_off = 0), or rows written into
+// a larger cache at an offset.  The scale is set from the maxima (and
+// written), or given (rows appended to a cache whose scales are set).
 template <typename T>
 __global__ __launch_bounds__(256) void quant_encode_kernel(QuantArgs a) {
   const int h = blockIdx.y, b = blockIdx.z;
-  const float amax = __uint_as_float(a.amax_bits[h]);
-  const float s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
-  if (blockIdx.x == 0 && b == 0 && threadIdx.x == 0) a.scale[h] = s;
-  const size_t off = (size_t)(b * a.Hkv + h) * a.slab;
-  const T* base = static_cast<const T*>(a.kv) + off;
-  uint8_t* out = a.codes + off;
+  float s;
+  if (a.scale_given) {
+    s = a.scale[h];
+  } else {
+    const float amax = __uint_as_float(a.amax_bits[h]);
+    s = amax == 0.f ? 1.f : __fdiv_rn(amax, 448.f);
+    if (blockIdx.x == 0 && b == 0 && threadIdx.x == 0) a.scale[h] = s;
+  }
+  const T* base = static_cast<const T*>(a.kv) + (size_t)(b * a.Hkv + h) * a.slab;
+  uint8_t* out = a.codes + (size_t)(b * a.Hkv + h) * a.dst_slab + a.dst_off;
   const long long n8 = a.slab / 8;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
     float x[8];
     load8<T>(base + i * 8, x);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(__fdiv_rn(x[e], s), -448.f), 448.f);
     u32x2 w;
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
-    w[0] = (uint32_t)lo;
-    w[1] = (uint32_t)hi;
+    w[0] = encode_e4m3_x4(x[0], x[1], x[2], x[3], s);
+    w[1] = encode_e4m3_x4(x[4], x[5], x[6], x[7], s);
     *reinterpret_cast<u32x2*>(out + i * 8) = w;
   }
 }
 
-hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_clear_kernel, dim3((a.Hkv + 255) / 256), dim3(256), 0, stream, a.amax_bits, a.Hkv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+static dim3 quant_grid(const QuantArgs& a) {
   const long long n8 = a.slab / 8;
   long long per_slab = (n8 + 256 * 4 - 1) / (256 * 4);   // ~4 steps per thread
   if (per_slab > 1024) per_slab = 1024;
   if (per_slab < 1) per_slab = 1;
-  dim3 grid((unsigned)per_slab, a.Hkv, a.B);
-  if (is_bf16)
-    hipLaunchKernelGGL((quant_amax_kernel<bf16>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((quant_amax_kernel<float>), grid, dim3(256), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (is_bf16)
-    hipLaunchKernelGGL((quant_encode_kernel<bf16>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((quant_encode_kernel<float>), grid, dim3(256), 0, stream, a);
+  return dim3((unsigned)per_slab, a.Hkv, a.B);
+}
+
+hipError_t launch_quant_clear(uint32_t* amax_bits, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(quant_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, amax_bits, n);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_amax(const QuantArgs& a, bool is_bf16, hipStream_t stream) {
+  if (is_bf16)
+    hipLaunchKernelGGL((quant_amax_kernel<bf16>), quant_grid(a), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((quant_amax_kernel<float>), quant_grid(a), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_encode(const QuantArgs& a, bool is_bf16, hipStream_t stream) {
+  if (is_bf16)
+    hipLaunchKernelGGL((quant_encode_kernel<bf16>), quant_grid(a), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((quant_encode_kernel<float>), quant_grid(a), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream) {
+  hipError_t e = launch_quant_clear(a.amax_bits, a.Hkv, stream);
+  if (e != hipSuccess) return e;
+  e = launch_quant_amax(a, is_bf16, stream);
+  if (e != hipSuccess) return e;
+  return launch_quant_encode(a, is_bf16, stream);
 }
 
 }  // namespace yoco

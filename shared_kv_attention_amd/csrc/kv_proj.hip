@@ -239,6 +239,9 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
   __syncthreads();
 
   // Epilogue: acc[i][jj][e] = C^T[feature f0 + wf*64 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*64 + jj*32 + r32]
+  // A wave's 64 features lie in one head of one of K and V (f0 is a multiple
+  // of 128 and Hkv*d, d of 64).
+  float amax = 0.f;   // largest |value| this lane stores (amax_bits mode)
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     const int tl = wt * 64 + jj * 32 + r32;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
         const int fr = which ? f - HD : f;
         const int hh = fr / a.d, c = fr % a.d;
         T* dst = static_cast<T*>(which ? a.v_out : a.k_out) +
-                 ((size_t)(bb * a.Hkv + hh) * a.n_cap + a.pos0 + n) * a.d + c;
+                 ((size_t)(bb * a.Hkv + hh) * a.n_cap + a.row0 + n) * a.d + c;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][jj][4 * qd + e] * rs;
@@ -265,16 +268,35 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
           rope_pair(v[0], v[1], (double)p * rope_inv_freq(c >> 1, a.d, a.rope_log2_theta));
           rope_pair(v[2], v[3], (double)p * rope_inv_freq((c >> 1) + 1, a.d, a.rope_log2_theta));
         }
+        // the values as stored in the activation dtype
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (float)(bf16)v[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(v[e]));
         if constexpr (sizeof(T) == 2) {
           bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (bf16)v[e];
+          for (int e = 0; e < 4; ++e) v4[e] = (bf16)v[e];   // exact: already bf16 values
           *reinterpret_cast<bf16x4*>(dst) = v4;
         } else {
           *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
         }
       }
     }
+  }
+  if (a.amax_bits != nullptr) {
+    // per-head maxima for a following 8-bit encode: one atomic per wave
+    // (integer max on the bit patterns of non-negative floats orders them
+    // like their values)
+    amax = row16_max(amax);
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int f = f0 + wf * 64;
+    const int which = f >= HD;
+    const int hh = (which ? f - HD : f) / a.d;
+    if (l == 0 && amax > 0.f) atomicMax(a.amax_bits + which * a.Hkv + hh, __float_as_uint(amax));
   }
 }
 

@@ -49,9 +49,15 @@ struct ProjArgs {
   const void* w_v;
   void* k_out;
   void* v_out;
-  int B, N, D, Hkv, d, n_cap, pos0;
+  int B, N, D, Hkv, d, n_cap;
+  int pos0;                // position of token 0 (rotary embedding)
+  int row0;                // cache row written for token 0 (pos0, or 0 into a staging buffer)
   float eps;
   double rope_log2_theta;  // rotary embedding of K at position pos0 + n (0: none)
+  // amax_bits (non-null, for an 8-bit cache that follows): also raise
+  // amax_bits[head] (K) and amax_bits[Hkv + head] (V) to the bit pattern of
+  // the largest |value| written, each value as stored in the activation dtype
+  uint32_t* amax_bits;
 };
 
 // Position-wise block layers (linear.hip).  Weight matrices are [rows, K]
@@ -136,7 +142,10 @@ struct QuantArgs {
   float* scale;
   uint32_t* amax_bits;  // workspace [Hkv]
   int B, Hkv;
-  long long slab;       // n * d elements per (batch, head)
+  long long slab;       // n * d elements per (batch, head) of kv
+  long long dst_slab;   // elements per (batch, head) of codes (n_cap * d)
+  long long dst_off;    // first element written in each codes slab (pos0 * d)
+  int scale_given;      // encode with scale[] as given instead of setting it from amax_bits
 };
 
 hipError_t launch_attn(const AttnArgs& a, bool is_bf16, int d, bool swa, hipStream_t stream);
@@ -144,6 +153,11 @@ hipError_t launch_decode(const DecodeArgs& a, int q_kind, int kv_kind, int d, hi
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_linear(const LinArgs& a, int mode, bool is_bf16, hipStream_t stream);
 hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream);
+// The steps of launch_quant_fp8 one by one (clear n maxima, raise them over a
+// tensor, encode), for an 8-bit cache filled from a staged projection.
+hipError_t launch_quant_clear(uint32_t* amax_bits, int n, hipStream_t stream);
+hipError_t launch_quant_amax(const QuantArgs& a, bool is_bf16, hipStream_t stream);
+hipError_t launch_quant_encode(const QuantArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
 hipError_t launch_attn_merge(const MergeArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_peak_read(const void* src, long long bytes, uint32_t* partial, int blocks, hipStream_t stream);

@@ -23,6 +23,11 @@ extern LinArgs g_lin;
 extern MergeArgs g_merge;
 extern int g_lin_mode;
 extern int g_decode_kinds[3];
+extern uint32_t* g_clear_ptr;
+extern int g_clear_n;
+extern QuantArgs g_encode[2];
+extern int g_encodes;
+extern int g_amax_passes;
 }  // namespace yoco
 
 static int failures = 0;
@@ -43,27 +48,98 @@ int main() {
 
   // ---- global KV projection
   n = yoco::g_launches;
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 100, 128, 2, 64, 132, 3, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, nullptr, 2, 100, 128, 2, 64, 132, 3, 1e-6f, 0.f, YOCO_BF16, YOCO_BF16, nullptr, 0, nullptr) == YOCO_OK);
   CHECK(yoco::g_launches == n + 1);
   CHECK(yoco::g_proj.B == 2 && yoco::g_proj.N == 100 && yoco::g_proj.pos0 == 3 && yoco::g_proj.n_cap == 132);
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 12, 3, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_ERR_SHAPE);
-  CHECK(yoco_global_kv_proj(P, M, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, 1e-6f, 0.f, YOCO_F32, nullptr) == YOCO_ERR_ALIGN);
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 100, 2, 64, 32, 3, 1e-6f, 0.f, YOCO_F32, nullptr) == YOCO_ERR_UNSUPPORTED);
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 10, 128, 2, 64, 32, 3, NAN, 0.f, YOCO_F32, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, nullptr, 2, 10, 128, 2, 64, 12, 3, 1e-6f, 0.f, YOCO_BF16, YOCO_BF16, nullptr, 0, nullptr) == YOCO_ERR_SHAPE);
+  CHECK(yoco_global_kv_proj(P, M, P, P, P, P, nullptr, nullptr, 2, 10, 128, 2, 64, 32, 3, 1e-6f, 0.f, YOCO_F32, YOCO_F32, nullptr, 0, nullptr) == YOCO_ERR_ALIGN);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, nullptr, 2, 10, 100, 2, 64, 32, 3, 1e-6f, 0.f, YOCO_F32, YOCO_F32, nullptr, 0, nullptr) == YOCO_ERR_UNSUPPORTED);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, nullptr, 2, 10, 128, 2, 64, 32, 3, NAN, 0.f, YOCO_F32, YOCO_F32, nullptr, 0, nullptr) == YOCO_ERR_SHAPE);
   CHECK(yoco::g_launches == n + 1);
   // bf16 with 16384 tokens or more goes to the block-layer GEMM's Q/K/V form with no query heads
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, nullptr, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, 0.f, YOCO_BF16, YOCO_BF16, nullptr, 0, nullptr) == YOCO_OK);
   CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.F == 256 && yoco::g_lin.f1 == 0 && yoco::g_lin.f2 == 128);
   CHECK(yoco::g_lin.h1 == 2 && yoco::g_lin.kv_rows == 9100 && yoco::g_lin.kv_pos0 == 7 && yoco::g_lin.norm == 1);
   CHECK(yoco::g_lin.w0 == nullptr && yoco::g_lin.y0 == nullptr && yoco::g_launches == n + 2);
   CHECK(yoco::g_lin.rope_log2_theta == 0.0);
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, 1024.f, YOCO_BF16, nullptr) ==
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, nullptr, 2, 9000, 128, 2, 64, 9100, 7, 1e-6f, 1024.f, YOCO_BF16, YOCO_BF16, nullptr, 0, nullptr) ==
         YOCO_OK);
   CHECK(yoco::g_lin.rope_log2_theta == 10.0 && yoco::g_lin.rope_pos0 == 7);
   n = yoco::g_launches;
   // and so does a one-token append (the form for a few tokens)
-  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, 16, 1, 128, 2, 64, 40, 39, 1e-6f, 0.f, YOCO_BF16, nullptr) == YOCO_OK);
+  CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, nullptr, 16, 1, 128, 2, 64, 40, 39, 1e-6f, 0.f, YOCO_BF16, YOCO_BF16, nullptr, 0, nullptr) == YOCO_OK);
   CHECK(yoco::g_lin_mode == yoco::kLinQKV && yoco::g_lin.kv_pos0 == 39 && yoco::g_lin.B == 16 && yoco::g_launches == n + 1);
+
+  // ---- global KV projection into an 8-bit cache
+  {
+    float* ks = reinterpret_cast<float*>(arena + 1024);
+    float* vs = reinterpret_cast<float*>(arena + 1056);
+    const int B = 2, N = 40, Hkv = 2, d = 64, n_cap = 64;   // B * N > 64: the 128 x 128 kernel
+    const size_t need = yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, YOCO_BF16, YOCO_FP8_E4M3);
+    CHECK(need == 16 + 2 * (size_t)B * Hkv * N * d * 2);
+    CHECK(yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, YOCO_F32, YOCO_FP8_E4M3) == 16 + 2 * (size_t)B * Hkv * N * d * 4);
+    CHECK(yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, YOCO_BF16, YOCO_BF16) == 0);
+    CHECK(yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, YOCO_FP8_E4M3, YOCO_FP8_E4M3) == 0);
+    CHECK(yoco_global_kv_proj_workspace_bytes(B, N, Hkv, 96, YOCO_BF16, YOCO_FP8_E4M3) == 0);
+    unsigned char* big = static_cast<unsigned char*>(std::aligned_alloc(256, 1 << 20));
+    unsigned char* ws = big;
+    n = yoco::g_launches;
+    yoco::g_encodes = 0;
+    // scales from these rows: clear, projection into the staging (the 128 x 128
+    // kernel collects the maxima), two encodes
+    yoco::g_amax_passes = 0;
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, N, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_BF16,
+                              YOCO_FP8_E4M3, ws, need, nullptr) == YOCO_OK);
+    CHECK(yoco::g_launches == n + 4 && yoco::g_encodes == 2 && yoco::g_amax_passes == 0);
+    CHECK(yoco::g_clear_ptr == reinterpret_cast<uint32_t*>(ws) && yoco::g_clear_n == 2 * Hkv);
+    CHECK(yoco::g_proj.amax_bits == reinterpret_cast<uint32_t*>(ws));
+    CHECK(yoco::g_proj.n_cap == N && yoco::g_proj.pos0 == 0 && yoco::g_proj.row0 == 0);
+    CHECK(yoco::g_proj.k_out == ws + 16 && yoco::g_proj.v_out == ws + 16 + (size_t)B * Hkv * N * d * 2);
+    CHECK(static_cast<const unsigned char*>(yoco::g_proj.v_out) + (size_t)B * Hkv * N * d * 2 == ws + need);
+    CHECK(yoco::g_encode[0].kv == yoco::g_proj.k_out && yoco::g_encode[0].codes == P && yoco::g_encode[0].scale == ks);
+    CHECK(yoco::g_encode[1].kv == yoco::g_proj.v_out && yoco::g_encode[1].scale == vs);
+    CHECK(yoco::g_encode[0].amax_bits == reinterpret_cast<uint32_t*>(ws));
+    CHECK(yoco::g_encode[1].amax_bits == reinterpret_cast<uint32_t*>(ws) + Hkv);
+    CHECK(yoco::g_encode[0].slab == (long long)N * d && yoco::g_encode[0].dst_slab == (long long)n_cap * d &&
+          yoco::g_encode[0].dst_off == 0 && yoco::g_encode[0].scale_given == 0);
+    // a few tokens (the block-layer GEMM's form): a separate pass collects the maxima
+    n = yoco::g_launches;
+    const size_t need1 = yoco_global_kv_proj_workspace_bytes(B, 1, Hkv, d, YOCO_BF16, YOCO_FP8_E4M3);
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, 1, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_BF16,
+                              YOCO_FP8_E4M3, ws, need1, nullptr) == YOCO_OK);
+    CHECK(yoco::g_launches == n + 6 && yoco::g_amax_passes == 2 && yoco::g_lin.kv_rows == 1 && yoco::g_lin.kv_pos0 == 0);
+    // appended rows: staged, then encoded with the given scales at row pos0
+    n = yoco::g_launches;
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, 1, 128, Hkv, d, n_cap, 30, 1e-6f, 1e4f, YOCO_BF16,
+                              YOCO_FP8_E4M3, ws, need1, nullptr) == YOCO_OK);
+    CHECK(yoco::g_launches == n + 3 && yoco::g_amax_passes == 2);
+    CHECK(yoco::g_lin.kv_rows == 1 && yoco::g_lin.kv_pos0 == 0 && yoco::g_lin.rope_pos0 == 30);
+    CHECK(yoco::g_encode[0].scale_given == 1 && yoco::g_encode[0].dst_off == 30LL * d && yoco::g_encode[0].scale == ks);
+    CHECK(yoco::g_encode[1].scale_given == 1 && yoco::g_encode[1].scale == vs);
+    n = yoco::g_launches;
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, N, 128, Hkv, d, n_cap, 16, 1e-6f, 0.f, YOCO_F32,
+                              YOCO_FP8_E4M3, ws, 1 << 20, nullptr) == YOCO_OK);
+    CHECK(yoco::g_launches == n + 3 && yoco::g_proj.pos0 == 16 && yoco::g_proj.row0 == 0 &&
+          yoco::g_proj.amax_bits == nullptr && yoco::g_proj.n_cap == N);
+    // errors, none of which launches
+    n = yoco::g_launches;
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, nullptr, vs, B, N, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_BF16,
+                              YOCO_FP8_E4M3, ws, need, nullptr) == YOCO_ERR_NULL);
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, N, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_BF16,
+                              YOCO_FP8_E4M3, ws, need - 1, nullptr) == YOCO_ERR_WORKSPACE);
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, N, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_BF16,
+                              YOCO_FP8_E4M3, nullptr, 0, nullptr) == YOCO_ERR_WORKSPACE);
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, N, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_BF16,
+                              YOCO_FP8_E4M3, ws + 4, need, nullptr) == YOCO_ERR_ALIGN);
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, N, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_FP8_E4M3,
+                              YOCO_FP8_E4M3, ws, need, nullptr) == YOCO_ERR_DTYPE);
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, ks, vs, B, N, 128, Hkv, d, n_cap, 0, 1e-6f, 0.f, YOCO_BF16,
+                              YOCO_F32, ws, need, nullptr) == YOCO_ERR_DTYPE);
+    CHECK(yoco_global_kv_proj(P, nullptr, P, P, P, P, reinterpret_cast<float*>(arena + 1025), vs, B, N, 128, Hkv, d,
+                              n_cap, 0, 1e-6f, 0.f, YOCO_BF16, YOCO_FP8_E4M3, ws, need, nullptr) == YOCO_ERR_ALIGN);
+    CHECK(yoco::g_launches == n);
+    std::free(big);
+  }
 
   // ---- sliding window and cross prefill
   n = yoco::g_launches;

@@ -25,6 +25,18 @@ hipError_t launch_decode(const DecodeArgs& a, int qk, int kk, int d, hipStream_t
 }
 hipError_t launch_kv_proj(const ProjArgs& a, bool, hipStream_t) { ++g_launches; g_proj = a; return hipSuccess; }
 hipError_t launch_quant_fp8(const QuantArgs& a, bool, hipStream_t) { ++g_launches; g_quant = a; return hipSuccess; }
+uint32_t* g_clear_ptr = nullptr;
+int g_clear_n = 0;
+QuantArgs g_encode[2];
+int g_encodes = 0;
+hipError_t launch_quant_clear(uint32_t* p, int n, hipStream_t) {
+  ++g_launches; g_clear_ptr = p; g_clear_n = n; return hipSuccess;
+}
+int g_amax_passes = 0;
+hipError_t launch_quant_amax(const QuantArgs&, bool, hipStream_t) { ++g_launches; ++g_amax_passes; return hipSuccess; }
+hipError_t launch_quant_encode(const QuantArgs& a, bool, hipStream_t) {
+  ++g_launches; g_encode[g_encodes++ & 1] = a; return hipSuccess;
+}
 hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t) { ++g_launches; g_ring = a; return hipSuccess; }
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t) { ++g_launches; g_gret = a; return hipSuccess; }
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool, hipStream_t) { ++g_launches; g_gret_dec = a; return hipSuccess; }

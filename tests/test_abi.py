@@ -50,16 +50,26 @@ def test_version_and_status_strings(L):
 
 
 def proj(L, **kw):
-    a = dict(x=P, g=None, wk=P, wv=P, ko=P, vo=P, B=1, N=8, D=128, Hkv=2, d=64, n_cap=16, pos0=0, eps=1e-6,
-             rope=0.0, dt=yk.BF16)
+    a = dict(x=P, g=None, wk=P, wv=P, ko=P, vo=P, ks=None, vs=None, B=1, N=8, D=128, Hkv=2, d=64, n_cap=16, pos0=0,
+             eps=1e-6, rope=0.0, dt=yk.BF16, kvdt=None, ws=None, ws_bytes=0)
     a.update(kw)
-    return L.yoco_global_kv_proj(a["x"], a["g"], a["wk"], a["wv"], a["ko"], a["vo"], a["B"], a["N"], a["D"],
-                                 a["Hkv"], a["d"], a["n_cap"], a["pos0"], a["eps"], a["rope"], a["dt"], None)
+    kvdt = a["dt"] if a["kvdt"] is None else a["kvdt"]
+    return L.yoco_global_kv_proj(a["x"], a["g"], a["wk"], a["wv"], a["ko"], a["vo"], a["ks"], a["vs"], a["B"], a["N"],
+                                 a["D"], a["Hkv"], a["d"], a["n_cap"], a["pos0"], a["eps"], a["rope"], a["dt"], kvdt,
+                                 a["ws"], a["ws_bytes"], None)
+
+
+FP8 = dict(kvdt=yk.FP8_E4M3, ks=P, vs=P, ws=P, ws_bytes=1 << 20)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), NULL), (dict(wv=None), NULL), (dict(vo=None), NULL),
-    (dict(dt=yk.FP8_E4M3), DTYPE), (dict(dt=7), DTYPE),
+    (dict(dt=yk.FP8_E4M3, kvdt=yk.BF16), DTYPE), (dict(dt=7, kvdt=yk.BF16), DTYPE),
+    # an 8-bit cache: scales required; its workspace only when the call sets the scales (pos0 == 0)
+    (dict(FP8, ks=None), NULL), (dict(FP8, vs=None), NULL),
+    (dict(FP8, ws=None), WS), (dict(FP8, ws_bytes=16), WS), (dict(FP8, ws=MIS), ALIGN), (dict(FP8, ks=P + 2), ALIGN),
+    (dict(FP8, dt=yk.FP8_E4M3), DTYPE), (dict(kvdt=yk.F32), DTYPE), (dict(dt=yk.F32, kvdt=yk.BF16), DTYPE),
+    (dict(FP8, N=0), SHAPE), (dict(FP8, d=96), UNSUP),
     (dict(N=0), SHAPE), (dict(pos0=-1), SHAPE), (dict(pos0=9), SHAPE), (dict(n_cap=7), SHAPE),
     (dict(eps=float("nan")), SHAPE), (dict(eps=-1.0), SHAPE), (dict(Hkv=0), SHAPE),
     (dict(rope=-1.0), SHAPE), (dict(rope=float("nan")), SHAPE), (dict(rope=float("inf")), SHAPE),
@@ -68,6 +78,17 @@ def proj(L, **kw):
 ])
 def test_global_kv_proj_errors(L, kw, code):
     assert proj(L, **kw) == code
+
+
+def test_global_kv_proj_workspace_query():
+    B, N, Hkv, d = 2, 300, 4, 128
+    assert yk.yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, yk.BF16, yk.BF16) == 0
+    assert yk.yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, yk.F32, yk.F32) == 0
+    # per-head maxima (2 Hkv words, one 16-byte line here), then K and V staged in the activation dtype
+    assert yk.yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, yk.BF16, yk.FP8_E4M3) == 32 + 2 * B * Hkv * N * d * 2
+    assert yk.yoco_global_kv_proj_workspace_bytes(B, N, Hkv, d, yk.F32, yk.FP8_E4M3) == 32 + 2 * B * Hkv * N * d * 4
+    assert yk.yoco_global_kv_proj_workspace_bytes(B, N, Hkv, 96, yk.BF16, yk.FP8_E4M3) == 0
+    assert yk.yoco_global_kv_proj_workspace_bytes(0, N, Hkv, d, yk.BF16, yk.FP8_E4M3) == 0
 
 
 def swa(L, **kw):

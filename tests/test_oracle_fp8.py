@@ -114,3 +114,29 @@ def test_quantize_per_head_scales_and_error_bound():
         # half a quantisation step: 2^-4 relative for normals, 2^-10 absolute for subnormals
         bound = np.maximum(y * 2.0 ** -4, 2.0 ** -10) * s * (1 + 1e-6)
         assert np.all(np.abs(deq[:, h] - x[:, h]) <= bound)
+
+
+def test_encode_with_given_scales_round_trips_every_code():
+    """With a power-of-two scale the division is exact, so the value s*decode(c)
+    of every finite code c must encode back to c (negative zero to 0x80)."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    for s in (0.25, 1.0, 8.0):
+        vals = (e4m3_decode(codes) * s).astype(np.float32).reshape(1, 1, -1, 1)
+        scales = np.array([s], dtype=np.float32)
+        assert np.array_equal(oracle.encode_kv_fp8(vals, scales).reshape(-1), codes)
+
+
+def test_encode_with_given_scales_saturates_and_uses_each_heads_scale():
+    x = np.array([[[[1000.0, -1000.0, 3.0, -3.0]], [[1000.0, -1000.0, 3.0, -3.0]]]], dtype=np.float32)
+    c = oracle.encode_kv_fp8(x, np.array([1.0, 2.0], dtype=np.float32))
+    # 3 = 1.5 * 2^1: exponent field 1 + 7 = 0b1000, mantissa 0b100
+    assert list(c[0, 0, 0]) == [0x7E, 0xFE, 0x44, 0xC4]
+    # 3 / 2 = 1.5 * 2^0: exponent field 0b0111
+    assert list(c[0, 1, 0]) == [0x7E, 0xFE, 0x3C, 0xBC]
+
+
+def test_encode_with_the_quantisers_own_scales_gives_its_codes():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 3, 17, 8)).astype(np.float32)
+    codes, scales = quantize_kv_fp8(x)
+    assert np.array_equal(oracle.encode_kv_fp8(x, scales), codes)
