@@ -41,8 +41,33 @@ def _compile(src):
     return obj
 
 
+# A test-only library over decode.hip (tests/gpu_lib): runs the decode kernels
+# with an explicit split plan and K-load form, for the test that compares the
+# two forms bitwise.  Built with the product so that GPU runs need no compiler.
+TEST_LIB = os.path.join(ROOT, "tests", "gpu_lib", "libyoco_decode_forms.so")
+TEST_SRC = os.path.join(ROOT, "tests", "gpu_lib", "decode_forms.hip")
+
+
+def build_test_lib(verbose=True):
+    obj = os.path.join(BUILD, "decode_forms.hip.o")
+    r = subprocess.run([HIPCC, *CFLAGS, "-c", TEST_SRC, "-o", obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {TEST_SRC}:\n{r.stderr}")
+    objs = [obj, os.path.join(BUILD, "decode.hip.o"), os.path.join(BUILD, "plan.cpp.o")]
+    tmp = TEST_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, TEST_LIB)
+    if verbose:
+        print(f"built {TEST_LIB}")
+    return TEST_LIB
+
+
 def build(jobs=None, verbose=True):
-    """Compile every source for gfx950 and link libyoco.so; returns its path."""
+    """Compile every source for gfx950 and link libyoco.so (and the test-only
+    decode-form library); returns libyoco.so's path."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
     with cf.ThreadPoolExecutor(jobs) as ex:
@@ -55,6 +80,7 @@ def build(jobs=None, verbose=True):
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_test_lib(verbose)
     return LIB
 
 

@@ -166,3 +166,29 @@ def test_cache_past_2_pow_31_bytes_reads_its_first_keys():
     assert (o[0, 0, 0].float() - v[0, 0, 0].float()).abs().max().item() <= 2e-2
     del k, v
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["swa", "causal"])
+def test_attention_writes_nothing_outside_its_outputs(kind, dt):
+    """o and lse inside NaN-filled guard regions (ragged query count, several
+    query tiles): every guard element is still NaN afterwards, every output
+    element finite."""
+    B, Hq, Hkv, N, d, G = 2, 6, 2, 333, 128, 8192
+    q, k, v = _inputs(B, Hq, Hkv, N, N, d, dt, 820)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    obuf = torch.full((G + B * Hq * N * d + G,), float("nan"), dtype=tdt, device=DEV)
+    lbuf = torch.full((G + B * Hq * N + G,), float("nan"), dtype=torch.float32, device=DEV)
+    o = obuf[G:G + B * Hq * N * d].view(B, Hq, N, d)
+    lse = lbuf[G:G + B * Hq * N].view(B, Hq, N)
+    if kind == "swa":
+        yk.yoco_swa_attn(q, k, v, 100, o=o, lse=lse)
+    else:
+        yk.yoco_cross_attn_prefill(q[:, :, 33:].contiguous(), k, v, q_offset=33, o=obuf[G:G + B * Hq * (N - 33) * d]
+                                   .view(B, Hq, N - 33, d), lse=lbuf[G:G + B * Hq * (N - 33)].view(B, Hq, N - 33))
+        o = obuf[G:G + B * Hq * (N - 33) * d]
+        lse = lbuf[G:G + B * Hq * (N - 33)]
+    torch.cuda.synchronize()
+    for buf, m in ((obuf, o.numel()), (lbuf, lse.numel())):
+        assert bool(torch.isnan(buf[:G]).all()) and bool(torch.isnan(buf[G + m:]).all())
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())

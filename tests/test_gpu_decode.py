@@ -1,5 +1,8 @@
 """GPU parity of yoco_cross_attn_decode (bf16, f32, fp8-e4m3 caches) and of the
 fp8 cache writer yoco_kv_quantize_fp8 against the oracle."""
+import ctypes
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -88,14 +91,18 @@ def test_quantize_fp8_bit_exact(src):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,n,lens", [
-    (2, 8, 2, 3000, [3000, 1234]),
+@pytest.mark.parametrize("B,Hq,Hkv,n,lens,d", [
+    (2, 8, 2, 3000, [3000, 1234], 128),
     # 32 sequences of ragged length over a 16384-row cache (splits of 1024 keys)
-    (32, 32, 8, 16384, [16384, 1, 16383, 1024, 1025, 2047, 5000, 16000] * 4),
+    (32, 32, 8, 16384, [16384, 1, 16383, 1024, 1025, 2047, 5000, 16000] * 4, 128),
+    # head dim 64 (one code byte per lane and key in P V) and 1, 3, 6 query heads per KV head
+    (2, 8, 2, 3000, [3000, 777], 64),
+    (3, 4, 4, 2500, [2500, 1, 1999], 64),        # 1 query head per KV head
+    (2, 6, 2, 4100, [4100, 4099], 128),          # 3 per KV head
+    (2, 12, 2, 1500, [1500, 65], 64),            # 6 per KV head: two head groups, the second of 2
 ])
-def test_decode_fp8_parity(B, Hq, Hkv, n, lens):
-    d = 128
-    print(f"fp8 decode parity B={B} Hq={Hq} Hkv={Hkv} n={n}", flush=True)
+def test_decode_fp8_parity(B, Hq, Hkv, n, lens, d):
+    print(f"fp8 decode parity B={B} Hq={Hq} Hkv={Hkv} n={n} d={d}", flush=True)
     q = randn((B, Hq, d), 940, device=DEV)
     kf = randn((B, Hkv, n, d), 941, dtype="f32", device=DEV)
     vf = randn((B, Hkv, n, d), 942, dtype="f32", device=DEV)
@@ -121,3 +128,70 @@ def test_decode_constant_values():
     o = yk.yoco_cross_attn_decode(q, k, v, n)
     torch.cuda.synchronize()
     assert (o.float() - 1).abs().max().item() <= 2e-2
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_writes_nothing_outside_its_outputs(kv):
+    """o and lse live inside NaN-filled guard regions of a larger allocation:
+    every guard element is still NaN (bitwise) after the call."""
+    B, Hq, Hkv, n, d, G = 3, 8, 2, 5000, 128, 4096
+    q = randn((B, Hq, d), 960, device=DEV)
+    if kv == "fp8":
+        kc, ks = yk.yoco_kv_quantize_fp8(randn((B, Hkv, n, d), 961, dtype="f32", device=DEV))
+        vc, vs = yk.yoco_kv_quantize_fp8(randn((B, Hkv, n, d), 962, dtype="f32", device=DEV))
+    else:
+        kc, vc = randn((B, Hkv, n, d), 961, device=DEV), randn((B, Hkv, n, d), 962, device=DEV)
+        ks = vs = None
+    obuf = torch.full((G + B * Hq * d + G,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lbuf = torch.full((G + B * Hq + G,), float("nan"), dtype=torch.float32, device=DEV)
+    o = obuf[G:G + B * Hq * d].view(B, Hq, d)
+    lse = lbuf[G:G + B * Hq].view(B, Hq)
+    yk.yoco_cross_attn_decode(q, kc, vc, n, k_scale=ks, v_scale=vs, o=o, lse=lse)
+    torch.cuda.synchronize()
+    for buf, m in ((obuf, B * Hq * d), (lbuf, B * Hq)):
+        assert bool(torch.isnan(buf[:G]).all()) and bool(torch.isnan(buf[G + m:]).all())
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+
+
+# ---------------------------------------------------------------------------
+# The two K-load forms of the bf16 d = 128 split kernel over one split plan
+# ---------------------------------------------------------------------------
+_FORMS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gpu_lib", "libyoco_decode_forms.so")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,ctx,lens,n_splits", [
+    (16, 32, 8, 32768, None, 32),                                  # 1024-key splits (libyoco's 4096-workgroup plan)
+    (4, 24, 8, 20000, [20000, 1, 12345, 19999], 7),                # ragged, 2880-key splits
+    (2, 8, 2, 3000, [3000, 64], 47),                               # 64-key splits (short: operand-layout territory)
+])
+def test_decode_k_load_forms_are_bitwise_equal(B, Hq, Hkv, ctx, lens, n_splits):
+    """The whole-line form (8 keys x one 128-byte line per load, a DPP row
+    rotate into the operand layout) and the operand-layout form run over the
+    same split plan give identical o and lse."""
+    print(f"decode K-load forms B={B} Hq={Hq} ctx={ctx} splits={n_splits}", flush=True)
+    L = ctypes.CDLL(_FORMS)
+    vp, i_, f_ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.yoco_test_decode_form.argtypes = [vp] * 4 + [i_] + [vp] * 3 + [i_] * 7 + [f_, vp]
+    d = 128
+    chunk = -(-ctx // n_splits)
+    chunk = -(-chunk // 64) * 64
+    n_splits = -(-ctx // chunk)
+    q = randn((B, Hq, d), 970, device=DEV)
+    k = randn((B, Hkv, ctx, d), 971, device=DEV)
+    v = randn((B, Hkv, ctx, d), 972, device=DEV)
+    cl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ws = torch.empty(B * Hq * n_splits * (d + 2), dtype=torch.float32, device=DEV)
+    outs = []
+    for full in (0, 1):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        p = lambda t: None if t is None else vp(t.data_ptr())  # noqa: E731
+        st = L.yoco_test_decode_form(p(q), p(k), p(v), p(cl), ctx, p(o), p(lse), p(ws), B, Hq, Hkv, ctx, n_splits,
+                                     chunk, full, f_(d ** -0.5 * 1.4426950408889634),
+                                     vp(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    ro, _ = oracle.decode_attention(to64(q), to64(k), to64(v), [ctx] * B if lens is None else lens)
+    check(to64(outs[1][0]), ro, "bf16", "whole-line form", rel_axes=(2,))
