@@ -35,6 +35,16 @@ head is not part of the path); the cross-decoder's residual stream continues
 from the self-decoder output, the same tensor the global K/V are projected
 from.
 
+The self-decoder's layers may instead be gated retention ([S §3 Gated
+Retention]; [P seg. 16]; the better-scoring layout of [S §4 Scaling model
+size]), BlockParams.self_kind = "gret".  Readings taken for such a layer (the
+pages give its parts in words only): from n = rmsnorm(x), q = W_q n,
+k = W_k n, v = W_v n with n_heads heads each (no grouping, no rotation), the
+per-head gate logits z = W_z n, the retention of oracle/retention.py with
+temperature gret_tau, the per-head GroupNorm times swish(W_g n), then W_o and
+the residual, then the feed-forward as for a window layer.  Generation keeps
+one d x d state per head and layer in place of the window ring.
+
 Position-wise products are computed row by row with one routine (a
 matrix-vector product), so that a row's value is bitwise the same whether or
 not other rows are computed -- this is what makes the early-exit identity
@@ -50,6 +60,7 @@ import numpy as np
 
 from .attention import attend_row, cross_prefill_attention, ring_window, swa_attention
 from .projection import global_kv_proj, rmsnorm_row
+from .retention import gret_group_norm_swish, gret_log_decay, gret_recurrent
 from .rope import apply_rope
 
 __all__ = ["BlockParams", "linear_rows", "silu", "swiglu_hidden_row", "swiglu_ffn_row", "yoco_block", "yoco_block_early_exit",
@@ -78,6 +89,14 @@ class BlockParams:
     # rotary embedding base (0: none): queries and keys of every attention,
     # and the global keys, rotated at their absolute positions
     rope_theta: float = 0.0
+    # self-decoder layer kind: "swa" (sliding-window attention) or "gret"
+    # (gated retention: swa_wk / swa_wv are then [n_heads*d, D], and each
+    # layer adds gate-logit weights [n_heads, D] and swish-gate weights
+    # [n_heads*d, D]); gated retention takes no rotary embedding
+    self_kind: str = "swa"
+    gret_wz: List[np.ndarray] = field(default_factory=list)
+    gret_wg: List[np.ndarray] = field(default_factory=list)
+    gret_tau: float = 16.0
 
     def ffn(self, kind, layer):
         lst = self.swa_ffn if kind == "swa" else self.cross_ffn
@@ -150,10 +169,28 @@ def _merge(t):
     return t.transpose(0, 2, 1, 3).reshape(B, N, H * d)
 
 
+def _gret_layer_rows(x, p, layer):
+    """The residual stream after gated-retention layer `layer` (before its
+    feed-forward), every position at once."""
+    H, d = p.n_heads, p.head_dim
+    n = _norm_rows(x, p.eps)
+    q = _heads(linear_rows(n, p.swa_wq[layer]), H, d)
+    k = _heads(linear_rows(n, p.swa_wk[layer]), H, d)
+    v = _heads(linear_rows(n, p.swa_wv[layer]), H, d)
+    z = linear_rows(n, p.gret_wz[layer]).transpose(0, 2, 1)        # [B, H, N]
+    y, _ = gret_recurrent(q, k, v, z, p.gret_tau)
+    g = linear_rows(n, p.gret_wg[layer])                           # [B, N, H*d]
+    return x + linear_rows(gret_group_norm_swish(y, g, p.eps), p.swa_wo[layer])
+
+
 def _self_decoder_and_projection(x, p):
     Hq, Hkv, d = p.n_heads, p.n_kv_heads, p.head_dim
     x = np.array(x, dtype=np.float64)
     for layer, (wq, wk, wv, wo) in enumerate(zip(p.swa_wq, p.swa_wk, p.swa_wv, p.swa_wo)):
+        if p.self_kind == "gret":
+            x = _gret_layer_rows(x, p, layer)
+            x = _ffn_rows(x, p.ffn("swa", layer), p.eps)
+            continue
         n = _norm_rows(x, p.eps)
         q = _rope(_heads(linear_rows(n, wq), Hq, d), 0, p)
         k = _rope(_heads(linear_rows(n, wk), Hkv, d), 0, p)
@@ -228,6 +265,7 @@ def yoco_block_generate(x, p):
     g = Hq // Hkv
     scale = 1.0 / math.sqrt(d)
     rings = [(np.zeros((B, Hkv, W, d)), np.zeros((B, Hkv, W, d))) for _ in p.swa_wq]
+    states = [np.zeros((B, Hq, d, d)) for _ in p.swa_wq]      # gated-retention layers
     k_glob = np.zeros((B, Hkv, N, d))
     v_glob = np.zeros((B, Hkv, N, d))
     out = np.empty_like(x)
@@ -238,6 +276,23 @@ def yoco_block_generate(x, p):
                                                                  rings)):
             ffn = p.ffn("swa", layer)
             new = np.empty_like(h_t)
+            if p.self_kind == "gret":
+                # one recurrent step per head: S <- gamma S + k^T v, y = q S
+                for b in range(B):
+                    n = rmsnorm_row(h_t[b], None, p.eps)
+                    q, k, v = (wq @ n).reshape(Hq, d), (wk @ n).reshape(Hq, d), (wv @ n).reshape(Hq, d)
+                    lg = gret_log_decay(p.gret_wz[layer] @ n, p.gret_tau)
+                    y = np.empty((Hq, d))
+                    for h in range(Hq):
+                        S = math.exp(lg[h]) * states[layer][b, h] + np.outer(k[h], v[h])
+                        states[layer][b, h] = S
+                        y[h] = q[h] @ S
+                    gn = gret_group_norm_swish(y[None, :, None, :], (p.gret_wg[layer] @ n)[None, None, :], p.eps)
+                    new[b] = h_t[b] + wo @ gn[0, 0]
+                    if ffn is not None:
+                        new[b] = swiglu_ffn_row(new[b], ffn, p.eps)
+                h_t = new
+                continue
             for b in range(B):
                 n = rmsnorm_row(h_t[b], None, p.eps)
                 q = _rope((wq @ n).reshape(Hq, 1, d), t, p)[:, 0]

@@ -151,3 +151,100 @@ def test_swiglu_row_brute_force():
         hid.append(a / (1 + math.exp(-a)) * b)
     ref = [x[i] + sum(wd[i, j] * hid[j] for j in range(F)) for i in range(D)]
     assert np.allclose(oracle.swiglu_ffn_row(x, (wg, wu, wd), 1e-6), ref, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# The block with a gated-retention self-decoder
+# ---------------------------------------------------------------------------
+def make_gret_params(D=32, H=4, Hkv=2, d=8, Ls=2, Lc=2, ffn_dim=None, tau=4.0):
+    p = make_params(D=D, Hq=H, Hkv=Hkv, d=d, Ls=Ls, Lc=Lc, ffn_dim=ffn_dim)
+    std = 1 / math.sqrt(D)
+    r = lambda *s: RNG.standard_normal(s) * std  # noqa: E731
+    p.self_kind = "gret"
+    p.swa_wk = [r(H * d, D) for _ in range(Ls)]
+    p.swa_wv = [r(H * d, D) for _ in range(Ls)]
+    p.gret_wz = [r(H, D) * 6 for _ in range(Ls)]        # gate logits of order +-6: decays from ~0 to ~1
+    p.gret_wg = [r(H * d, D) for _ in range(Ls)]
+    p.gret_tau = tau
+    return p
+
+
+@pytest.mark.parametrize("ffn_dim", [None, 24])
+def test_gret_block_early_exit_and_generation_are_bitwise(ffn_dim):
+    p = make_gret_params(ffn_dim=ffn_dim)
+    x = RNG.standard_normal((2, 21, 32))
+    full, (kf, vf) = oracle.yoco_block(x, p)
+    last, _ = oracle.yoco_block_early_exit(x, p)
+    gen, (kg, vg), _ = oracle.yoco_block_generate(x, p)
+    assert np.array_equal(full[:, -1], last)
+    assert np.array_equal(full, gen) and np.array_equal(kf, kg) and np.array_equal(vf, vg)
+
+
+def test_gret_block_causality_bitwise():
+    p = make_gret_params(ffn_dim=16)
+    x = RNG.standard_normal((1, 18, 32))
+    x2 = x.copy()
+    x2[:, 10:] = -1e4
+    a, _ = oracle.yoco_block(x, p)
+    b, _ = oracle.yoco_block(x2, p)
+    assert np.array_equal(a[:, :10], b[:, :10])
+
+
+def _torch_gret_block(x, p):
+    """Independent composition: gated retention in its parallel form with an
+    explicit decay matrix built from torch's logsigmoid, GroupNorm from
+    torch.nn.functional.group_norm, swish from silu."""
+    t = lambda a: torch.from_numpy(np.asarray(a))  # noqa: E731
+    X = t(x)
+    B, N, D = X.shape
+    H, Hkv, d = p.n_heads, p.n_kv_heads, p.head_dim
+    g = H // Hkv
+    F = torch.nn.functional
+    split = lambda y, h: y.view(B, N, h, d).permute(0, 2, 1, 3)  # noqa: E731
+    causal = torch.arange(N)[None, :] <= torch.arange(N)[:, None]
+    for layer in range(len(p.swa_wq)):
+        n = F.rms_norm(X, (D,), eps=p.eps)
+        q, k, v = (split(F.linear(n, t(w[layer])), H) for w in (p.swa_wq, p.swa_wk, p.swa_wv))
+        lg = F.logsigmoid(F.linear(n, t(p.gret_wz[layer]))).permute(0, 2, 1) / p.gret_tau   # [B, H, N]
+        c = torch.cumsum(lg, dim=-1)
+        dec = torch.exp(c[..., :, None] - c[..., None, :]).masked_fill(~causal, 0.0)
+        y = (q @ k.transpose(-1, -2) * dec) @ v                                            # [B, H, N, d]
+        yn = F.group_norm(y.permute(0, 2, 1, 3).reshape(B * N, H * d), H, eps=p.eps).view(B, N, H * d)
+        X = X + F.linear(F.silu(F.linear(n, t(p.gret_wg[layer]))) * yn, t(p.swa_wo[layer]))
+        if p.swa_ffn:
+            wg_, wu_, wd_ = p.swa_ffn[layer]
+            n2 = F.rms_norm(X, (D,), eps=p.eps)
+            X = X + F.linear(F.silu(F.linear(n2, t(wg_))) * F.linear(n2, t(wu_)), t(wd_))
+    n = F.rms_norm(X, (D,), eps=p.eps)
+    K, V = split(F.linear(n, t(p.glob_wk)), Hkv), split(F.linear(n, t(p.glob_wv)), Hkv)
+    for layer, (wq, wo) in enumerate(zip(p.cross_wq, p.cross_wo)):
+        qq = split(F.linear(F.rms_norm(X, (D,), eps=p.eps), t(wq)), H)
+        o = F.scaled_dot_product_attention(qq, K.repeat_interleave(g, 1), V.repeat_interleave(g, 1), attn_mask=causal)
+        X = X + F.linear(o.permute(0, 2, 1, 3).reshape(B, N, H * d), t(wo))
+        if p.cross_ffn:
+            wg_, wu_, wd_ = p.cross_ffn[layer]
+            n2 = F.rms_norm(X, (D,), eps=p.eps)
+            X = X + F.linear(F.silu(F.linear(n2, t(wg_))) * F.linear(n2, t(wu_)), t(wd_))
+    return X.numpy()
+
+
+@pytest.mark.parametrize("ffn_dim", [None, 40])
+def test_gret_block_matches_independent_torch_composition(ffn_dim):
+    p = make_gret_params(D=48, H=6, Hkv=2, d=8, Ls=2, Lc=2, ffn_dim=ffn_dim, tau=3.0)
+    x = RNG.standard_normal((2, 26, 48))
+    out, _ = oracle.yoco_block(x, p)
+    assert np.max(np.abs(out - _torch_gret_block(x, p))) < 1e-10
+
+
+def test_gret_self_decoder_differs_from_the_window_one():
+    """The gated-retention branch is really taken (same weights, window layers
+    instead: a different block)."""
+    p = make_gret_params()
+    x = RNG.standard_normal((1, 12, 32))
+    a, _ = oracle.yoco_block(x, p)
+    p.self_kind = "swa"
+    p.n_kv_heads = p.n_heads   # window layers with the same [H*d, D] K/V weights
+    p.glob_wk = np.vstack([p.glob_wk, p.glob_wk])
+    p.glob_wv = np.vstack([p.glob_wv, p.glob_wv])
+    b, _ = oracle.yoco_block(x, p)
+    assert np.max(np.abs(a - b)) > 1e-2
