@@ -60,19 +60,24 @@ template <> struct Raw8<bf16> { u32x4 w; };
 template <> struct Raw8<float> { u32x4 lo, hi; };
 template <> struct Raw8<uint8_t> { u32x2 w; };
 
+// The same 8 elements through a buffer resource: `off` bytes from its base.
+// Bytes at or past the resource's size read as zeros.
 template <typename KVT>
-__device__ __forceinline__ Raw8<KVT> load_raw8(const KVT* p) {
-  Raw8<KVT> r;
+__device__ __forceinline__ Raw8<KVT> buf_raw8(__amdgpu_buffer_rsrc_t r, int off) {
+  Raw8<KVT> x;
   if constexpr (sizeof(KVT) == 2) {
-    r.w = *reinterpret_cast<const u32x4*>(p);
+    x.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   } else if constexpr (sizeof(KVT) == 4) {
-    r.lo = *reinterpret_cast<const u32x4*>(p);
-    r.hi = *reinterpret_cast<const u32x4*>(p + 4);
+    x.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    x.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
   } else {
-    r.w = *reinterpret_cast<const u32x2*>(p);
+    x.w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
   }
-  return r;
+  return x;
 }
+
+// Cache-policy bits of a buffer load: streaming (non-temporal).
+constexpr int kLoadNT = 2;
 
 // Raw K elements -> matrix-core operand fragment.
 template <typename KVT>
@@ -83,18 +88,29 @@ __device__ __forceinline__ typename Elem<typename KvTraits<KVT>::mma_t>::frag to
     f32x4 a = __builtin_bit_cast(f32x4, r.lo), b = __builtin_bit_cast(f32x4, r.hi);
     return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   } else {
+    // two codes per instruction, straight to bf16 (exact: every e4m3 value
+    // is a bf16 value; the scale operand is 1)
     bf16x8 f;
 #pragma unroll
     for (int wd = 0; wd < 2; ++wd) {
-      const f32x2 lo = fp8x2_to_f32(r.w[wd], false);
-      const f32x2 hi = fp8x2_to_f32(r.w[wd], true);
-      f[4 * wd + 0] = (bf16)lo[0];   // exact: every e4m3 value is a bf16 value
-      f[4 * wd + 1] = (bf16)lo[1];
-      f[4 * wd + 2] = (bf16)hi[0];
-      f[4 * wd + 3] = (bf16)hi[1];
+      const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.w[wd], 1.0f, false);
+      const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.w[wd], 1.0f, true);
+      f[4 * wd + 0] = lo[0];
+      f[4 * wd + 1] = lo[1];
+      f[4 * wd + 2] = hi[0];
+      f[4 * wd + 3] = hi[1];
     }
     return f;
   }
+}
+
+// One lane's V slice of one row through a buffer resource (streaming load).
+template <typename W>
+__device__ __forceinline__ W buf_vword(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (sizeof(W) == 1) return (W)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, kLoadNT);
+  else if constexpr (sizeof(W) == 2) return (W)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kLoadNT);
+  else if constexpr (sizeof(W) == 4) return (W)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadNT);
+  else return __builtin_bit_cast(W, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadNT));
 }
 
 // The V slice one lane owns in one key row: DPL = D/64 consecutive elements.
@@ -181,9 +197,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   float sc = a.scale_log2;
   if constexpr (sizeof(KVT) == 1) sc *= a.k_scale[kvh];
 
+  // Loads go through buffer resources built per 16-key block: base = the
+  // block's first row, size = its rows below key_end.  Lane offsets are then
+  // loop-invariant (no per-load address arithmetic) and rows at or past
+  // key_end -- the tail of the last block -- read as zeros (masked out).
+  constexpr int RB = D * (int)sizeof(KVT);                                       // bytes per cache row
   const size_t head_off = (size_t)(b * a.Hkv + kvh) * a.n_cap;
-  const KVT* kb = static_cast<const KVT*>(a.k) + head_off * D + 8 * G;          // K: MFMA operand layout
-  const KVT* vb = static_cast<const KVT*>(a.v) + head_off * D + DPL * l;        // V: lane-owned dims
+  const char* kh = uniform_ptr(static_cast<const char*>(a.k) + head_off * RB);
+  const char* vh = uniform_ptr(static_cast<const char*>(a.v) + head_off * RB);
+  const int kend = __builtin_amdgcn_readfirstlane(key_end);
+  auto block_rsrc = [&](const char* hb, int key0) {
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, kend - key0)));
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(hb + (size_t)key0 * RB), (short)0, rows * RB, kBufferFlags);
+  };
+  const int koff = r16 * RB + 8 * G * (int)sizeof(KVT);   // K, operand layout: key r16, elements 8G ..
+  const int voff = DPL * l * (int)sizeof(KVT);            // V: this lane's dims
 
   float m_run[4], l_run[4];
   float acc[4][DPL];
@@ -203,13 +231,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // is under way when the second arrives (+3 % on the 32K decode; fp8 measured
   // slower with it and keeps one block).
   constexpr bool KFULL = KF && sizeof(KVT) == 2;
-  auto is_lead = [](int c) { return !KFULL && sizeof(KVT) == 2 && (c & 1) == 0; };
+  // fp8 caches: every K and V load is issued two blocks ahead (a block is
+  // only 4 KB there, half of a bf16 block)
+  constexpr bool AHEAD2 = sizeof(KVT) == 1;
+  auto is_lead = [](int c) { return AHEAD2 || (!KFULL && sizeof(KVT) == 2 && (c & 1) == 0); };
   Raw8<KVT> kc[NC], kn[NC], k2[NC];
   auto load_k = [&](int key0, Raw8<KVT>* kr, bool lead) {
-    const int kkey = min(key0 + r16, key_end - 1);   // never read rows >= ctx_b
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kh, key0);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      if (is_lead(c) == lead) kr[c] = load_raw8<KVT>(kb + (size_t)kkey * D + 32 * c);
+      if (is_lead(c) == lead) kr[c] = buf_raw8<KVT>(rk, koff + 32 * c * (int)sizeof(KVT));
   };
   // Whole-line K loads (bf16, long splits): instruction (line L, half h)
   // gives lane (G, k) the 16 bytes of key 8h + (k & 7) at element
@@ -220,16 +251,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // two halves of line L into the fragments of steps 2L and 2L + 1 (lane
   // (G, k): key k, elements 32c + 8G .. +7).  Three blocks in flight.
   constexpr int NL = D / 64;
-  const KVT* kb0 = static_cast<const KVT*>(a.k) + head_off * D;
+  const int kfoff = (r16 & 7) * RB + (32 * (r16 >> 3) + 8 * G) * (int)sizeof(KVT);
   auto load_kf = [&](int key0, u32x4 (&raw)[NL][2]) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kh, key0);
 #pragma unroll
     for (int L = 0; L < NL; ++L)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = min(key0 + 8 * h + (r16 & 7), key_end - 1);
-        raw[L][h] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(kb0 + (size_t)key * D + 64 * L + 32 * (r16 >> 3) + 8 * G));
-      }
+      for (int h = 0; h < 2; ++h)
+        raw[L][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            rk, kfoff + 8 * h * RB + 64 * L * (int)sizeof(KVT), 0, kLoadNT));
   };
   auto kf_frags = [&](const u32x4 (&raw)[NL][2], Raw8<KVT>* kr) {
     if constexpr (KFULL) {
@@ -244,15 +274,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     }
   };
   u32x4 kf0[NL][2], kf1[NL][2], kf2[NL][2], kf3[NL][2];
-  vword vc[16], vn[16];
+  vword vc[16], vn[16], v2[16];
   auto load_v = [&](int key0, vword* vr) {
+    // each V row is consumed whole by these loads: stream it non-temporally
+    // (+8 % on the 32K decode over cached loads)
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(vh, key0);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int vkey = min(key0 + j, key_end - 1);
-      // each V row is consumed whole by this one load: stream it non-temporally
-      // (+8 % on the 32K decode over cached loads)
-      vr[j] = __builtin_nontemporal_load(reinterpret_cast<const vword*>(vb + (size_t)vkey * D));
-    }
+    for (int j = 0; j < 16; ++j) vr[j] = buf_vword<vword>(rv, voff + j * RB);
   };
 
   if constexpr (KFULL) {
@@ -265,13 +293,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
   load_v(key_begin, vc);
   if (!KFULL && key_begin + 16 < key_end) load_k(key_begin + 16, kn, true);
+  if (AHEAD2 && key_begin + 16 < key_end) load_v(key_begin + 16, vn);
   for (int key0 = key_begin; key0 < key_end; key0 += 16) {
     const bool has_next = key0 + 16 < key_end;
     if (has_next) {
       if constexpr (!KFULL) load_k(key0 + 16, kn, false);
-      load_v(key0 + 16, vn);
+      if constexpr (!AHEAD2) load_v(key0 + 16, vn);
     }
     if (!KFULL && key0 + 32 < key_end) load_k(key0 + 32, k2, true);
+    if (AHEAD2 && key0 + 32 < key_end) load_v(key0 + 32, v2);
     if constexpr (KFULL) {
       if (key0 + 48 < key_end) load_kf(key0 + 48, kf3);
       kf_frags(kf0, kc);
@@ -347,16 +377,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
             vp[0] = __builtin_bit_cast(bf16x2, (uint32_t)vc[2 * m] | ((uint32_t)vc[2 * m + 1] << 16));
           }
         } else {
+          // codes of keys 2m (a) and 2m + 1 (b), interleaved by dim, then two
+          // codes per instruction to bf16 (exact)
           if constexpr (DPL == 2) {
-            const uint32_t w = (uint32_t)vc[2 * m] | ((uint32_t)vc[2 * m + 1] << 16);   // a0 a1 b0 b1
-            const uint32_t x = __builtin_amdgcn_perm(w, w, 0x03010200u);                  // a0 b0 a1 b1
-            const f32x2 lo = fp8x2_to_f32(x, false), hi = fp8x2_to_f32(x, true);
-            vp[0] = bf16x2{(bf16)lo[0], (bf16)lo[1]};   // exact conversions
-            vp[1] = bf16x2{(bf16)hi[0], (bf16)hi[1]};
+            const uint32_t x = __builtin_amdgcn_perm((uint32_t)vc[2 * m + 1], (uint32_t)vc[2 * m], 0x05010400u);  // a0 b0 a1 b1
+            vp[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+            vp[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
           } else {
-            const uint32_t w = (uint32_t)vc[2 * m] | ((uint32_t)vc[2 * m + 1] << 8);
-            const f32x2 lo = fp8x2_to_f32(w, false);
-            vp[0] = bf16x2{(bf16)lo[0], (bf16)lo[1]};
+            const uint32_t w = (uint32_t)vc[2 * m] | ((uint32_t)vc[2 * m + 1] << 8);   // a0 b0
+            vp[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
           }
         }
 #pragma unroll
@@ -384,7 +413,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) vc[j] = vn[j];
+      for (int j = 0; j < 16; ++j) {
+        vc[j] = vn[j];
+        if constexpr (AHEAD2) vn[j] = v2[j];
+      }
     }
   }
 
