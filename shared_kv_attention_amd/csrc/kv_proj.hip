@@ -118,25 +118,28 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
   const int HD = a.Hkv * a.d;
   const int F = 2 * HD;
   const int M = a.B * a.N;
-  // Workgroup -> (token tile, feature tile).  With the feature tiles split
-  // evenly over the 8 XCDs (workgroups are dealt to XCDs round-robin), each
-  // XCD keeps its slice of W in its own L2 while all XCDs stream the same
-  // token tiles of X at the same time (X is read from HBM about once).
+  // Workgroup -> (token tile, feature tile).  Workgroups are dealt to the 8
+  // XCDs round-robin; each XCD takes one block of a 2 x 4 partition of the
+  // (feature tile, token tile) grid -- half of the features, a quarter of
+  // the tokens -- so that X is fetched by 2 XCDs and W by 4 (dealing only the
+  // feature tiles made every XCD fetch all of X).  Workgroups of the padded
+  // partition that fall outside the grid have no work.
   const int nft = F / C::BM;
   const int ntt = (M + C::BN - 1) / C::BN;
   const int id = blockIdx.x;
   int tt, ft;
-  if (nft % 8 == 0) {
-    const int per = nft / 8, xcd = id & 7, sl = id >> 3;
-    ft = xcd * per + sl % per;
-    tt = sl / per;
+  if (nft % 2 == 0) {
+    const int xcd = id & 7, sl = id >> 3;
+    const int fpx = nft / 2, tpx = (ntt + 3) / 4;
+    ft = (xcd & 1) * fpx + sl % fpx;
+    tt = (xcd >> 1) * tpx + sl / fpx;
+    if (tt >= ntt) return;
   } else {
     ft = id % nft;
     tt = id / nft;
   }
   const int t0 = tt * C::BN;
   const int f0 = ft * C::BM;
-  (void)ntt;
 
   // staging: chunk slot P = 256 r + tid of a tile holds row P / 8 at physical
   // chunk P % 8 (logical chunk (P % 8) ^ swizzle(row)).  W goes global -> LDS
@@ -303,7 +306,10 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream) {
   const int F = 2 * a.Hkv * a.d;
   const int M = a.B * a.N;
-  dim3 grid((unsigned)(((long long)(M + 127) / 128) * (F / 128)));
+  const long long ntt = (M + 127) / 128, nft = F / 128;
+  // the 2 x 4 XCD partition pads the token tiles to a multiple of 4
+  const long long nwg = nft % 2 == 0 ? 8 * (nft / 2) * ((ntt + 3) / 4) : ntt * nft;
+  dim3 grid((unsigned)nwg);
   if (is_bf16)
     hipLaunchKernelGGL((kv_proj_kernel<bf16>), grid, dim3(256), 0, stream, a);
   else
