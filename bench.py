@@ -180,8 +180,104 @@ def cpu_baseline_prefill(step, budget_s):
     }
 
 
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
+def _time_until(fn, budget_s):
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            return (time.perf_counter() - t0) / reps, reps
+
+
+def cpu_baseline_decode(smp, budget_s):
+    """The oracle's decode (float64) on the sampled (sequence, KV head) groups
+    of one call, extrapolated to every group of the call and to the
+    workload's calls."""
+    import numpy as np
+
+    import oracle
+    groups = smp["groups"]
+
+    def one():
+        for i in range(len(groups)):
+            if smp["fp8"]:
+                k = oracle.dequantize_kv_fp8(smp["k"][i][None, None], np.array([smp["ks"][i]], dtype=np.float32))
+                v = oracle.dequantize_kv_fp8(smp["v"][i][None, None], np.array([smp["vs"][i]], dtype=np.float32))
+            else:
+                k, v = smp["k"][i][None, None], smp["v"][i][None, None]
+            oracle.decode_attention(smp["q"][i][None], k, v, [smp["ctx"]])
+
+    per_sample, reps = _time_until(one, budget_s)
+    per_call = per_sample / len(groups) * smp["B"] * smp["Hkv"]
+    return {
+        "workload": smp["workload"], "extrapolated": True,
+        "value": smp["bytes_per_call"] / per_call / 1e9, "unit": "GB/s",
+        "oracle_s_per_call": per_call, "oracle_s_workload": per_call * smp["calls"], "calls": smp["calls"],
+        "cores": _threads(), "kind": "oracle",
+        "sample": (f"{reps}x: {len(groups)} of {smp['B'] * smp['Hkv']} (sequence, KV head) groups of one call "
+                   f"({smp['g']} query heads x {smp['ctx']} keys each"
+                   + (", codes decoded to float64 first" if smp["fp8"] else "")
+                   + "), float64 numpy; extrapolated to the whole call and to every call"),
+    }
+
+
+def cpu_baseline_early_exit(smp, budget_s):
+    """The oracle on samples of the 1M-token early exit: window rows of one
+    layer, projection rows, and the last position's decode over one KV head
+    of the full cache -- each extrapolated to the whole flow."""
+    import numpy as np
+
+    import oracle
+    N, W, Ls, Lc, Hkv, d = smp["N"], smp["W"], smp["Ls"], smp["Lc"], smp["Hkv"], smp["d"]
+    rows = smp["rows"]
+
+    def swa_rows():
+        # each sampled row with its window of keys: the query sits at the
+        # window's last position and sees all of it (the window's allowed set)
+        for q, k, v in smp["swa"]:
+            oracle.cross_prefill_attention(q, k, v, n_kv=k.shape[2], q_offset=k.shape[2] - 1)
+
+    def proj_rows():
+        oracle.global_kv_proj(smp["x"], smp["wk"], smp["wv"], Hkv, d)
+
+    def decode_head():
+        oracle.decode_attention(smp["dec_q"], smp["dec_k"], smp["dec_v"], [N])
+
+    t_swa, r1 = _time_until(swa_rows, budget_s / 3)
+    t_proj, r2 = _time_until(proj_rows, budget_s / 3)
+    t_dec, r3 = _time_until(decode_head, budget_s / 3)
+    s_swa = t_swa / len(rows) * N * Ls
+    s_proj = t_proj / len(rows) * N
+    s_dec = t_dec * Hkv * Lc
+    total = s_swa + s_proj + s_dec
+    flops = (Ls * attn_flops(swa_pairs(N, W), Hkv * smp["g"], d, 1) + proj_flops(1, N, smp["x"].shape[-1], Hkv * d)
+             + Lc * attn_flops(N, Hkv * smp["g"], d, 1))
+    return {
+        "workload": smp["workload"], "extrapolated": True,
+        "value": flops / total / 1e12, "unit": "TFLOP/s",
+        "oracle_s_per_step": total,
+        "parts_s": {"swa": s_swa, "kv_proj": s_proj, "last_token_decode": s_dec},
+        "cores": _threads(), "kind": "oracle",
+        "sample": (f"window layer: {len(rows)} query rows x all heads ({r1}x), projection: {len(rows)} rows "
+                   f"({r2}x), decode of the last position over one KV head of the 2^20-row cache ({r3}x); "
+                   "float64 numpy; extrapolated to every row, layer and KV head"),
+    }
+
+
 # ---------------------------------------------------------------- decode
-def run_decode(wl, dev, steps):
+def run_decode(wl, dev, steps, sample=None, n_groups=2):
+    """Times the decode calls; with `sample` (a dict), also copies n_groups
+    (sequence, KV head) groups of the cache and one call's queries to the host
+    for the oracle timing."""
     B, ctx, Hq, Hkv, d, L = wl.batch, wl.seq, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.n_cross_layers
     wid = wl.wid
     fp8 = wl.dtype == "fp8-kv"
@@ -204,6 +300,17 @@ def run_decode(wl, dev, steps):
 
     def call(layer):
         yk.yoco_cross_attn_decode(qs[layer], kc, vc, ctx, k_scale=ks, v_scale=vs, o=o, workspace=ws)
+
+    if sample is not None:
+        g = Hq // Hkv
+        groups = [((7 * i) % B, (3 * i + 1) % Hkv) for i in range(n_groups)]
+        sample.update(workload=wl.name, groups=groups, g=g, B=B, Hkv=Hkv, ctx=ctx, d=d, fp8=fp8,
+                      calls=steps * L, bytes_per_call=decode_bytes(B, Hkv, ctx, d, Hq, kv_bytes, 2),
+                      q=[qs[0, b, kvh * g:(kvh + 1) * g].float().cpu().numpy() for b, kvh in groups],
+                      k=[kc[b, kvh].cpu().numpy() if fp8 else kc[b, kvh].float().cpu().numpy() for b, kvh in groups],
+                      v=[vc[b, kvh].cpu().numpy() if fp8 else vc[b, kvh].float().cpu().numpy() for b, kvh in groups],
+                      ks=None if not fp8 else [float(ks[kvh]) for _, kvh in groups],
+                      vs=None if not fp8 else [float(vs[kvh]) for _, kvh in groups])
 
     for layer in range(min(L, 4)):   # warm-up
         call(layer)
@@ -414,11 +521,15 @@ def run_gret(wl, dev, reps, decode_batch=16, chunk=256, tau=16.0, n_states=16):
                     "ms_per_layer": res["prefill"], "TFLOP/s": flops / (res["prefill"] * 1e-3) / 1e12,
                     "GB/s": pgbs,
                     "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": pgbs / HBM_PEAK_GBS, "traffic": None},
+                                 "frac": pgbs / HBM_PEAK_GBS,
+                                 "traffic": traffic_from_profile(f"gret_prefill_{wl.name}.txt", "gret.hip",
+                                                                 "hbm bytes per layer")},
                     "flops_per_layer": flops, "bytes_per_layer": pbytes},
         "decode": {"batch": Bd, "heads": H, "head_dim": d, "ms_per_step": res["decode"], "GB/s": dgbs,
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": dgbs / HBM_PEAK_GBS, "traffic": None},
+                                "frac": dgbs / HBM_PEAK_GBS,
+                                "traffic": traffic_from_profile(f"gret_decode_{wl.name}.txt", "gret.hip",
+                                                                "hbm bytes per step")},
                    "bytes_per_step": dbytes},
         "timing": "HIP events around one replay of a HIP graph of back-to-back calls (prefill: 3 kernels; decode: 1 kernel)",
     }
@@ -624,10 +735,14 @@ def run_shard(wl, dev, parts=8, reps=3):
 
 
 # ---------------------------------------------------------------- early exit
-def run_early_exit(wl, dev, steps):
+def run_early_exit(wl, dev, steps, sample=None):
     """1M-token early-exit prefill: L_s SWA layers over all tokens, the global
     KV projection of all tokens, then the cross-decoder for the last position
-    only (one decode call per cross layer over the full cache)."""
+    only (one decode call per cross layer over the full cache).  With
+    `sample` (a dict), copies to the host what the oracle timing needs:
+    sampled query rows of one window layer with their windows, sampled
+    projection rows with the weights, one KV head of the full cache and its
+    last-position queries."""
     B, N, D, Hq, Hkv, d, W = wl.batch, wl.seq, wl.hidden, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.window
     wid = wl.wid
     layers = []
@@ -672,6 +787,20 @@ def run_early_exit(wl, dev, steps):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    if sample is not None:
+        # window rows: the first rows (partial windows), both sides of the
+        # first full window, and spread over the sequence
+        rows = sorted({0, 1, W - 2, W - 1, W, W + 1, N // 2, N - 1} | {(N // 8) * i + 333 for i in range(8)})
+        q0, k0, v0 = layers[0]
+        g = Hq // Hkv
+        sample.update(workload=wl.name, N=N, W=W, Ls=wl.n_self_layers, Lc=wl.n_cross_layers, Hkv=Hkv, g=g, d=d,
+                      rows=rows,
+                      swa=[(q0[:, :, t:t + 1].float().cpu().numpy(),
+                            k0[:, :, max(0, t - W + 1):t + 1].float().cpu().numpy(),
+                            v0[:, :, max(0, t - W + 1):t + 1].float().cpu().numpy()) for t in rows],
+                      x=x[:, rows].float().cpu().numpy(), wk=wk.float().cpu().numpy(), wv=wv.float().cpu().numpy(),
+                      dec_q=ql[0][:, 0:g].float().cpu().numpy(), dec_k=kc[:, 0:1].float().cpu().numpy(),
+                      dec_v=vc[:, 0:1].float().cpu().numpy())
     swa_ms = sum(events_ms(ev["swa"])) / len(ev["swa"])
     proj_ms = sum(events_ms(ev["proj"])) / len(ev["proj"])
     dec_ms = sum(events_ms(ev["decode"])) / len(ev["decode"])
@@ -733,7 +862,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=128,
                     help="decode steps (x16 cross layers) of the 32K-context decode measurement")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU work")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle CPU work on the prefill sample (as much again on the other configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -746,6 +876,7 @@ def main():
     ap.add_argument("--extra-steps", type=int, default=3, help="steps of the 1M early-exit flow")
     ap.add_argument("--no-generation", action="store_true", help="skip the one-token generation step measurement")
     ap.add_argument("--no-gret", action="store_true", help="skip the gated-retention measurement")
+    ap.add_argument("--gret-reps", type=int, default=50, help="calls per timed HIP graph of the gated-retention layer")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the whole-block measurement (3B shape with all layer glue on the GPU)")
     args = ap.parse_args()
@@ -832,13 +963,17 @@ def main():
     del step
     torch.cuda.empty_cache()
 
+    smp_dec, smp_fp8, smp_ee = {}, {}, {}
+    want_cpu = not args.no_cpu_baseline
     if not args.no_decode:
-        out["decode"] = run_decode(WORKLOADS["decode_32k_bf16"], dev, args.decode_steps)
+        out["decode"] = run_decode(WORKLOADS["decode_32k_bf16"], dev, args.decode_steps,
+                                   sample=smp_dec if want_cpu else None)
         out["decode"]["roofline"]["measured_peak"] = peaks["hbm_read_GB/s"]
         out["decode"]["roofline"]["frac_of_measured_peak"] = out["decode"]["GB/s"] / peaks["hbm_read_GB/s"]
         torch.cuda.empty_cache()
     if not args.no_fp8_decode:
-        out["decode_fp8"] = run_decode(WORKLOADS["decode_512k_fp8"], dev, WORKLOADS["decode_512k_fp8"].decode_steps)
+        out["decode_fp8"] = run_decode(WORKLOADS["decode_512k_fp8"], dev, WORKLOADS["decode_512k_fp8"].decode_steps,
+                                       sample=smp_fp8 if want_cpu else None, n_groups=1)
         torch.cuda.empty_cache()
     if not args.no_generation:
         wg = WORKLOADS["generation_32k_bf16"]
@@ -848,18 +983,30 @@ def main():
         out["block_prefill"] = run_block(wl, dev, 3)
         torch.cuda.empty_cache()
     if not args.no_gret:
-        out["gated_retention"] = run_gret(WORKLOADS["gret_3b_bf16"], dev, 50)
+        out["gated_retention"] = run_gret(WORKLOADS["gret_3b_bf16"], dev, args.gret_reps)
         torch.cuda.empty_cache()
     if not args.no_early_exit:
-        out["early_exit_1m"] = run_early_exit(WORKLOADS["early_exit_1m_bf16"], dev, args.extra_steps)
+        out["early_exit_1m"] = run_early_exit(WORKLOADS["early_exit_1m_bf16"], dev, args.extra_steps,
+                                              sample=smp_ee if want_cpu else None)
         torch.cuda.empty_cache()
         out["early_exit_1m_one_of_8_devices"] = run_shard(WORKLOADS["early_exit_1m_bf16"], dev)
         torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
+    if want_cpu:
         step = PrefillStep(wl, dev)
         out["cpu_baseline"] = cpu_baseline_prefill(step, args.cpu_budget)
         del step
+        # the same oracle beside the other measured configurations (sampled,
+        # extrapolated), each on its own slice of the CPU budget
+        per = {}
+        budget = args.cpu_budget / 3
+        if smp_dec:
+            per["decode_32k_bf16"] = cpu_baseline_decode(smp_dec, budget)
+        if smp_fp8:
+            per["decode_512k_fp8"] = cpu_baseline_decode(smp_fp8, budget)
+        if smp_ee:
+            per["early_exit_1m_bf16"] = cpu_baseline_early_exit(smp_ee, budget)
+        out["cpu_baseline"]["per_config"] = per
     else:
         out["cpu_baseline"] = None
 
