@@ -121,15 +121,17 @@ class PrefillStep:
         for (q, k, v), o in zip(self.swa, self.o_swa):
             yk.yoco_swa_attn(q, k, v, wl.window, o=o)
         yk.yoco_global_kv_proj(self.x, self.wk, self.wv, self.kc, self.vc)
+        # the cross layers run back to back; one event pair around all of
+        # them (an event between two launches opens a gap of several
+        # microseconds in the stream), so a launch's duration is the span / L
+        if ev is not None:
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
         for q, o in zip(self.cross_q, self.o_cross):
-            if ev is not None:
-                s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                s.record()
-                yk.yoco_cross_attn_prefill(q, self.kc, self.vc, o=o)
-                e.record()
-                ev.append((s, e))
-            else:
-                yk.yoco_cross_attn_prefill(q, self.kc, self.vc, o=o)
+            yk.yoco_cross_attn_prefill(q, self.kc, self.vc, o=o)
+        if ev is not None:
+            e.record()
+            ev.append((s, e))
 
 
 def cpu_baseline_prefill(step, budget_s):
@@ -319,22 +321,24 @@ def run_decode(wl, dev, steps, sample=None, n_groups=2):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
+    # one event pair per step around its L back-to-back calls (an event
+    # between two launches opens a gap of several microseconds)
     for _ in range(steps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
         for layer in range(L):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
             call(layer)
-            e.record()
-            ev.append((s, e))
+        e.record()
+        ev.append((s, e))
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    per_call = sum(events_ms(ev)) / len(ev)
+    per_call = sum(events_ms(ev)) / (len(ev) * L)
     nbytes = decode_bytes(B, Hkv, ctx, d, Hq, kv_bytes, 2)
     gbs = nbytes / (per_call * 1e-3) / 1e9
     return {
         "workload": wl.name,
-        "calls": len(ev),
+        "calls": len(ev) * L,
         "ms_per_call": per_call,
         "total_ms": total_ms,
         "bytes_per_call": nbytes,
@@ -344,7 +348,7 @@ def run_decode(wl, dev, steps, sample=None, n_groups=2):
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": traffic_from_profile(f"decode_split_{wl.name}.txt", "decode.hip",
                                                      "hbm bytes per launch")},
-        "timing": "HIP events around each call (split kernel + combine kernel)",
+        "timing": "HIP events around each step's back-to-back calls (split kernel + combine kernel per call); per call = span / calls",
     }
 
 
@@ -918,7 +922,7 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
     tflops = step.flops / (ms * 1e-3) / 1e12
 
-    attn_ms = sum(events_ms(ev)) / len(ev)
+    attn_ms = sum(events_ms(ev)) / (len(ev) * wl.n_cross_layers)
     attn_tflops = step.flops_cross / (attn_ms * 1e-3) / 1e12
     roofline = {
         "bound": "mfma",
@@ -930,6 +934,7 @@ def main():
         "traffic": traffic_from_profile("attn_fwd_prefill_3b_bf16.txt", "attn_fwd.hip", "hbm bytes per launch"),
         "flops_per_launch": step.flops_cross,
         "ms_per_launch": attn_ms,
+        "timing": "HIP events around the back-to-back cross-layer launches of every timed step; per launch = span / layers",
     }
 
     peaks = run_peaks(dev)

@@ -17,6 +17,12 @@ CASES = [
     (2, 300, 256, 2, 128, 320, 5, False, "bf16", 0.06),
     (1, 129, 512, 8, 128, 200, 71, True, "bf16", 0.04),
     (3, 77, 192, 3, 64, 100, 0, True, "f32", 0.07),
+    # bf16 with 16 feature tiles and >= 16 tiles of 256 tokens: the 256-token
+    # form; a ragged last token tile, an odd number of k stages (5 and 3), a
+    # token tile across the batch boundary (weights scaled so that outputs stay
+    # O(1): the absolute bound assumes bf16 output ulps of at most 2^-6)
+    (1, 4100, 320, 8, 128, 4200, 37, True, "bf16", 0.03),
+    (2, 2100, 192, 8, 128, 2100, 0, False, "bf16", 0.04),
 ]
 
 
