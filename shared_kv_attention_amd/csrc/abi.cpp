@@ -39,14 +39,16 @@ struct DecodeLayout {
 
 // The workspace holds the partials of the plan for kDecodeMaxWorkgroups
 // (what the size queries return, whatever the dtype).  A bf16 d = 128 cache
-// whose splits are long enough is read by the whole-line K form, planned for
-// that form's own workgroup target (never more splits).
+// whose splits are long enough is read by the whole-line K form, and an fp8
+// d = 128 cache with splits that long by the 8-bit form; both are planned for
+// their own workgroup target (never more splits).
 DecodeLayout decode_layout(int B, int Hq, int Hkv, int ctx, int d, int kv_kind = 1) {
   DecodeLayout L{};
   yoco::decode_plan(B, Hq, Hkv, ctx, yoco::kDecodeMaxWorkgroups, &L.n_splits, &L.chunk, &L.n_hg);
   const int cap_splits = L.n_splits;
-  L.full_lines = kv_kind == 1 && d == 128 && L.chunk >= yoco::kDecodeFullLineMinChunk;
-  if (L.full_lines)
+  const bool long_splits = d == 128 && L.chunk >= yoco::kDecodeFullLineMinChunk;
+  L.full_lines = kv_kind == 1 && long_splits;
+  if (long_splits && (kv_kind == 1 || kv_kind == 2))
     yoco::decode_plan(B, Hq, Hkv, ctx, yoco::decode_workgroup_target(kv_kind, d), &L.n_splits, &L.chunk, &L.n_hg);
   const size_t rows = (size_t)B * Hq * cap_splits;
   L.o_bytes = align16(rows * d * sizeof(float));

@@ -175,7 +175,8 @@ constexpr int kDecodeMaxSplits = 4096;
 // 0 float32, 1 bf16, 2 fp8).
 constexpr int kDecodeMaxWorkgroups = 4096;
 // bf16 d = 128 splits of at least this many keys use the whole-line K form
-// (three blocks in flight, 3 waves per SIMD) and its own workgroup target.
+// (three blocks in flight, 3 waves per SIMD) and its own workgroup target;
+// fp8 d = 128 splits that long are planned for 3 waves per SIMD as well.
 constexpr int kDecodeFullLineMinChunk = 1024;
 int decode_workgroup_target(int kv_kind, int d);
 void decode_plan(int B, int Hq, int Hkv, int ctx, int target, int* n_splits, int* chunk, int* n_hg);

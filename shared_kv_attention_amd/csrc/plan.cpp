@@ -19,8 +19,12 @@ int decode_split_bound(int B, int Hq, int Hkv, int ctx) {
 }
 
 // One resident round of the whole-line K form (bf16, d = 128): three K
-// blocks in flight take 152 VGPRs, 3 waves per SIMD, 12 per CU.
-int decode_workgroup_target(int kv_kind, int d) { return kv_kind == 1 && d == 128 ? 256 * 12 : kDecodeMaxWorkgroups; }
+// blocks in flight take 152 VGPRs, 3 waves per SIMD, 12 per CU.  The fp8
+// d = 128 form (116 VGPRs) could hold 4 waves per SIMD, but with long splits
+// 3 per SIMD stream faster (512K-key x 8 decode: 6.30 against 6.16 TB/s).
+int decode_workgroup_target(int kv_kind, int d) {
+  return (kv_kind == 1 || kv_kind == 2) && d == 128 ? 256 * 12 : kDecodeMaxWorkgroups;
+}
 
 // Split-K plan of the decode kernel: about `target` one-wave workgroups (one
 // resident round on the 256 CUs), at least 64 keys per split, the chunk a

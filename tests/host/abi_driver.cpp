@@ -195,13 +195,15 @@ int main() {
     std::free(ws);
   }
   {
-    // long bf16 d = 128 splits take the whole-line K form (12-wave-per-CU plan);
-    // short splits, fp8 and float32 caches do not
-    struct Case { int B, Hq, Hkv, ctx, d; yoco_dtype kv; int full; };
-    const Case cases[] = {{16, 32, 8, 32768, 128, YOCO_BF16, 1}, {1, 24, 8, 1 << 20, 128, YOCO_BF16, 1},
-                          {32, 32, 8, 16384, 128, YOCO_BF16, 1}, {1, 24, 8, 131072, 128, YOCO_BF16, 0},
-                          {16, 32, 8, 32768, 64, YOCO_BF16, 0}, {16, 32, 8, 32768, 128, YOCO_FP8_E4M3, 0},
-                          {16, 32, 8, 32768, 128, YOCO_F32, 0}};
+    // long bf16 d = 128 splits take the whole-line K form (12-wave-per-CU
+    // plan); short splits, fp8 and float32 caches do not.  Long fp8 d = 128
+    // splits get the 12-wave-per-CU plan too.
+    struct Case { int B, Hq, Hkv, ctx, d; yoco_dtype kv; int full, twelve; };
+    const Case cases[] = {{16, 32, 8, 32768, 128, YOCO_BF16, 1, 1}, {1, 24, 8, 1 << 20, 128, YOCO_BF16, 1, 1},
+                          {32, 32, 8, 16384, 128, YOCO_BF16, 1, 1}, {1, 24, 8, 131072, 128, YOCO_BF16, 0, 0},
+                          {16, 32, 8, 32768, 64, YOCO_BF16, 0, 0}, {16, 32, 8, 32768, 128, YOCO_FP8_E4M3, 0, 1},
+                          {8, 32, 8, 1 << 19, 128, YOCO_FP8_E4M3, 0, 1}, {1, 24, 8, 131072, 128, YOCO_FP8_E4M3, 0, 0},
+                          {16, 32, 8, 32768, 128, YOCO_F32, 0, 0}};
     for (const Case& c : cases) {
       const size_t need = yoco_cross_attn_decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.ctx, c.d);
       unsigned char* ws = (unsigned char*)std::malloc(need);
@@ -210,7 +212,9 @@ int main() {
                                    c.d, 0.f, qd, c.kv, ws, need, nullptr) == YOCO_OK);
       const yoco::DecodeArgs& a = yoco::g_decode;
       CHECK(a.full_lines == c.full);
-      if (c.full) CHECK(a.chunk >= yoco::kDecodeFullLineMinChunk && (long long)a.n_splits * c.B * c.Hkv <= 256 * 12);
+      const long long wgs = (long long)a.n_splits * c.B * c.Hkv * a.n_hg;
+      if (c.twelve) CHECK(a.chunk >= yoco::kDecodeFullLineMinChunk && wgs <= 256 * 12 && wgs > 256 * 8);
+      else CHECK(wgs > 256 * 12 || a.chunk < yoco::kDecodeFullLineMinChunk || c.d != 128);
       CHECK((unsigned char*)(a.part_l + (size_t)c.B * c.Hq * a.n_splits) <= ws + need);
       std::free(ws);
     }
