@@ -91,10 +91,7 @@ __device__ __forceinline__ void pipe_sched_steps() {
 
 // Key tiles [lo, hi] that query tile qt (bq rows) needs.
 __device__ __forceinline__ void key_span(const AttnArgs& a, bool swa, int bq, int bk, int qt, int& lo, int& hi) {
-  const int q_first = qt * bq, q_last = min(q_first + bq, a.Nq) - 1;
-  const int P0 = a.q_offset + q_first, P1 = a.q_offset + q_last;
-  lo = swa ? max(0, P0 - a.window + 1) / bk : 0;
-  hi = min(P1, a.n_kv - 1) / bk;
+  attn_key_span(a.Nq, a.n_kv, a.q_offset, a.window, swa, bq, bk, qt, lo, hi);
 }
 
 // One wave's 32 query rows of one (batch, head): Q operands, running
@@ -329,9 +326,8 @@ struct TileStager {
 #pragma unroll
     for (int r = 0; r < C::PER_T; ++r) {
       const int slot = C::NT * r + wslot + l;
-      const int row = slot / C::CH, pch = slot % C::CH;
-      koff[r] = (unsigned)(row * ROWB + ((pch ^ swz_k<C::CH>(row)) << 4));
-      voff[r] = (unsigned)(row * ROWB + ((pch ^ swz_v<C::CH>(row)) << 4));
+      koff[r] = stage_offset<C::CH, true>(slot, ROWB);
+      voff[r] = stage_offset<C::CH, false>(slot, ROWB);
     }
   }
   // Every buffer starts zeroed, so a slot that an out-of-range load leaves
@@ -352,7 +348,7 @@ struct TileStager {
     // bytes of rows < n_kv (uniform; read back as a scalar so the resource
     // stays in SGPRs).  The row count is clamped to one tile before it is
     // scaled to bytes, so the product stays small for any cache length.
-    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(C::BK, n_kv - t * C::BK)) * ROWB);
+    const int valid = __builtin_amdgcn_readfirstlane(tile_valid_bytes(n_kv, t, C::BK, ROWB));
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tb), (short)0, valid, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tb), (short)0, valid, kBufferFlags);
 #pragma unroll
@@ -388,15 +384,12 @@ __global__ __launch_bounds__((AttnCfg<T, D, SWA>::NT), (AttnCfg<T, D, SWA>::MIN_
   const int l = tid & 63;
 
   // ---- workgroup -> (batch, head, query tile) ----
-  const int BH = a.B * a.Hq;
-  const int nqt = (a.Nq + C::BQ - 1) / C::BQ;
-  const int id = blockIdx.x;
   // causal: heaviest (latest) query tiles first; sliding window: all tiles
-  // cost the same, and the natural order lets neighbouring windows share L2
-  const int qt = SWA ? id / BH : nqt - 1 - id / BH;
-  int j = id % BH;
-  if ((BH & 7) == 0) j = (j & 7) * (BH >> 3) + (j >> 3);   // same KV head -> same XCD
-  const int b = j / a.Hq, h = j % a.Hq;
+  // cost the same, and the natural order lets neighbouring windows share L2;
+  // the heads of one KV head on one XCD
+  const int nqt = (a.Nq + C::BQ - 1) / C::BQ;
+  const AttnTile tile = attn_tile(blockIdx.x, a.B, a.Hq, nqt, SWA);
+  const int qt = tile.qt, b = tile.b, h = tile.h;
   const int kvh = h / (a.Hq / a.Hkv);
 
   const T* qbase = static_cast<const T*>(a.q) + ((size_t)(b * a.Hq + h) * a.Nq) * D;

@@ -46,6 +46,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "index_map.hpp"
 
 namespace yoco {
 
@@ -177,9 +178,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int nh = min(4, grp - 4 * hg);
 
   const int ctx_b = decode_ctx(a, b);
-  const int key_begin = split * a.chunk;
+  const int key_begin = decode_key_begin(split, a.chunk);
   if (key_begin >= ctx_b) return;
-  const int key_end = min(key_begin + a.chunk, ctx_b);
+  const int key_end = decode_key_end(split, a.chunk, ctx_b);
 
   // Query operand: row r -> head (r & 3) of this group (zero beyond nh).
   frag qa[NC];
@@ -207,11 +208,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const char* vh = uniform_ptr(static_cast<const char*>(a.v) + head_off * RB);
   const int kend = __builtin_amdgcn_readfirstlane(key_end);
   auto block_rsrc = [&](const char* hb, int key0) {
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(16, kend - key0)));
+    const int rows = __builtin_amdgcn_readfirstlane(decode_block_rows(kend, key0));
     return __builtin_amdgcn_make_buffer_rsrc((void*)(hb + (size_t)key0 * RB), (short)0, rows * RB, kBufferFlags);
   };
-  const int koff = r16 * RB + 8 * G * (int)sizeof(KVT);   // K, operand layout: key r16, elements 8G ..
-  const int voff = DPL * l * (int)sizeof(KVT);            // V: this lane's dims
+  const int koff = decode_k_offset(l, RB, (int)sizeof(KVT));     // K, operand layout: key r16, elements 8G ..
+  const int voff = decode_v_offset(l, DPL, (int)sizeof(KVT));    // V: this lane's dims
 
   float m_run[4], l_run[4];
   float acc[4][DPL];
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   // two halves of line L into the fragments of steps 2L and 2L + 1 (lane
   // (G, k): key k, elements 32c + 8G .. +7).  Three blocks in flight.
   constexpr int NL = D / 64;
-  const int kfoff = (r16 & 7) * RB + (32 * (r16 >> 3) + 8 * G) * (int)sizeof(KVT);
+  const int kfoff = decode_kf_offset(l, RB, (int)sizeof(KVT));
   auto load_kf = [&](int key0, u32x4 (&raw)[NL][2]) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(kh, key0);
 #pragma unroll

@@ -22,6 +22,7 @@
 //    float32), LDS double buffering with XOR-swizzled 16-byte chunks.
 #include "common.hpp"
 #include "launch.hpp"
+#include "index_map.hpp"
 
 namespace yoco {
 
@@ -37,10 +38,7 @@ struct ProjCfg {
   static constexpr int TILE_BYTES = 128 * 128;
 };
 
-// XOR swizzle of the 16-byte chunk index within a 128-byte tile row: the 32
-// rows a wave reads at once spread over all banks whether the LDS serves 8
-// or 16 lanes of 16-byte accesses per cycle.
-__device__ __forceinline__ int swz8(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+// (swz8, the XOR swizzle of 128-byte tile rows, is defined in index_map.hpp)
 
 template <typename T>
 __device__ __forceinline__ typename Elem<T>::frag lds_frag_row(const char* tile, int row, int kc, int g) {
@@ -126,18 +124,8 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
   // partition that fall outside the grid have no work.
   const int nft = F / C::BM;
   const int ntt = (M + C::BN - 1) / C::BN;
-  const int id = blockIdx.x;
   int tt, ft;
-  if (nft % 2 == 0) {
-    const int xcd = id & 7, sl = id >> 3;
-    const int fpx = nft / 2, tpx = (ntt + 3) / 4;
-    ft = (xcd & 1) * fpx + sl % fpx;
-    tt = (xcd >> 1) * tpx + sl / fpx;
-    if (tt >= ntt) return;
-  } else {
-    ft = id % nft;
-    tt = id / nft;
-  }
+  if (!proj_tile(blockIdx.x, nft, ntt, ft, tt)) return;
   const int t0 = tt * C::BN;
   const int f0 = ft * C::BM;
 
@@ -308,7 +296,7 @@ hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream) {
   const int M = a.B * a.N;
   const long long ntt = (M + 127) / 128, nft = F / 128;
   // the 2 x 4 XCD partition pads the token tiles to a multiple of 4
-  const long long nwg = nft % 2 == 0 ? 8 * (nft / 2) * ((ntt + 3) / 4) : ntt * nft;
+  const long long nwg = proj_workgroups((int)nft, (int)ntt);
   dim3 grid((unsigned)nwg);
   if (is_bf16)
     hipLaunchKernelGGL((kv_proj_kernel<bf16>), grid, dim3(256), 0, stream, a);
