@@ -435,12 +435,6 @@ yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new,
   const DecodeLayout L = decode_layout(B, Hq, Hkv, ctx, d, dtype == YOCO_F32 ? 0 : 1);
   if (!workspace || workspace_bytes < L.total) return YOCO_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return YOCO_ERR_ALIGN;
-  const int esz = dtype == YOCO_F32 ? 4 : 2;
-  if (k_new) {
-    yoco::RingAppendArgs r{k_new, v_new, k_ring, v_ring, B, Hkv, W, pos % W, d * esz};
-    const yoco_status st = launched(yoco::launch_ring_append(r, as_stream(stream)));
-    if (st != YOCO_OK) return st;
-  }
   char* ws = static_cast<char*>(workspace);
   yoco::DecodeArgs a{};
   a.q = q;
@@ -462,6 +456,10 @@ yoco_status yoco_swa_decode(const void* q, const void* k_new, const void* v_new,
   a.n_hg = L.n_hg;
   a.full_lines = L.full_lines;
   a.scale_log2 = resolve_scale(softmax_scale, d) * 1.4426950408889634f;
+  // the token's K/V go into slot pos % W inside the decode launch
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_slot = pos % W;
   const int kind = dtype == YOCO_F32 ? 0 : 1;
   return launched(yoco::launch_decode(a, kind, kind, d, as_stream(stream)));
 }

@@ -77,6 +77,21 @@ __device__ __forceinline__ Raw8<KVT> buf_raw8(__amdgpu_buffer_rsrc_t r, int off)
   return x;
 }
 
+// The same 8 elements from a plain pointer.
+template <typename KVT>
+__device__ __forceinline__ Raw8<KVT> raw8_at(const char* p) {
+  Raw8<KVT> x;
+  if constexpr (sizeof(KVT) == 2) {
+    x.w = *reinterpret_cast<const u32x4*>(p);
+  } else if constexpr (sizeof(KVT) == 4) {
+    x.lo = *reinterpret_cast<const u32x4*>(p);
+    x.hi = *reinterpret_cast<const u32x4*>(p + 16);
+  } else {
+    x.w = *reinterpret_cast<const u32x2*>(p);
+  }
+  return x;
+}
+
 // Cache-policy bits of a buffer load: streaming (non-temporal).
 constexpr int kLoadNT = 2;
 
@@ -160,7 +175,7 @@ __device__ __forceinline__ int decode_ctx(const DecodeArgs& a, int b) {
   return min(max((int)a.ctx_lens[b], 1), a.ctx);
 }
 
-template <typename QT, typename KVT, int D, bool KF>
+template <typename QT, typename KVT, int D, bool KF, bool RING = false>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using MT = typename KvTraits<KVT>::mma_t;
   static_assert(sizeof(MT) == sizeof(QT), "query dtype must match the matrix-core dtype");
@@ -213,6 +228,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   };
   const int koff = decode_k_offset(l, RB, (int)sizeof(KVT));     // K, operand layout: key r16, elements 8G ..
   const int voff = decode_v_offset(l, DPL, (int)sizeof(KVT));    // V: this lane's dims
+
+  // The current token of a ring cache (the append folded in): its row lies
+  // in this split's range for one split only; that split reads it from
+  // k_new / v_new (below), and its first head group writes it into the
+  // ring.  No other workgroup of this launch reads that ring row.
+  const int ns = RING ? a.new_slot : -1;
+  const bool patch = RING && ns >= key_begin && ns < key_end;
+  const char* knew_row = static_cast<const char*>(a.k_new) + (size_t)(b * a.Hkv + kvh) * RB;
+  const char* vnew_row = static_cast<const char*>(a.v_new) + (size_t)(b * a.Hkv + kvh) * RB;
+  if (RING && patch && hg == 0) {
+    char* kd = const_cast<char*>(kh) + (size_t)ns * RB;
+    char* vd = const_cast<char*>(vh) + (size_t)ns * RB;
+    for (int i = l; i < RB / 4; i += 64) {
+      reinterpret_cast<uint32_t*>(kd)[i] = reinterpret_cast<const uint32_t*>(knew_row)[i];
+      reinterpret_cast<uint32_t*>(vd)[i] = reinterpret_cast<const uint32_t*>(vnew_row)[i];
+    }
+  }
 
   float m_run[4], l_run[4];
   float acc[4][DPL];
@@ -306,6 +338,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if constexpr (KFULL) {
       if (key0 + 48 < key_end) load_kf(key0 + 48, kf3);
       kf_frags(kf0, kc);
+    }
+
+    if (RING && patch && key0 <= ns && ns < key0 + 16) {
+      // the current token's row: K for the lanes of its key, V for every lane
+      const int rel = ns - key0;
+      if (r16 == rel) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kc[c] = raw8_at<KVT>(knew_row + (32 * c + 8 * G) * (int)sizeof(KVT));
+      }
+      const vword nv = *reinterpret_cast<const vword*>(vnew_row + voff);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) vc[j] = j == rel ? nv : vc[j];
     }
 
     // scores: lane (G, r16) receives head i's score of key key0 + r16 in s[i]
@@ -510,10 +554,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 template <typename QT, typename KVT, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.n_splits, a.Hkv * a.n_hg, a.B);
+  // ring caches with a token to append take the RING instantiations (the
+  // plain decode kernels carry none of that code)
+  const bool ring = sizeof(KVT) != 1 && a.k_new != nullptr;
   bool launched = false;
   if constexpr (sizeof(KVT) == 2 && D == 128) {
     if (a.full_lines) {
-      hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D, true>), grid, dim3(64), 0, stream, a);
+      if (ring) hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D, true, true>), grid, dim3(64), 0, stream, a);
+      else hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D, true>), grid, dim3(64), 0, stream, a);
+      launched = true;
+    }
+  }
+  if constexpr (sizeof(KVT) != 1) {
+    if (!launched && ring) {
+      hipLaunchKernelGGL((decode_split_kernel<QT, KVT, D, false, true>), grid, dim3(64), 0, stream, a);
       launched = true;
     }
   }
@@ -522,21 +576,6 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<QT, D>), dim3(a.Hq, a.B, D / 32), dim3(256), 0, stream, a);
   return hipGetLastError();
-}
-
-// Writes the current token's K and V rows into ring slot `slot` of every
-// (sequence, KV head): one workgroup per (sequence, KV head), 4-byte words.
-__global__ __launch_bounds__(64) void ring_append_kernel(RingAppendArgs a) {
-  const int bh = blockIdx.x;
-  const int words = a.row_bytes / 4;
-  const uint32_t* ks = static_cast<const uint32_t*>(a.k_new) + (size_t)bh * words;
-  const uint32_t* vs = static_cast<const uint32_t*>(a.v_new) + (size_t)bh * words;
-  uint32_t* kd = static_cast<uint32_t*>(a.k_ring) + ((size_t)bh * a.W + a.slot) * words;
-  uint32_t* vd = static_cast<uint32_t*>(a.v_ring) + ((size_t)bh * a.W + a.slot) * words;
-  for (int i = threadIdx.x; i < words; i += 64) {
-    kd[i] = ks[i];
-    vd[i] = vs[i];
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -563,11 +602,6 @@ __global__ void attn_merge_kernel(MergeArgs a) {
 hipError_t launch_attn_merge(const MergeArgs& a, bool is_bf16, hipStream_t stream) {
   if (is_bf16) hipLaunchKernelGGL(attn_merge_kernel<bf16>, dim3((unsigned)a.rows), dim3(a.d), 0, stream, a);
   else hipLaunchKernelGGL(attn_merge_kernel<float>, dim3((unsigned)a.rows), dim3(a.d), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(ring_append_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

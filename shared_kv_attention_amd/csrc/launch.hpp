@@ -40,6 +40,12 @@ struct DecodeArgs {
   int n_splits, chunk, n_hg;
   float scale_log2;
   int full_lines;          // bf16 K read in whole lines, three blocks ahead (long splits)
+  // Ring append folded into the decode (self-decoder window): when k_new is
+  // set, key row new_slot of every (sequence, KV head) is read from
+  // k_new / v_new [B, Hkv, d] instead of k / v, and written into k / v
+  const void* k_new;
+  const void* v_new;
+  int new_slot;
 };
 
 struct ProjArgs {
@@ -90,15 +96,6 @@ struct MergeArgs {
   void* o;                 // [rows, d]
   float* lse;              // [rows] or null
   int S, rows, d;
-};
-
-struct RingAppendArgs {
-  const void* k_new;   // [B, Hkv, d]
-  const void* v_new;
-  void* k_ring;        // [B, Hkv, W, d]
-  void* v_ring;
-  int B, Hkv, W, slot;
-  int row_bytes;       // d * element size (a multiple of 4)
 };
 
 struct GretArgs {
@@ -158,7 +155,6 @@ hipError_t launch_quant_fp8(const QuantArgs& a, bool is_bf16, hipStream_t stream
 hipError_t launch_quant_clear(uint32_t* amax_bits, int n, hipStream_t stream);
 hipError_t launch_quant_amax(const QuantArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_quant_encode(const QuantArgs& a, bool is_bf16, hipStream_t stream);
-hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t stream);
 hipError_t launch_attn_merge(const MergeArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_peak_read(const void* src, long long bytes, uint32_t* partial, int blocks, hipStream_t stream);
 hipError_t launch_peak_mfma(int iters, float* out, int blocks, hipStream_t stream);

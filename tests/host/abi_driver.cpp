@@ -17,7 +17,6 @@ extern AttnArgs g_attn;
 extern DecodeArgs g_decode;
 extern ProjArgs g_proj;
 extern QuantArgs g_quant;
-extern RingAppendArgs g_ring;
 extern GretArgs g_gret;
 extern LinArgs g_lin;
 extern MergeArgs g_merge;
@@ -232,7 +231,7 @@ int main() {
     CHECK(yoco::g_launches == n + 1);
   }
 
-  // ---- self-decoder ring decode: append + decode, workspace bound over all positions
+  // ---- self-decoder ring decode: one launch (the append folded into the decode), workspace bound over all positions
   {
     const int B = 3, Hq = 8, Hkv = 2, W = 1024, d = 128;
     const size_t need = yoco_swa_decode_workspace_bytes(B, Hq, Hkv, W, d);
@@ -241,9 +240,9 @@ int main() {
     for (int pos : {0, 1, 255, 256, 1022, 1023, 1024, 5000, 1 << 20}) {
       n = yoco::g_launches;
       CHECK(yoco_swa_decode(P, P, P, P, P, pos, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_BF16, ws, need, nullptr) == YOCO_OK);
-      CHECK(yoco::g_launches == n + 2);
-      CHECK(yoco::g_ring.slot == pos % W && yoco::g_ring.row_bytes == d * 2 && yoco::g_ring.W == W);
+      CHECK(yoco::g_launches == n + 1);
       const yoco::DecodeArgs& a = yoco::g_decode;
+      CHECK(a.k_new == P && a.v_new == P && a.new_slot == pos % W && a.new_slot < a.ctx);
       CHECK(a.ctx == (pos + 1 < W ? pos + 1 : W) && a.n_cap == W && a.ctx_lens == nullptr);
       const size_t rows = (size_t)B * Hq * a.n_splits;
       CHECK((unsigned char*)(a.part_l + rows) <= ws + need);
@@ -251,7 +250,7 @@ int main() {
     }
     n = yoco::g_launches;
     CHECK(yoco_swa_decode(P, nullptr, nullptr, P, P, 7, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_OK);
-    CHECK(yoco::g_launches == n + 1);   // no append without new K/V
+    CHECK(yoco::g_launches == n + 1 && yoco::g_decode.k_new == nullptr);   // no append without new K/V
     CHECK(yoco_swa_decode(P, P, nullptr, P, P, 7, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_ERR_NULL);
     CHECK(yoco_swa_decode(P, P, P, P, P, -1, P, nullptr, B, Hq, Hkv, W, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_ERR_SHAPE);
     CHECK(yoco_swa_decode(P, P, P, P, P, 7, P, nullptr, B, Hq, Hkv, 0, d, 0.f, YOCO_F32, ws, need, nullptr) == YOCO_ERR_SHAPE);

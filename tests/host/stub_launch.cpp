@@ -10,7 +10,6 @@ AttnArgs g_attn;
 DecodeArgs g_decode;
 ProjArgs g_proj;
 QuantArgs g_quant;
-RingAppendArgs g_ring;
 GretArgs g_gret;
 GretDecodeArgs g_gret_dec;
 GretNormArgs g_gret_norm;
@@ -37,7 +36,6 @@ hipError_t launch_quant_amax(const QuantArgs&, bool, hipStream_t) { ++g_launches
 hipError_t launch_quant_encode(const QuantArgs& a, bool, hipStream_t) {
   ++g_launches; g_encode[g_encodes++ & 1] = a; return hipSuccess;
 }
-hipError_t launch_ring_append(const RingAppendArgs& a, hipStream_t) { ++g_launches; g_ring = a; return hipSuccess; }
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t) { ++g_launches; g_gret = a; return hipSuccess; }
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool, hipStream_t) { ++g_launches; g_gret_dec = a; return hipSuccess; }
 hipError_t launch_gret_norm(const GretNormArgs& a, bool, hipStream_t) { ++g_launches; g_gret_norm = a; return hipSuccess; }

@@ -59,6 +59,32 @@ def test_swa_decode_matches_oracle(dt, d, W, pos):
     assert np.abs(to64(lse) - ref_lse).max() <= tol
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,W,pos,rows", [
+    (2, 16, 2, 512, 700, None),          # 8 query heads per KV head: two head groups share each split
+    (64, 8, 8, 8192, 10000, [0, 37, 63]),  # long splits: the whole-line K form (sampled sequences checked)
+])
+def test_swa_decode_append_with_head_groups_and_long_splits(B, Hq, Hkv, W, pos, rows):
+    """The append folded into the decode: the split holding slot pos mod W
+    reads the token from k_new / v_new in every head group and in the
+    whole-line K form; the ring ends up holding it."""
+    d = 128
+    print(f"swa_decode append B={B} Hq={Hq} Hkv={Hkv} W={W} pos={pos}", flush=True)
+    q = randn((B, Hq, d), 7401 + B, device=DEV)
+    kr = randn((B, Hkv, W, d), 7402 + B, device=DEV)
+    vr = randn((B, Hkv, W, d), 7403 + B, device=DEV)
+    kn = randn((B, Hkv, d), 7404 + B, device=DEV)
+    vn = randn((B, Hkv, d), 7405 + B, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV)
+    o = yk.yoco_swa_decode(q, kr, vr, pos, k_new=kn, v_new=vn, lse=lse)
+    torch.cuda.synchronize()
+    s = pos % W
+    assert torch.equal(kr[:, :, s], kn) and torch.equal(vr[:, :, s], vn)
+    rows = list(range(B)) if rows is None else rows
+    ref_o, ref_lse = oracle.swa_ring_decode_attention(to64(q[rows]), to64(kr[rows]), to64(vr[rows]), pos)
+    check(to64(o[rows]), ref_o, "bf16", "swa_decode with append", rel_axes=(2,))
+    assert np.abs(to64(lse[rows]) - ref_lse).max() <= 1e-3
+
+
 def test_swa_decode_without_append_leaves_ring_untouched():
     B, Hq, Hkv, W, d = 1, 4, 1, 128, 64
     q = randn((B, Hq, d), 7101, device=DEV)
