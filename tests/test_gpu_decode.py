@@ -27,6 +27,11 @@ DECODE_CASES = [
     # splits of 1024 keys: the whole-line K form, with ragged lengths (rows past
     # each length hold NaN and must never be read)
     (32, 32, 8, 16384, 16384, [16384, 1, 16383, 1024, 1025, 2047, 5000, 16000] * 4, 128, "bf16"),
+    # 64-key splits over many (sequence, KV head) pairs with ragged lengths that
+    # leave some splits empty; two head groups at head dim 64; 256-key splits
+    (16, 32, 8, 1024, 1024, [1024, 1, 63, 64, 65, 1000, 512, 1023] * 2, 128, "bf16"),
+    (8, 64, 8, 300, 300, None, 64, "bf16"),
+    (64, 32, 8, 2048, 2048, None, 128, "bf16"),
 ]
 
 
@@ -100,6 +105,8 @@ def test_quantize_fp8_bit_exact(src):
     (3, 4, 4, 2500, [2500, 1, 1999], 64),        # 1 query head per KV head
     (2, 6, 2, 4100, [4100, 4099], 128),          # 3 per KV head
     (2, 12, 2, 1500, [1500, 65], 64),            # 6 per KV head: two head groups, the second of 2
+    # 16 splits of 64 keys over 128 (sequence, KV head) pairs, some empty
+    (16, 32, 8, 1024, [1024, 3, 64, 65, 1000, 1, 512, 1023] * 2, 128),
 ])
 def test_decode_fp8_parity(B, Hq, Hkv, n, lens, d):
     print(f"fp8 decode parity B={B} Hq={Hq} Hkv={Hkv} n={n} d={d}", flush=True)
@@ -131,10 +138,11 @@ def test_decode_constant_values():
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_decode_writes_nothing_outside_its_outputs(kv):
+@pytest.mark.parametrize("B,Hq,Hkv,n", [(3, 8, 2, 5000), (16, 32, 8, 1024)])
+def test_decode_writes_nothing_outside_its_outputs(kv, B, Hq, Hkv, n):
     """o and lse live inside NaN-filled guard regions of a larger allocation:
     every guard element is still NaN (bitwise) after the call."""
-    B, Hq, Hkv, n, d, G = 3, 8, 2, 5000, 128, 4096
+    d, G = 128, 4096
     q = randn((B, Hq, d), 960, device=DEV)
     if kv == "fp8":
         kc, ks = yk.yoco_kv_quantize_fp8(randn((B, Hkv, n, d), 961, dtype="f32", device=DEV))

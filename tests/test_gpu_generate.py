@@ -62,6 +62,8 @@ def test_swa_decode_matches_oracle(dt, d, W, pos):
 @pytest.mark.parametrize("B,Hq,Hkv,W,pos,rows", [
     (2, 16, 2, 512, 700, None),          # 8 query heads per KV head: two head groups share each split
     (64, 8, 8, 8192, 10000, [0, 37, 63]),  # long splits: the whole-line K form (sampled sequences checked)
+    (16, 32, 8, 1024, 1500, [0, 5, 15]),   # the generation shape: 16 splits of 64 slots
+    (16, 64, 8, 1024, 700, [1, 9]),        # two head groups, 11 splits
 ])
 def test_swa_decode_append_with_head_groups_and_long_splits(B, Hq, Hkv, W, pos, rows):
     """The append folded into the decode: the split holding slot pos mod W
