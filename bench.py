@@ -937,6 +937,24 @@ def main():
         "timing": "HIP events around the back-to-back cross-layer launches of every timed step; per launch = span / layers",
     }
 
+    # the same step captured once as a HIP graph and replayed (no host launch
+    # gaps between its 17 kernels); the headline value stays the stream-launched step
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        g.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    ms_graph = g0.elapsed_time(g1) / args.steps
+    del g
+
     peaks = run_peaks(dev)
     roofline["measured_peak"] = peaks["mfma_bf16_TFLOP/s"]
     roofline["frac_of_measured_peak"] = attn_tflops / peaks["mfma_bf16_TFLOP/s"]
@@ -962,6 +980,8 @@ def main():
             "flops_per_step": step.flops,
         },
         "frac_mfma_peak": tflops / BF16_PEAK_TFLOPS,
+        "graph": {"ms_per_step": ms_graph, "TFLOP/s": step.flops / (ms_graph * 1e-3) / 1e12,
+                  "timing": "the step captured once as a HIP graph; events around back-to-back replays"},
         "roofline": roofline,
         "measured_peaks": peaks,
     }

@@ -192,3 +192,44 @@ def test_attention_writes_nothing_outside_its_outputs(kind, dt):
     for buf, m in ((obuf, o.numel()), (lbuf, lse.numel())):
         assert bool(torch.isnan(buf[:G]).all()) and bool(torch.isnan(buf[G + m:]).all())
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+
+
+def test_prefill_step_graph_replays_match_eager():
+    """The prefill step (window layers, the global projection, causal cross
+    layers over the shared cache) captured as a HIP graph: every replay, with
+    eager work and synchronisations between the replays, reproduces the eager
+    step bitwise."""
+    B, Hq, Hkv, N, d, D, W = 1, 8, 2, 640, 128, 512, 128
+    swa = [_inputs(B, Hq, Hkv, N, N, d, "bf16", 1300 + 10 * i) for i in range(2)]
+    x = randn((B, N, D), 1350, device=DEV)
+    wk = randn((Hkv * d, D), 1351, std=0.05, device=DEV)
+    wv = randn((Hkv * d, D), 1352, std=0.05, device=DEV)
+    qc = [randn((B, Hq, N, d), 1360 + i, device=DEV) for i in range(2)]
+    kc = torch.empty(B, Hkv, N, d, dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    o_swa = [torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=DEV) for _ in swa]
+    o_cross = [torch.empty(B, Hq, N, d, dtype=torch.bfloat16, device=DEV) for _ in qc]
+
+    def step():
+        for (q, k, v), o in zip(swa, o_swa):
+            yk.yoco_swa_attn(q, k, v, W, o=o)
+        yk.yoco_global_kv_proj(x, wk, wv, kc, vc)
+        for q, o in zip(qc, o_cross):
+            yk.yoco_cross_attn_prefill(q, kc, vc, o=o)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in o_swa + o_cross + [kc, vc]]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in o_swa + o_cross + [kc, vc]:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(o_swa + o_cross + [kc, vc], ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
