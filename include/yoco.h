@@ -414,9 +414,14 @@ size_t yoco_kv_quantize_fp8_workspace_bytes(int Hkv);
  * rounds of 8 independent 32x32x16 bf16 MFMAs (2^18 flops per round) on
  * operands of ones, and writes out[4 * blocks] = 128 * iters per wave
  * (exact for iters <= 2^20).
+ * yoco_peak_mfma_bf16_toggling runs the same count of MFMAs (iters a
+ * multiple of 8) on operands that change every instruction, as real data's
+ * do: per-lane integers in [-127, 127] whose products cancel over every 8
+ * rounds, so out[4 * blocks] = 0 exactly per wave.
  */
 yoco_status yoco_peak_hbm_read(const void* buf, size_t bytes, uint32_t* partial, int blocks, void* stream);
 yoco_status yoco_peak_mfma_bf16(int iters, float* out, int blocks, void* stream);
+yoco_status yoco_peak_mfma_bf16_toggling(int iters, float* out, int blocks, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* yoco_status_string(yoco_status status);

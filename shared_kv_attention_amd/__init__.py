@@ -27,6 +27,7 @@ __all__ = [
     "yoco_swa_attn_halo",
     "yoco_peak_hbm_read",
     "yoco_peak_mfma_bf16",
+    "yoco_peak_mfma_bf16_toggling",
     "yoco_attn_merge",
     "yoco_cross_attn_prefill",
     "yoco_cross_attn_decode",
@@ -85,6 +86,7 @@ _SIGS = {
     "yoco_kv_quantize_fp8_workspace_bytes": (_sz, [_i]),
     "yoco_peak_hbm_read": (_i, [_vp, _sz, _vp, _i, _vp]),
     "yoco_peak_mfma_bf16": (_i, [_i, _vp, _i, _vp]),
+    "yoco_peak_mfma_bf16_toggling": (_i, [_i, _vp, _i, _vp]),
     "yoco_status_string": (ctypes.c_char_p, [_i]),
     "yoco_version": (_i, []),
 }
@@ -271,6 +273,17 @@ def yoco_peak_mfma_bf16(iters, blocks=1024, out=None, device=None, stream=None):
         out = torch.empty(4 * blocks, dtype=torch.float32, device=device or "cuda")
     st = lib().yoco_peak_mfma_bf16(int(iters), _ptr(out), int(blocks), _stream(stream))
     _check(st, "yoco_peak_mfma_bf16")
+    return out
+
+
+def yoco_peak_mfma_bf16_toggling(iters, blocks=1024, out=None, device=None, stream=None):
+    """The matrix-core loop on operands that change every instruction (iters a multiple of 8); returns
+    out [4 * blocks], exactly 0."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(4 * blocks, dtype=torch.float32, device=device or "cuda")
+    st = lib().yoco_peak_mfma_bf16_toggling(int(iters), _ptr(out), int(blocks), _stream(stream))
+    _check(st, "yoco_peak_mfma_bf16_toggling")
     return out
 
 

@@ -344,6 +344,13 @@ yoco_status yoco_peak_mfma_bf16(int iters, float* out, int blocks, void* stream)
   return launched(yoco::launch_peak_mfma(iters, out, blocks, as_stream(stream)));
 }
 
+yoco_status yoco_peak_mfma_bf16_toggling(int iters, float* out, int blocks, void* stream) {
+  if (!out) return YOCO_ERR_NULL;
+  if (iters < 8 || iters % 8 != 0 || iters > (1 << 20) || blocks < 1 || blocks > 65536) return YOCO_ERR_SHAPE;
+  if (!aligned(out, 4)) return YOCO_ERR_ALIGN;
+  return launched(yoco::launch_peak_mfma_toggle(iters, out, blocks, as_stream(stream)));
+}
+
 yoco_status yoco_cross_attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                                     int Hq, int Hkv, int Nq, int n_kv, int n_cap, int q_offset, int d,
                                     float softmax_scale, yoco_dtype dtype, void* stream) {

@@ -158,6 +158,7 @@ hipError_t launch_quant_encode(const QuantArgs& a, bool is_bf16, hipStream_t str
 hipError_t launch_attn_merge(const MergeArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_peak_read(const void* src, long long bytes, uint32_t* partial, int blocks, hipStream_t stream);
 hipError_t launch_peak_mfma(int iters, float* out, int blocks, hipStream_t stream);
+hipError_t launch_peak_mfma_toggle(int iters, float* out, int blocks, hipStream_t stream);
 hipError_t launch_gret_prefill(const GretArgs& a, hipStream_t stream);
 hipError_t launch_gret_decode(const GretDecodeArgs& a, bool is_bf16, hipStream_t stream);
 hipError_t launch_gret_norm(const GretNormArgs& a, bool is_bf16, hipStream_t stream);

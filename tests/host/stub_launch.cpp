@@ -42,6 +42,7 @@ hipError_t launch_gret_norm(const GretNormArgs& a, bool, hipStream_t) { ++g_laun
 hipError_t launch_attn_merge(const MergeArgs& a, bool, hipStream_t) { ++g_launches; g_merge = a; return hipSuccess; }
 hipError_t launch_peak_read(const void*, long long, uint32_t*, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_peak_mfma(int, float*, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_peak_mfma_toggle(int, float*, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_linear(const LinArgs& a, int mode, bool, hipStream_t) {
   ++g_launches; g_lin = a; g_lin_mode = mode; return hipSuccess;
 }

@@ -319,6 +319,12 @@ def test_peak_microbenchmark_errors(L):
     assert L.yoco_peak_mfma_bf16(0, P, 8, None) == SHAPE
     assert L.yoco_peak_mfma_bf16((1 << 20) + 1, P, 8, None) == SHAPE
     assert L.yoco_peak_mfma_bf16(10, P, 70000, None) == SHAPE
+    assert L.yoco_peak_mfma_bf16_toggling(16, None, 8, None) == NULL
+    assert L.yoco_peak_mfma_bf16_toggling(12, P, 8, None) == SHAPE
+    assert L.yoco_peak_mfma_bf16_toggling(0, P, 8, None) == SHAPE
+    assert L.yoco_peak_mfma_bf16_toggling(1 << 21, P, 8, None) == SHAPE
+    assert L.yoco_peak_mfma_bf16_toggling(16, P, 0, None) == SHAPE
+    assert L.yoco_peak_mfma_bf16_toggling(16, P + 1, 8, None) == ALIGN
 
 
 def quant(L, **kw):

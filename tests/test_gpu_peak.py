@@ -1,6 +1,7 @@
 """The achievable-peak microbenchmarks compute checkable results: the read's
 per-workgroup sums add up (modulo 2^32) to the sum of every 32-bit word of
-the buffer, and the matrix-core loop's outputs equal 128 * iters exactly."""
+the buffer, and the matrix-core loops' outputs equal 128 * iters (operands
+of ones) and 0 (operands that cancel over every 8 rounds) exactly."""
 import pytest
 import torch
 
@@ -27,3 +28,10 @@ def test_peak_mfma_exact(iters, blocks):
     out = yk.yoco_peak_mfma_bf16(iters, blocks=blocks)
     torch.cuda.synchronize()
     assert torch.all(out == 128.0 * iters)
+
+
+@pytest.mark.parametrize("iters,blocks", [(8, 1), (1000, 256), (1 << 20, 8)])
+def test_peak_mfma_toggling_exact(iters, blocks):
+    out = yk.yoco_peak_mfma_bf16_toggling(iters, blocks=blocks)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0.0)
