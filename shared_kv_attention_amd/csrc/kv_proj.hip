@@ -20,6 +20,14 @@
 //    A norm gain gamma, when given, multiplies X during staging.
 //  * 128x128 output tile per 256-thread workgroup, 64-element k steps (32 for
 //    float32), LDS double buffering with XOR-swizzled 16-byte chunks.
+//  * bf16 without a norm gain, when the features fill 256-row tiles and the
+//    grid still covers the chip: 256 features x 128 tokens per 8-wave
+//    workgroup, one workgroup per CU, a ring of three LDS stages with both
+//    operands loaded global -> LDS two stages ahead, so that a stage's load
+//    latency is covered by two stages of matrix work.  The row sums of
+//    squares come from the X fragments each wave reads for the matrix core
+//    (summed in the same order as the staging form's, so both forms give
+//    identical bits).
 #include "common.hpp"
 #include "launch.hpp"
 #include "index_map.hpp"
@@ -291,10 +299,222 @@ __global__ __launch_bounds__(256, 2) void kv_proj_kernel(ProjArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Three-stage ring form (bf16, no norm gain).  Eight waves: wave w computes
+// features f0 + (w >> 1) * 64 .. + 63 for tokens t0 + (w & 1) * 64 .. + 63.
+// Every load is an LDS DMA issued in inline assembly, so the compiler sees
+// no memory operation in flight in the k loop and adds no waits of its own;
+// the loop waits for exactly the stage it needs (vmcnt) before each barrier.
+// ---------------------------------------------------------------------------
+struct ProjRing {
+  static constexpr int BM = 256, BN = 128, NW = 8, NT = 512;
+  static constexpr int BKK = 64;                   // bf16 elements per stage (128-byte rows)
+  static constexpr int W_PER_T = BM * 8 / NT;      // W chunks per thread per stage (4)
+  static constexpr int X_PER_T = BN * 8 / NT;      // X chunks per thread per stage (2)
+  static constexpr int LOADS = W_PER_T + X_PER_T;  // loads per thread per stage
+  static constexpr int W_BYTES = BM * 128, X_BYTES = BN * 128;
+  static constexpr int NKS = BKK / 16;
+};
+
+// one 16-byte global -> LDS load; m0 = the wave's LDS destination
+__device__ __forceinline__ void proj_dma16(const char* src, unsigned lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_dst) : "memory");
+}
+// wait until at most N loads are in flight, then a workgroup barrier
+// (the scheduling barriers keep the instruction scheduler from moving LDS
+// reads of either stage across it)
+template <int N>
+__device__ __forceinline__ void proj_stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
+  using C = ProjRing;
+  __shared__ __attribute__((aligned(16))) char wb0[C::W_BYTES], xb0[C::X_BYTES];
+  __shared__ __attribute__((aligned(16))) char wb1[C::W_BYTES], xb1[C::X_BYTES];
+  __shared__ __attribute__((aligned(16))) char wb2[C::W_BYTES], xb2[C::X_BYTES];
+  char* const wbuf[3] = {wb0, wb1, wb2};
+  char* const xbuf[3] = {xb0, xb1, xb2};
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 5, r32 = l & 31;
+  const int wf = w >> 1, wt = w & 1;
+  const int HD = a.Hkv * a.d;
+  const int F = 2 * HD;
+  const int M = a.B * a.N;
+  // the same 2 x 4 XCD partition of the (feature tile, token tile) grid as
+  // the staging form
+  const int nft = F / C::BM;
+  const int ntt = (M + C::BN - 1) / C::BN;
+  int tt, ft;
+  if (!proj_tile(blockIdx.x, nft, ntt, ft, tt)) return;
+  const int t0 = tt * C::BN;
+  const int f0 = ft * C::BM;
+
+  // slot P = NT r + tid of a tile holds row P / 8 at physical chunk P % 8,
+  // fetched from logical chunk (P % 8) ^ swizzle(row); each wave
+  // instruction fills 64 consecutive slots.  Token rows past the end read
+  // the last row (finite data; never written).
+  const char* wsrc[C::W_PER_T];
+  const char* xsrc[C::X_PER_T];
+#pragma unroll
+  for (int r = 0; r < C::W_PER_T; ++r) {
+    const int slot = C::NT * r + tid, row = slot >> 3, pch = slot & 7;
+    const int frow = f0 + row;
+    const void* wmat = frow < HD ? a.w_k : a.w_v;
+    const int fr = frow < HD ? frow : frow - HD;
+    wsrc[r] = static_cast<const char*>(wmat) + (size_t)fr * a.D * 2 + ((pch ^ swz8(row)) << 4);
+  }
+#pragma unroll
+  for (int r = 0; r < C::X_PER_T; ++r) {
+    const int slot = C::NT * r + tid, row = slot >> 3, pch = slot & 7;
+    const int trow = min(t0 + row, M - 1);
+    xsrc[r] = static_cast<const char*>(a.x) + (size_t)trow * a.D * 2 + ((pch ^ swz8(row)) << 4);
+  }
+  auto issue = [&](int ks, int buf) __attribute__((always_inline)) {
+    const size_t koff = (size_t)ks * C::BKK * 2;
+    const unsigned wd = (unsigned)(size_t)wbuf[buf] + 64 * 16 * w;
+    const unsigned xd = (unsigned)(size_t)xbuf[buf] + 64 * 16 * w;
+#pragma unroll
+    for (int r = 0; r < C::W_PER_T; ++r) proj_dma16(wsrc[r] + koff, __builtin_amdgcn_readfirstlane(wd + C::NT * 16 * r));
+#pragma unroll
+    for (int r = 0; r < C::X_PER_T; ++r) proj_dma16(xsrc[r] + koff, __builtin_amdgcn_readfirstlane(xd + C::NT * 16 * r));
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
+  // sums of squares of this lane's X rows (tokens wt*64 + jj*32 + r32), one
+  // per 16-byte chunk position 2 kc + g of a stage, accumulated over stages
+  float ssc[2][C::NKS];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int kc = 0; kc < C::NKS; ++kc) ssc[jj][kc] = 0.f;
+
+  const int nks = a.D / C::BKK;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const char* wt_tile = wbuf[buf];
+    const char* xt_tile = xbuf[buf];
+#pragma unroll
+    for (int kc = 0; kc < C::NKS; ++kc) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = lds_frag_row<bf16>(wt_tile, wf * 64 + i * 32 + r32, kc, g);
+        bfr[i] = lds_frag_row<bf16>(xt_tile, wt * 64 + i * 32 + r32, kc, g);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma32(af[i], bfr[jj], acc[i][jj]);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) ssc[jj][kc] += chunk_sumsq<bf16>(__builtin_bit_cast(u32x4, bfr[jj]));
+    }
+  };
+  // prologue: stages 0 and 1 in flight, wait for stage 0
+  issue(0, 0);
+  issue(min(1, nks - 1), 1);
+  proj_stage_barrier<C::LOADS>();
+  // stage ks: issue stage ks + 2 (the last stage again past the end: its
+  // buffer is never read again and the count in flight stays fixed), compute
+  // from stage ks's buffer, wait for stage ks + 1 and barrier.  Buffer
+  // indices rotate by three, so the loop is unrolled by three.
+  int ks = 0;
+  for (; ks + 3 <= nks; ks += 3) {
+    issue(min(ks + 2, nks - 1), 2); compute(0); proj_stage_barrier<C::LOADS>();
+    issue(min(ks + 3, nks - 1), 0); compute(1); proj_stage_barrier<C::LOADS>();
+    issue(min(ks + 4, nks - 1), 1); compute(2); proj_stage_barrier<C::LOADS>();
+  }
+  if (ks < nks) { issue(min(ks + 2, nks - 1), 2); compute(0); proj_stage_barrier<C::LOADS>(); }
+  if (ks + 1 < nks) { issue(min(ks + 3, nks - 1), 0); compute(1); proj_stage_barrier<C::LOADS>(); }
+  // drain the loads still in flight before the LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Row factors: lanes l and l ^ 32 hold the chunk sums of the even and odd
+  // chunk positions; the sum is formed as
+  // ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)).
+  float rs[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    float p[C::NKS];
+#pragma unroll
+    for (int kc = 0; kc < C::NKS; ++kc) p[kc] = ssc[jj][kc] + __shfl_xor(ssc[jj][kc], 32);
+    const float s = (p[0] + p[1]) + (p[2] + p[3]);
+    rs[jj] = 1.0f / sqrtf(s / (float)a.D + a.eps);
+  }
+
+  // Epilogue: acc[i][jj][e] = C^T[feature f0 + wf*64 + i*32 + 8*(e/4) + 4g + e%4][token t0 + wt*64 + jj*32 + r32]
+  // A wave's 64 features lie in one head of one of K and V (f0 is a multiple
+  // of 128 and Hkv*d, d of 64).
+  float amax = 0.f;   // largest |value| this lane stores (amax_bits mode)
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int tl = wt * 64 + jj * 32 + r32;
+    const int tok = t0 + tl;
+    if (tok >= M) continue;
+    const float rsj = rs[jj];
+    const int bb = tok / a.N, n = tok % a.N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int f = f0 + wf * 64 + i * 32 + 8 * qd + 4 * g;
+        if (f >= F) continue;
+        const int which = f >= HD;
+        const int fr = which ? f - HD : f;
+        const int hh = fr / a.d, c = fr % a.d;
+        bf16* dst = static_cast<bf16*>(which ? a.v_out : a.k_out) +
+                 ((size_t)(bb * a.Hkv + hh) * a.n_cap + a.row0 + n) * a.d + c;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][jj][4 * qd + e] * rsj;
+        if (a.rope_log2_theta != 0.0 && !which) {   // keys only, at their cache position
+          const long long p = a.pos0 + n;
+          rope_pair(v[0], v[1], (double)p * rope_inv_freq(c >> 1, a.d, a.rope_log2_theta));
+          rope_pair(v[2], v[3], (double)p * rope_inv_freq((c >> 1) + 1, a.d, a.rope_log2_theta));
+        }
+        // the values as stored
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (float)(bf16)v[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (bf16)v[e];   // exact: already bf16 values
+        *reinterpret_cast<bf16x4*>(dst) = v4;
+      }
+    }
+  }
+  if (a.amax_bits != nullptr) {
+    // per-head maxima for a following 8-bit encode: one atomic per wave
+    // (integer max on the bit patterns of non-negative floats orders them
+    // like their values)
+    amax = row16_max(amax);
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int f = f0 + wf * 64;
+    const int which = f >= HD;
+    const int hh = (which ? f - HD : f) / a.d;
+    if (l == 0 && amax > 0.f) atomicMax(a.amax_bits + which * a.Hkv + hh, __float_as_uint(amax));
+  }
+}
+
 hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream) {
   const int F = 2 * a.Hkv * a.d;
   const int M = a.B * a.N;
   const long long ntt = (M + 127) / 128, nft = F / 128;
+  // the ring form when its grid (one workgroup per CU) still covers the 256 CUs
+  if (is_bf16 && a.norm_w == nullptr && F % 256 == 0 && ntt * (F / 256) >= 256) {
+    hipLaunchKernelGGL(kv_proj_ring_kernel, dim3((unsigned)proj_workgroups(F / 256, (int)ntt)), dim3(512), 0, stream, a);
+    return hipGetLastError();
+  }
   // the 2 x 4 XCD partition pads the token tiles to a multiple of 4
   const long long nwg = proj_workgroups((int)nft, (int)ntt);
   dim3 grid((unsigned)nwg);

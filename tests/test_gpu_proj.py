@@ -174,3 +174,37 @@ def test_decode_over_a_cache_the_projection_wrote_in_8_bits():
     vd = oracle.dequantize_kv_fp8(vc.cpu().numpy(), vs.cpu().numpy())
     ro, _ = oracle.decode_attention(to64(q), kd, vd, [N] * B)
     check(to64(o), ro, "bf16", "decode over the projected 8-bit cache", rel_axes=(2,))
+
+
+@pytest.mark.parametrize("B,N,D,pos0,rope", [(1, 4096, 3072, 0, 0.0), (2, 2100, 192, 3, 1e4), (1, 4100, 256, 0, 0.0),
+                                             (3, 1400, 320, 9, 1e4)])
+def test_kv_proj_ring_form_equals_staging_form(B, N, D, pos0, rope):
+    """bf16 without a norm gain runs the three-stage ring form when its grid (256 features x 128 tokens per
+    workgroup) covers the chip; with a gain of ones the 128 x 128 staging form runs on the same values.  The two
+    forms sum every product and every square in the same order: outputs bitwise equal.  D / 64 = 48, 3, 4, 5 k
+    stages cover every remainder of the ring's three buffers; ragged token tiles and tiles across the batch
+    boundary included."""
+    Hkv, d = 8, 128
+    n_cap = pos0 + N + 5
+    print(f"kv_proj ring vs staging B={B} N={N} D={D} pos0={pos0} rope={rope}", flush=True)
+    x = randn((B, N, D), 1100 + D, device=DEV)
+    wk = randn((Hkv * d, D), 1101 + D, std=D ** -0.5, device=DEV)
+    wv = randn((Hkv * d, D), 1102 + D, std=D ** -0.5, device=DEV)
+    ones = torch.ones(D, dtype=torch.bfloat16, device=DEV)
+    outs = []
+    for g in (None, ones):
+        ko = torch.full((B, Hkv, n_cap, d), 7.0, dtype=torch.bfloat16, device=DEV)
+        vo = torch.full_like(ko, 7.0)
+        yk.yoco_global_kv_proj(x, wk, wv, ko, vo, pos0=pos0, norm_w=g, rope_theta=rope)
+        outs.append((ko, vo))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    rows = [0, 1, 127, 128, N - 1]
+    rk, rv = oracle.global_kv_proj(to64(x)[:, rows], to64(wk), to64(wv), Hkv, d)
+    if rope:
+        # keys rotated at their cache positions
+        rk = np.concatenate([oracle.apply_rope(rk[:, :, i:i + 1], pos0 + r, rope) for i, r in enumerate(rows)], axis=2)
+    idx = [pos0 + r for r in rows]
+    check(to64(outs[0][0])[:, :, idx], rk, "bf16", "K", rel_axes=(2, 3))
+    check(to64(outs[0][1])[:, :, idx], rv, "bf16", "V", rel_axes=(2, 3))
+    assert torch.all(outs[0][0][:, :, :pos0] == 7.0) and torch.all(outs[0][0][:, :, pos0 + N:] == 7.0)
