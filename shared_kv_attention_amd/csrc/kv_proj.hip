@@ -390,33 +390,49 @@ __global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
-  // sums of squares of this lane's X rows (tokens wt*64 + jj*32 + r32), one
-  // per 16-byte chunk position 2 kc + g of a stage, accumulated over stages
-  float ssc[2][C::NKS];
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-    for (int kc = 0; kc < C::NKS; ++kc) ssc[jj][kc] = 0.f;
+  // sums of squares of this lane's X rows (tokens wt*64 + jj*32 + r32) at
+  // the 16-byte chunk position 2 wf + g of every stage: the four waves that
+  // read the same rows take one k step each
+  float ssc[2] = {0.f, 0.f};
 
   const int nks = a.D / C::BKK;
   auto compute = [&](int buf) __attribute__((always_inline)) {
     const char* wt_tile = wbuf[buf];
     const char* xt_tile = xbuf[buf];
+    // every fragment of the stage requested up front (16 LDS reads in
+    // flight), the matrix steps taking them as they arrive
+    bf16x8 af[C::NKS][2], bfr[C::NKS][2];
 #pragma unroll
     for (int kc = 0; kc < C::NKS; ++kc) {
-      bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        af[i] = lds_frag_row<bf16>(wt_tile, wf * 64 + i * 32 + r32, kc, g);
-        bfr[i] = lds_frag_row<bf16>(xt_tile, wt * 64 + i * 32 + r32, kc, g);
+        af[kc][i] = lds_frag_row<bf16>(wt_tile, wf * 64 + i * 32 + r32, kc, g);
+        bfr[kc][i] = lds_frag_row<bf16>(xt_tile, wt * 64 + i * 32 + r32, kc, g);
       }
+    }
+    // this wave's share of the row sums: its rows' chunk 2 wf + g, read again
+    const bf16x8 xs0 = lds_frag_row<bf16>(xt_tile, wt * 64 + r32, wf, g);
+    const bf16x8 xs1 = lds_frag_row<bf16>(xt_tile, wt * 64 + 32 + r32, wf, g);
+#pragma unroll
+    for (int kc = 0; kc < C::NKS; ++kc) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma32(af[i], bfr[jj], acc[i][jj]);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) ssc[jj][kc] += chunk_sumsq<bf16>(__builtin_bit_cast(u32x4, bfr[jj]));
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma32(af[kc][i], bfr[kc][jj], acc[i][jj]);
     }
+    ssc[0] += chunk_sumsq<bf16>(__builtin_bit_cast(u32x4, xs0));
+    ssc[1] += chunk_sumsq<bf16>(__builtin_bit_cast(u32x4, xs1));
+    // issue order: the reads of two k steps, then each k step's 4 matrix
+    // steps followed by the reads two steps ahead (masks: 0x100 LDS read,
+    // 0x008 MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // prologue: stages 0 and 1 in flight, wait for stage 0
   issue(0, 0);
@@ -434,19 +450,23 @@ __global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
   }
   if (ks < nks) { issue(min(ks + 2, nks - 1), 2); compute(0); proj_stage_barrier<C::LOADS>(); }
   if (ks + 1 < nks) { issue(min(ks + 3, nks - 1), 0); compute(1); proj_stage_barrier<C::LOADS>(); }
-  // drain the loads still in flight before the LDS is released
+  // drain the loads still in flight (the LDS is reused below and released)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  // Row factors: lanes l and l ^ 32 hold the chunk sums of the even and odd
-  // chunk positions; the sum is formed as
+  // Row factors: the chunk sums of the 128 rows meet in LDS (row-major, 8
+  // per row), and each row's sum is formed as
   // ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)).
+  float* const csum = reinterpret_cast<float*>(xb0);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) csum[(wt * 64 + jj * 32 + r32) * 8 + 2 * wf + g] = ssc[jj];
+  __syncthreads();
   float rs[2];
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
-    float p[C::NKS];
-#pragma unroll
-    for (int kc = 0; kc < C::NKS; ++kc) p[kc] = ssc[jj][kc] + __shfl_xor(ssc[jj][kc], 32);
-    const float s = (p[0] + p[1]) + (p[2] + p[3]);
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(csum + (wt * 64 + jj * 32 + r32) * 8);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(csum + (wt * 64 + jj * 32 + r32) * 8 + 4);
+    const float s = ((lo[0] + lo[1]) + (lo[2] + lo[3])) + ((hi[0] + hi[1]) + (hi[2] + hi[3]));
     rs[jj] = 1.0f / sqrtf(s / (float)a.D + a.eps);
   }
 
