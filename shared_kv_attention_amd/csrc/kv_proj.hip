@@ -396,11 +396,12 @@ __global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
   float ssc[2] = {0.f, 0.f};
 
   const int nks = a.D / C::BKK;
-  auto compute = [&](int buf) __attribute__((always_inline)) {
+  // stage work from buffer buf; the loads of stage ks_next into buffer nbuf
+  // are issued once the first k steps' fragments are requested
+  auto compute = [&](int buf, int ks_next, int nbuf) __attribute__((always_inline)) {
     const char* wt_tile = wbuf[buf];
     const char* xt_tile = xbuf[buf];
-    // every fragment of the stage requested up front (16 LDS reads in
-    // flight), the matrix steps taking them as they arrive
+    // every fragment of the stage requested ahead of its matrix steps
     bf16x8 af[C::NKS][2], bfr[C::NKS][2];
 #pragma unroll
     for (int kc = 0; kc < C::NKS; ++kc) {
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
         af[kc][i] = lds_frag_row<bf16>(wt_tile, wf * 64 + i * 32 + r32, kc, g);
         bfr[kc][i] = lds_frag_row<bf16>(xt_tile, wt * 64 + i * 32 + r32, kc, g);
       }
+      if (kc == 1) issue(ks_next, nbuf);
     }
     // this wave's share of the row sums: its rows' chunk 2 wf + g, read again
     const bf16x8 xs0 = lds_frag_row<bf16>(xt_tile, wt * 64 + r32, wf, g);
@@ -444,12 +446,12 @@ __global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
   // indices rotate by three, so the loop is unrolled by three.
   int ks = 0;
   for (; ks + 3 <= nks; ks += 3) {
-    issue(min(ks + 2, nks - 1), 2); compute(0); proj_stage_barrier<C::LOADS>();
-    issue(min(ks + 3, nks - 1), 0); compute(1); proj_stage_barrier<C::LOADS>();
-    issue(min(ks + 4, nks - 1), 1); compute(2); proj_stage_barrier<C::LOADS>();
+    compute(0, min(ks + 2, nks - 1), 2); proj_stage_barrier<C::LOADS>();
+    compute(1, min(ks + 3, nks - 1), 0); proj_stage_barrier<C::LOADS>();
+    compute(2, min(ks + 4, nks - 1), 1); proj_stage_barrier<C::LOADS>();
   }
-  if (ks < nks) { issue(min(ks + 2, nks - 1), 2); compute(0); proj_stage_barrier<C::LOADS>(); }
-  if (ks + 1 < nks) { issue(min(ks + 3, nks - 1), 0); compute(1); proj_stage_barrier<C::LOADS>(); }
+  if (ks < nks) { compute(0, min(ks + 2, nks - 1), 2); proj_stage_barrier<C::LOADS>(); }
+  if (ks + 1 < nks) { compute(1, min(ks + 3, nks - 1), 0); proj_stage_barrier<C::LOADS>(); }
   // drain the loads still in flight (the LDS is reused below and released)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
