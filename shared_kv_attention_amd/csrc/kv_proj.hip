@@ -317,7 +317,10 @@ struct ProjRing {
   static constexpr int NKS = BKK / 16;
 };
 
-// one 16-byte global -> LDS load; m0 = the wave's LDS destination
+// one 16-byte global -> LDS load; m0 = the wave's LDS destination.  m0 is a
+// reserved register the compiler cannot be told about; it is safe here
+// because nothing else in kv_proj_ring_kernel reads m0 (no LDS-DMA builtin,
+// no m0-indexed instruction; the cross-lane exchanges are ds_bpermute).
 __device__ __forceinline__ void proj_dma16(const char* src, unsigned lds_dst) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_dst) : "memory");
