@@ -177,13 +177,14 @@ def test_decode_over_a_cache_the_projection_wrote_in_8_bits():
 
 
 @pytest.mark.parametrize("B,N,D,pos0,rope", [(1, 4096, 3072, 0, 0.0), (2, 2100, 192, 3, 1e4), (1, 4100, 256, 0, 0.0),
-                                             (3, 1400, 320, 9, 1e4)])
+                                             (3, 1400, 320, 9, 1e4), (1, 4096, 64, 0, 0.0), (2, 2048, 128, 1, 1e4),
+                                             (1, 10000, 256, 0, 0.0)])
 def test_kv_proj_ring_form_equals_staging_form(B, N, D, pos0, rope):
     """bf16 without a norm gain runs the three-stage ring form when its grid (256 features x 128 tokens per
     workgroup) covers the chip; with a gain of ones the 128 x 128 staging form runs on the same values.  The two
     forms sum every product and every square in the same order: outputs bitwise equal.  D / 64 = 48, 3, 4, 5 k
     stages cover every remainder of the ring's three buffers; ragged token tiles and tiles across the batch
-    boundary included."""
+    boundary included; one and two k stages (D = 64, 128) and a grid of several rounds (10000 tokens)."""
     Hkv, d = 8, 128
     n_cap = pos0 + N + 5
     print(f"kv_proj ring vs staging B={B} N={N} D={D} pos0={pos0} rope={rope}", flush=True)
