@@ -352,6 +352,40 @@ def run_decode(wl, dev, steps, sample=None, n_groups=2):
     }
 
 
+# ---------------------------------------------------------------- 8-bit cache writer
+def run_quantize(wl, dev, reps=5):
+    """Times yoco_kv_quantize_fp8 on one bf16 cache tensor of the decode
+    workload's shape (its K).  The per-head scale needs every row's maximum
+    before any code is written, so the writer reads the input twice (maxima,
+    then encode) and writes the codes once: those are the bytes counted."""
+    B, ctx, Hkv, d = wl.batch, wl.seq, wl.n_kv_heads, wl.head_dim
+    kv = randn((B, Hkv, ctx, d), seed_for(wl.wid, 0), device=dev)
+    codes = torch.empty(kv.shape, dtype=torch.uint8, device=dev)
+    scale = torch.empty(Hkv, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(yk.yoco_kv_quantize_fp8_workspace_bytes(Hkv), 16), dtype=torch.uint8, device=dev)
+    call = lambda: yk.yoco_kv_quantize_fp8(kv, codes, scale, ws)  # noqa: E731
+    call()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        call()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    n = kv.numel()
+    nbytes = 2 * n * 2 + n
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"shape": [B, Hkv, ctx, d], "input": "bf16", "calls": reps, "ms_per_call": ms, "bytes_per_call": nbytes,
+           "GB/s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+           "bytes": "input read twice (per-head maxima, then encode), codes written once",
+           "timing": "HIP events around back-to-back calls (clear + maxima + encode kernels per call)"}
+    del kv, codes
+    return out
+
+
 # ---------------------------------------------------------------- generation
 def run_generation(wl, dev, steps):
     """One generated token per sequence: every self-decoder layer appends the
@@ -1004,6 +1038,7 @@ def main():
         out["decode"]["roofline"]["frac_of_measured_peak"] = out["decode"]["GB/s"] / peaks["hbm_read_GB/s"]
         torch.cuda.empty_cache()
     if not args.no_fp8_decode:
+        out["quantize_fp8"] = run_quantize(WORKLOADS["decode_32k_bf16"], dev)
         out["decode_fp8"] = run_decode(WORKLOADS["decode_512k_fp8"], dev, WORKLOADS["decode_512k_fp8"].decode_steps,
                                        sample=smp_fp8 if want_cpu else None, n_groups=1)
         torch.cuda.empty_cache()

@@ -46,8 +46,20 @@ __global__ __launch_bounds__(256) void quant_amax_kernel(QuantArgs a) {
   const int h = blockIdx.y, b = blockIdx.z;
   const T* base = static_cast<const T*>(a.kv) + (size_t)(b * a.Hkv + h) * a.slab;
   const long long n8 = a.slab / 8;
+  const long long stride = (long long)gridDim.x * 256;
   float m = 0.f;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
+  long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  // four chunks per thread in flight, then the remainder one at a time
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<T>(base + (i + u * stride) * 8, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[u][e]));
+  }
+  for (; i < n8; i += stride) {
     float x[8];
     load8<T>(base + i * 8, x);
 #pragma unroll
@@ -83,20 +95,39 @@ __global__ __launch_bounds__(256) void quant_encode_kernel(QuantArgs a) {
   const T* base = static_cast<const T*>(a.kv) + (size_t)(b * a.Hkv + h) * a.slab;
   uint8_t* out = a.codes + (size_t)(b * a.Hkv + h) * a.dst_slab + a.dst_off;
   const long long n8 = a.slab / 8;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256) {
-    float x[8];
-    load8<T>(base + i * 8, x);
+  const long long stride = (long long)gridDim.x * 256;
+  auto put = [&](long long j, const float* x) __attribute__((always_inline)) {
     u32x2 w;
     w[0] = encode_e4m3_x4(x[0], x[1], x[2], x[3], s);
     w[1] = encode_e4m3_x4(x[4], x[5], x[6], x[7], s);
-    *reinterpret_cast<u32x2*>(out + i * 8) = w;
+    *reinterpret_cast<u32x2*>(out + j * 8) = w;
+  };
+  long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  // four chunks per thread in flight, then the remainder one at a time
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<T>(base + (i + u * stride) * 8, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) put(i + u * stride, x[u]);
+  }
+  for (; i < n8; i += stride) {
+    float x[8];
+    load8<T>(base + i * 8, x);
+    put(i, x);
   }
 }
 
+// About 4096 workgroups over the whole tensor (16 per CU), each looping over
+// its share of a slab: every workgroup of the maxima pass ends in one atomic
+// on its head's word, so a grid of many small workgroups would queue
+// thousands of atomics on each of Hkv words.
 static dim3 quant_grid(const QuantArgs& a) {
   const long long n8 = a.slab / 8;
-  long long per_slab = (n8 + 256 * 4 - 1) / (256 * 4);   // ~4 steps per thread
-  if (per_slab > 1024) per_slab = 1024;
+  const long long slabs = (long long)a.B * a.Hkv;
+  long long per_slab = (n8 + 256 * 4 - 1) / (256 * 4);   // at least ~4 chunks per thread
+  const long long cap = (4096 + slabs - 1) / slabs;
+  if (per_slab > cap) per_slab = cap;
   if (per_slab < 1) per_slab = 1;
   return dim3((unsigned)per_slab, a.Hkv, a.B);
 }
