@@ -118,15 +118,18 @@ __global__ __launch_bounds__(256) void quant_encode_kernel(QuantArgs a) {
   }
 }
 
-// About 4096 workgroups over the whole tensor (16 per CU), each looping over
-// its share of a slab: every workgroup of the maxima pass ends in one atomic
-// on its head's word, so a grid of many small workgroups would queue
-// thousands of atomics on each of Hkv words.
-static dim3 quant_grid(const QuantArgs& a) {
+// A few looping workgroups per CU over the whole tensor (1024 for bf16
+// input, 256 for float32, whose threads move twice the bytes per chunk;
+// measured best of 256 to 8192), each over its share of a slab.  Every
+// workgroup of the maxima pass ends in one atomic on its head's word, so a
+// grid of many small workgroups would also queue thousands of atomics on
+// each of Hkv words.
+static dim3 quant_grid(const QuantArgs& a, bool is_bf16) {
   const long long n8 = a.slab / 8;
   const long long slabs = (long long)a.B * a.Hkv;
   long long per_slab = (n8 + 256 * 4 - 1) / (256 * 4);   // at least ~4 chunks per thread
-  const long long cap = (4096 + slabs - 1) / slabs;
+  const long long total = is_bf16 ? 1024 : 256;
+  const long long cap = (total + slabs - 1) / slabs;
   if (per_slab > cap) per_slab = cap;
   if (per_slab < 1) per_slab = 1;
   return dim3((unsigned)per_slab, a.Hkv, a.B);
@@ -139,17 +142,17 @@ hipError_t launch_quant_clear(uint32_t* amax_bits, int n, hipStream_t stream) {
 
 hipError_t launch_quant_amax(const QuantArgs& a, bool is_bf16, hipStream_t stream) {
   if (is_bf16)
-    hipLaunchKernelGGL((quant_amax_kernel<bf16>), quant_grid(a), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((quant_amax_kernel<bf16>), quant_grid(a, true), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((quant_amax_kernel<float>), quant_grid(a), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((quant_amax_kernel<float>), quant_grid(a, false), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_encode(const QuantArgs& a, bool is_bf16, hipStream_t stream) {
   if (is_bf16)
-    hipLaunchKernelGGL((quant_encode_kernel<bf16>), quant_grid(a), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((quant_encode_kernel<bf16>), quant_grid(a, true), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((quant_encode_kernel<float>), quant_grid(a), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((quant_encode_kernel<float>), quant_grid(a, false), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
