@@ -519,6 +519,19 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int ns = (ctx_b + a.chunk - 1) / a.chunk;
   const size_t base = (size_t)(b * a.Hq + h) * S;
 
+  const int dl = tid & 31, grp = tid >> 5;
+  const int dim = blockIdx.z * 32 + dl;
+  // this thread's first PF partial outputs (splits grp, grp + NG, ...) are
+  // requested with the maxima, so that the three phases below share one
+  // round trip to memory for the common split counts (ns <= NG * PF)
+  constexpr int PF = 8;
+  float ov[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) {
+    const int sk = grp + k * NG;
+    ov[k] = sk < ns ? a.part_o[(base + sk) * D + dim] : 0.f;
+  }
+
   float m = -INFINITY;
   for (int s = tid; s < ns; s += 256) m = fmaxf(m, a.part_m[base + s]);
   const float M = block256_reduce(m, true, red4);
@@ -530,15 +543,31 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
   const float L = block256_reduce(lsum, false, red4);   // its barriers also publish wgt[]
 
-  const int dl = tid & 31, grp = tid >> 5;
-  const int dim = blockIdx.z * 32 + dl;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};   // independent chains for memory-level parallelism
-  int s = grp;
-  for (; s + 3 * NG < ns; s += 4 * NG) {
+  // split k of this thread (s = grp + k NG, k < K) goes to chain k % 4 while
+  // a whole group of four remains (k < K4), the rest to chain 0, in order
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};   // independent chains
+  const int K = grp < ns ? (ns - grp + NG - 1) / NG : 0;
+  const int K4 = K & ~3;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = fmaf(wgt[s + u * NG], a.part_o[(base + s + u * NG) * D + dim], acc[u]);
+  for (int k = 0; k < PF; ++k) {
+    if (k < K) {
+      const float wk = wgt[grp + k * NG];
+      if (k < K4) acc[k & 3] = fmaf(wk, ov[k], acc[k & 3]);
+      else acc[0] = fmaf(wk, ov[k], acc[0]);
+    }
   }
-  for (; s < ns; s += NG) acc[0] = fmaf(wgt[s], a.part_o[(base + s) * D + dim], acc[0]);
+  int k = PF;
+  for (; k < K4; k += 4) {   // PF and K4 are multiples of 4
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int su = grp + (k + u) * NG;
+      acc[u] = fmaf(wgt[su], a.part_o[(base + su) * D + dim], acc[u]);
+    }
+  }
+  for (; k < K; ++k) {
+    const int sk = grp + k * NG;
+    acc[0] = fmaf(wgt[sk], a.part_o[(base + sk) * D + dim], acc[0]);
+  }
   part[grp][dl] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (grp == 0) {
