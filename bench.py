@@ -379,7 +379,9 @@ def run_quantize(wl, dev, reps=5):
     out = {"shape": [B, Hkv, ctx, d], "input": "bf16", "calls": reps, "ms_per_call": ms, "bytes_per_call": nbytes,
            "GB/s": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS,
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                        "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": traffic_from_profile("quant_fp8_decode_32k_bf16.txt", "fp8_quant.hip",
+                                                        "hbm bytes per call")},
            "bytes": "input read twice (per-head maxima, then encode), codes written once",
            "timing": "HIP events around back-to-back calls (clear + maxima + encode kernels per call)"}
     del kv, codes
