@@ -378,6 +378,8 @@ __global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
     const int trow = min(t0 + row, M - 1);
     xsrc[r] = static_cast<const char*>(a.x) + (size_t)trow * a.D * 2 + ((pch ^ swz8(row)) << 4);
   }
+  // (m0 takes the LDS byte offset: the low 32 bits of a generic pointer to
+  // LDS, whose aperture base is 4 GiB-aligned)
   auto issue = [&](int ks, int buf) __attribute__((always_inline)) {
     const size_t koff = (size_t)ks * C::BKK * 2;
     const unsigned wd = (unsigned)(size_t)wbuf[buf] + 64 * 16 * w;
@@ -443,10 +445,11 @@ __global__ __launch_bounds__(512, 2) void kv_proj_ring_kernel(ProjArgs a) {
   issue(0, 0);
   issue(min(1, nks - 1), 1);
   proj_stage_barrier<C::LOADS>();
-  // stage ks: issue stage ks + 2 (the last stage again past the end: its
-  // buffer is never read again and the count in flight stays fixed), compute
-  // from stage ks's buffer, wait for stage ks + 1 and barrier.  Buffer
-  // indices rotate by three, so the loop is unrolled by three.
+  // stage ks: compute from stage ks's buffer, issuing stage ks + 2 on the
+  // way (the last stage again past the end: its buffer is never read again
+  // and the count in flight stays fixed), then wait for stage ks + 1 and
+  // barrier.  Buffer indices rotate by three, so the loop is unrolled by
+  // three.
   int ks = 0;
   for (; ks + 3 <= nks; ks += 3) {
     compute(0, min(ks + 2, nks - 1), 2); proj_stage_barrier<C::LOADS>();
