@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include "launch.hpp"
+#include "index_map.hpp"
 
 namespace {
 
@@ -81,13 +82,19 @@ hipError_t proj_gemm(const void* x, const void* norm_w, const void* w_k, const v
                      int B, int N, int D, int Hkv, int d, int n_cap, int pos0, int row0, float eps,
                      float rope_theta, bool is_bf16, uint32_t* amax, hipStream_t st, bool* fused_amax = nullptr) {
   if (fused_amax) *fused_amax = false;
-  if (is_bf16 && ((long long)B * N >= 16384 || (long long)B * N <= 64)) {
+  // bf16 without a norm gain whose 256-feature tiles cover the 256 CUs: the
+  // projection's own three-stage ring form at every length (2^20 tokens:
+  // 16.4 ms against 19.3 for the wide form below; 4096 tokens: 55 us)
+  const long long M = (long long)B * N;
+  const bool ring = yoco::proj_ring_form(M, 2 * Hkv * d, is_bf16, norm_w != nullptr);
+  if (is_bf16 && !ring && (M >= 16384 || M <= 64)) {
     // the block-layer GEMM in its Q/K/V form with no query heads: for long
-    // prompts its wide bf16 tiles (measured 18.7 vs 22.9 ms at 2^20 tokens),
-    // for a few tokens (the one-token append of generation) its form that
-    // spreads K over many waves.  In between, the 128 x 128 kernel below, two
-    // workgroups per CU, hides latency better (72 vs 80 us at 4096 tokens); it
-    // also serves float32.
+    // prompts with a norm gain its wide bf16 tiles (measured 18.7 vs 22.9 ms
+    // at 2^20 tokens against the 128 x 128 kernel), for a few tokens (the
+    // one-token append of generation) its form that spreads K over many
+    // waves.  In between, the 128 x 128 kernel below, two workgroups per CU,
+    // hides latency better (72 vs 80 us at 4096 tokens); it also serves
+    // float32.
     yoco::LinArgs la{};
     la.x = x;
     la.norm_w = norm_w;

@@ -131,6 +131,11 @@ YOCO_HD int vt_frag_offset(int c, int db, int l, int hh) {
 // With an even number of feature tiles, each XCD takes one block of a 2 x 4
 // partition (half of the feature tiles, a quarter of the token tiles, the
 // token tiles padded to a multiple of 4); padded workgroups have no work.
+// The projection's three-stage ring form: bf16 without a norm gain, the
+// features in 256-row tiles, and at least one such tile per CU (256).
+YOCO_HD bool proj_ring_form(long long M, int F, bool is_bf16, bool has_gain) {
+  return is_bf16 && !has_gain && F % 256 == 0 && ((M + 127) / 128) * (F / 256) >= 256;
+}
 YOCO_HD int proj_workgroups(int nft, int ntt) { return nft % 2 == 0 ? 8 * (nft / 2) * ((ntt + 3) / 4) : ntt * nft; }
 YOCO_HD bool proj_tile(int id, int nft, int ntt, int& ft, int& tt) {
   YOCO_ASSERT(id >= 0 && id < proj_workgroups(nft, ntt));

@@ -539,7 +539,7 @@ hipError_t launch_kv_proj(const ProjArgs& a, bool is_bf16, hipStream_t stream) {
   const int M = a.B * a.N;
   const long long ntt = (M + 127) / 128, nft = F / 128;
   // the ring form when its grid (one workgroup per CU) still covers the 256 CUs
-  if (is_bf16 && a.norm_w == nullptr && F % 256 == 0 && ntt * (F / 256) >= 256) {
+  if (proj_ring_form((long long)M, F, is_bf16, a.norm_w != nullptr)) {
     hipLaunchKernelGGL(kv_proj_ring_kernel, dim3((unsigned)proj_workgroups(F / 256, (int)ntt)), dim3(512), 0, stream, a);
     return hipGetLastError();
   }
