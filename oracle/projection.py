@@ -12,7 +12,7 @@ What the method computes:
   normalisation of the baseline the paper compares against, [S §4 Scaling
   model size]), y = x / sqrt(mean(x^2) + eps) * gamma, eps = 1e-6, gamma = 1
   unless given.
-* Weight layout (a choice of this build, stated so tests can build inputs):
+* Weight layout (a choice made here, stated so tests can build inputs):
   W_K and W_V are [Hkv*d, D] ("out x in"), K = norm(X) @ W_K^T.  Output
   column j = h*d + c goes to KV head h, channel c; caches are head-major
   [B, Hkv, N, d].

@@ -17,7 +17,7 @@ What the method computes (pages cited as in the package docstring):
   (GroupNorm) and multiplied by a swish gate ([S §3 Gated Retention]).
 
 Readings taken (the pages give the forms in words only; the symbols below
-are this build's):
+are the ones used here):
 * gate: gamma_n = sigmoid(z_n) ** (1 / tau) for the per-head, per-position
   gate logit z_n (z_n = x_n . w_gamma is a position-wise product outside this
   path) and temperature tau > 0; log gamma_n = log sigmoid(z_n) / tau.
