@@ -64,24 +64,6 @@ __global__ __launch_bounds__(512) void gret_state_kernel(GretArgs a) {
   const int l = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int c0 = c * a.chunk, clen = min(a.chunk, a.N - c0);
 
-  // inclusive prefix sum of the chunk's log2 decays (positions past the end add 0)
-  {
-    const bool scan_t = t < 256;
-    float x = t < clen ? gate_log2(a.gate[(size_t)bh * a.N + c0 + t], a.inv_tau) : 0.f;
-    if (scan_t) lgc[t] = x;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const float y = scan_t && t >= off ? lgc[t - off] : 0.f;
-      __syncthreads();
-      x += y;
-      if (scan_t) lgc[t] = x;
-      __syncthreads();
-    }
-    if (t < clen) a.lg2[(size_t)bh * a.N + c0 + t] = x;
-    if (t == clen - 1) a.lam[(size_t)bh * a.nc + c] = __builtin_amdgcn_exp2f(x);
-  }
-  const float l_last = lgc[clen - 1];
-
   const bf16* kb = static_cast<const bf16*>(a.k) + ((size_t)bh * a.N + c0) * D;
   const bf16* vb = static_cast<const bf16*>(a.v) + ((size_t)bh * a.N + c0) * D;
   constexpr int TILES = C::NDB * C::NDB, TPW = TILES / 8 > 0 ? TILES / 8 : 1;
@@ -105,6 +87,7 @@ __global__ __launch_bounds__(512) void gret_state_kernel(GretArgs a) {
       vraw[r] = *reinterpret_cast<const u32x4*>(vb + off);
     }
   };
+  float l_last = 0.f;   // set once the prefix sums are in LDS
   auto put = [&](int r0) {   // rows past the chunk become zero; V rows scaled by 2^{L_last - L_m}
     const int rows = min(C::BK, clen - r0);
 #pragma unroll
@@ -123,7 +106,26 @@ __global__ __launch_bounds__(512) void gret_state_kernel(GretArgs a) {
       *reinterpret_cast<u32x4*>(vt + slot * 16) = vw;
     }
   };
+  // the first K/V tile is requested before the decay prefix sums, which do
+  // not need it, so that both memory round trips overlap
   fetch(0);
+  // inclusive prefix sum of the chunk's log2 decays (positions past the end add 0)
+  {
+    const bool scan_t = t < 256;
+    float x = t < clen ? gate_log2(a.gate[(size_t)bh * a.N + c0 + t], a.inv_tau) : 0.f;
+    if (scan_t) lgc[t] = x;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const float y = scan_t && t >= off ? lgc[t - off] : 0.f;
+      __syncthreads();
+      x += y;
+      if (scan_t) lgc[t] = x;
+      __syncthreads();
+    }
+    if (t < clen) a.lg2[(size_t)bh * a.N + c0 + t] = x;
+    if (t == clen - 1) a.lam[(size_t)bh * a.nc + c] = __builtin_amdgcn_exp2f(x);
+  }
+  l_last = lgc[clen - 1];
   for (int r0 = 0; r0 < clen; r0 += C::BK) {
     put(r0);
     if (r0 + C::BK < clen) fetch(r0 + C::BK);
